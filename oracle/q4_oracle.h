@@ -1,0 +1,85 @@
+/*
+ * CPU oracle for Q4_0 fused-dequantization matmul and routed-expert MoE decode.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path (the HIP library and
+ * its Python binding) includes, links or calls this code. Only the test suite,
+ * the smoke check and the benchmark's CPU-baseline leg use it.
+ *
+ * It is plain, single-threaded C++ that writes out the definitions on the
+ * pages: dequantize a weight, then multiply in double precision. It shares no
+ * code, header or table with the GPU library.
+ *
+ * Sources (pages, by title and section):
+ *  - "2000-line C++ DeepSeek inference engine" article (news.rkmt.cn/news/19011)
+ *    §2.2: the block_q4_0 record (fp16 scale d, 16 bytes of packed nibbles for
+ *    32 weights) and dequantize(): byte index/2, low nibble for even index,
+ *    high nibble for odd, value (q - 8) * fp16_to_fp32(d).
+ *    §2.3: row-major layout, one row's blocks stored contiguously, columns
+ *    padded to a multiple of 32.
+ *    §3.2: the (i, k, j) loop order with C cleared first.
+ *    §3.4: the fused matmul_q4_0(A, B, C, M, N, K): block (k, j) is
+ *    B[k*(N/32) + j/32] and covers columns j..j+31 of row k.
+ *    §7.1: weight files are little-endian.
+ *  - "KTransformers DeepSeek-V2 heterogeneous MoE inference" tutorial
+ *    (www.mhpn.cn/news/2178346), section "Optimization 3" (arithmetic-intensity
+ *    offload): routed experts of DeepSeek-V2, top-6 of 160, run as a set of
+ *    batched GEMVs; the MoE module's gate yields top-k ids and weights that the
+ *    experts consume.
+ *
+ * Parity pins: every function here is pinned by tests that do not reuse its
+ * code (hand-worked blocks, IEEE bit patterns checked against numpy's float16,
+ * integer-exact special cases checked against numpy matmul, invariants). No
+ * function is "parity unpinned".
+ *
+ * Conventions: B is K rows x N columns, row-major, blocks of 32 along N; each
+ * block is 18 little-endian bytes [d (binary16) | qs[16]]. N % 32 == 0.
+ * Return value of the int functions: 0 on success, -1 on invalid arguments.
+ */
+#ifndef Q4_ORACLE_H
+#define Q4_ORACLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* IEEE-754 binary16 -> double, exact (every binary16 value is a double). */
+double oracle_fp16_to_double(uint16_t bits);
+
+/* Dequantize one 18-byte block into 32 doubles (all exact). */
+void oracle_dequant_block(const uint8_t* block18, double* out32);
+
+/* Dequantize rows [k0, k1) of a K x N matrix into out[(k1-k0) * N] (float;
+ * every dequantized weight is exactly representable in binary32). */
+int oracle_dequant_rows(const uint8_t* B, int N, int k0, int k1, float* out);
+
+/* y[M x N] = x[M x K] . deq(B[K x N]), accumulated in double in (i, k, j)
+ * order, rounded once to float. If bound != NULL it receives
+ * sum_k |x[m][k] * w[k][n]| in double (the per-output error scale). */
+int oracle_q4_0_matmul(const float* x, const uint8_t* B, int M, int N, int K,
+                       float* y, double* bound);
+
+/* Same, with the activations given as binary16 bit patterns (prefill). */
+int oracle_q4_0_matmul_f16(const uint16_t* x16, const uint8_t* B, int M, int N,
+                           int K, float* y, double* bound);
+
+/* Routed-expert MoE decode:
+ *   out[t] = sum_{j < topk, 0 <= ids[t][j] < E} w[t][j] * down_e(SiLU(x_t . Wg_e) * (x_t . Wu_e))
+ * with e = ids[t][j]. Wg and Wu are E consecutive H x I Q4_0 matrices (blocks
+ * along I); Wd is E consecutive I x H matrices (blocks along H). The gate and
+ * up products, SiLU and the down product are all kept in double; out is rounded
+ * once to float. bound[t][n] (optional) = sum_j |w| * sum_k |h_k * Wd[k][n]|.
+ * h_out (optional, [T*topk][I] doubles) receives each slot's h (zeros for an
+ * out-of-range id). */
+int oracle_moe_decode(const float* x, const uint8_t* Wg, const uint8_t* Wu,
+                      const uint8_t* Wd, const int32_t* ids, const float* w,
+                      int T, int H, int I, int E, int topk, float* out,
+                      double* bound, double* h_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4_ORACLE_H */
