@@ -1,0 +1,341 @@
+"""Benchmark of the Q4_0 decode GEMV / MoE decode / prefill GEMM kernels on one GPU.
+
+Prints ONE JSON line on stdout (progress goes to stderr).
+
+Headline workload (``value``): dense 7B-shaped decode linears, Q4_0 weights
+4096x4096 (attention projection), 4096x11008 twice (gate, up) and 11008x4096
+(down), each at batch 1, 4 and 8 -> one step = 12 q4_0_gemv calls. ``value``
+is the step's algorithmic HBM bytes (each Q4_0 block once at 18 B per 32
+weights, plus activations and outputs) divided by the step time, in GB/s.
+Weights rotate over enough identical copies (>= 1 GiB in total) that every
+step reads them from HBM rather than from the 256 MB Infinity Cache.
+
+Also measured in the same run (reported under "also"): the DeepSeek-V2-shaped
+MoE decode (5120 hidden, 160 experts of 5120x1536 gate/up and 1536x5120 down,
+top-6) at 1 and 32 tokens (uniform and skewed routing) in tokens/s and GB/s,
+and the prefill GEMM 2048x4096 . 4096x{4096, 11008} in TFLOP/s.
+
+``cpu_baseline``: the CPU oracle (single-threaded, double accumulation) timed
+on this host over whole dense steps for about 10 s, as GB/s of the same
+algorithmic bytes. A reported baseline, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 4 SIMD x 16 lanes x 2.4 GHz x 2 flop (no packed FP32)
+GIB = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def q4_bytes(K, N):
+    return K * (N // 32) * 18
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true", help="skip the MoE and prefill measurements")
+    ap.add_argument("--only", choices=["dense", "moe", "prefill"], default=None,
+                    help="run a single workload (for profiling); prints its own JSON line")
+    return ap.parse_args()
+
+
+class EventTimer:
+    """Per-launch durations from HIP events recorded on the launching stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def run(self, key, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        out = fn()
+        e.record()
+        self.pairs.setdefault(key, []).append((s, e))
+        return out
+
+    def mean_ms(self, key):
+        ps = self.pairs.get(key, [])
+        return sum(s.elapsed_time(e) for s, e in ps) / len(ps) if ps else float("nan")
+
+
+# ---------------------------------------------------------------------------
+# dense decode linears
+# ---------------------------------------------------------------------------
+def bench_dense(torch, dev, steps, warmup):
+    from moe_experts_amd import datagen, q4_0_gemv, q4_0_gemv_workspace_bytes
+    shapes = datagen.DENSE_7B_SHAPES
+    Ms = datagen.DENSE_7B_BATCHES
+    wbytes = sum(q4_bytes(K, N) for _, K, N, _ in shapes)
+    R = max(2, math.ceil(GIB / wbytes))
+    log(f"[dense] generating 4 matrices ({wbytes / 1e6:.1f} MB), {R} device copies")
+    host = [datagen.q4_0_random(seed, K, N) for _, K, N, seed in shapes]
+    base = [torch.from_numpy(h).to(dev) for h in host]
+    copies = [base] + [[b.clone() for b in base] for _ in range(R - 1)]
+    xs = {M: {K: torch.from_numpy(datagen.activations(datagen.dense_x_seed(M), M, K)).to(dev)
+              for K in sorted({K for _, K, _, _ in shapes})} for M in Ms}
+    ys = {(M, i): torch.empty((M, N), dtype=torch.float32, device=dev)
+          for M in Ms for i, (_, _, N, _) in enumerate(shapes)}
+    need = max(q4_0_gemv_workspace_bytes(M, N, K) for M in Ms for _, K, N, _ in shapes)
+    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
+
+    calls = [(M, i) for M in Ms for i in range(len(shapes))]
+    step_bytes = sum(q4_bytes(K, N) + 4 * M * K + 4 * M * N
+                     for M in Ms for _, K, N, _ in shapes)
+
+    def step(r, timer=None):
+        ws_ = copies[r % R]
+        for (M, i) in calls:
+            _, K, N, _ = shapes[i]
+            f = lambda: q4_0_gemv(xs[M][K], ws_[i], N, y=ys[(M, i)], ws=ws)
+            if timer is None:
+                f()
+            else:
+                timer.run((M, i), f)
+
+    for r in range(warmup):
+        step(r)
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    t0 = time.perf_counter()
+    for r in range(steps):
+        step(warmup + r, timer)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+
+    per_call = {}
+    for (M, i) in calls:
+        name, K, N, _ = shapes[i]
+        ms = timer.mean_ms((M, i))
+        b = q4_bytes(K, N) + 4 * M * K + 4 * M * N
+        per_call[f"{name}_M{M}"] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
+                                    "TFLOPs": round(2 * M * K * N / (ms * 1e-3) / 1e12, 2)}
+    per_M = {}
+    for M in Ms:
+        ms = sum(timer.mean_ms((M, i)) for i in range(len(shapes)))
+        b = sum(q4_bytes(K, N) + 4 * M * K + 4 * M * N for _, K, N, _ in shapes)
+        per_M[M] = (ms, b)
+    return dict(step_s=dt, step_bytes=step_bytes, per_call=per_call, per_M=per_M, R=R,
+                host=host, timer=timer, shapes=shapes, Ms=Ms)
+
+
+def dense_roofline(d):
+    """Roofline of the dominant kernel: the batch size whose gemv launches take
+    the most time per step (each batch size is its own kernel instantiation)."""
+    Ms = d["Ms"]
+    tot = {M: d["per_M"][M][0] for M in Ms}
+    Mdom = max(Ms, key=lambda M: tot[M])
+    ms, b = d["per_M"][Mdom]
+    n = len(d["shapes"])
+    flops = sum(2 * Mdom * K * N for _, K, N, _ in d["shapes"])
+    gbs = b / (ms * 1e-3) / 1e9
+    tflops = flops / (ms * 1e-3) / 1e12
+    # VALU lane-ops per weight of the fused kernel (half a block per lane):
+    # 16 nibble converts + 4 masks + 1 scale convert per 16 weights, plus M FMAs
+    # and 2M scale products/corrections per 16 weights -> the ALU-bound time.
+    ops_per_weight = (21 + 18 * Mdom) / 16.0
+    alu_time_at_peak = sum(K * N for _, K, N, _ in d["shapes"]) * ops_per_weight / 39.3e12
+    hbm_time_at_peak = b / (HBM_PEAK_GBS * 1e9)
+    if alu_time_at_peak > hbm_time_at_peak:
+        roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": VALU_F32_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / VALU_F32_PEAK_TFLOPS, 4), "traffic": None,
+                "kernel": f"gemv_q4_0_kernel<M={Mdom}>",
+                "note": "useful FMA flops 2MKN only; unpack and scale work not counted",
+                "alu_ops_frac": round(alu_time_at_peak / (ms * 1e-3), 4),
+                "hbm_GBps": round(gbs, 1)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"gemv_q4_0_kernel<M={Mdom}>"}
+    roof["launches_per_step"] = n
+    roof["avg_launch_us"] = round(ms * 1e3 / n, 2)
+    return roof
+
+
+def cpu_baseline_dense(d, seconds):
+    import oracle
+    shapes, Ms = d["shapes"], d["Ms"]
+    xs = {M: {K: datagen_x(M, K) for K in sorted({K for _, K, _, _ in shapes})} for M in Ms}
+    done_bytes, t0, nsteps = 0, time.perf_counter(), 0
+    while True:
+        for M in Ms:
+            for i, (_, K, N, _) in enumerate(shapes):
+                oracle.q4_0_matmul(xs[M][K], d["host"][i], N, K, with_bound=False)
+                done_bytes += q4_bytes(K, N) + 4 * M * K + 4 * M * N
+        nsteps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nsteps} whole dense step(s) (12 GEMVs each), {dt:.1f} s, single thread, "
+                      f"double accumulation; host has {os.cpu_count()} logical CPUs"}
+
+
+def datagen_x(M, K):
+    from moe_experts_amd import datagen
+    return datagen.activations(datagen.dense_x_seed(M), M, K)
+
+
+# ---------------------------------------------------------------------------
+# MoE decode
+# ---------------------------------------------------------------------------
+def bench_moe(torch, dev, steps, warmup):
+    from moe_experts_amd import datagen, moe_q4_0_decode, moe_q4_0_workspace_bytes
+    c = datagen.MOE_DSV2
+    H, I, E, topk = c["H"], c["I"], c["E"], c["topk"]
+    log("[moe] generating 160 experts (2.1 GB)")
+    Wg, Wu, Wd = datagen.moe_experts(H, I, E)
+    layers = 4  # distinct copies of the layer, visited round robin (>8 GB)
+    dW = [(torch.from_numpy(Wg).to(dev), torch.from_numpy(Wu).to(dev), torch.from_numpy(Wd).to(dev))]
+    for _ in range(layers - 1):
+        dW.append(tuple(w.clone() for w in dW[0]))
+    del Wg, Wu, Wd
+    mat = H * (I // 32) * 18
+    res = {}
+    for label, T, bias, xseed, lseed in (("t1", 1, 0.0, datagen.MOE_T1["x_seed"], datagen.MOE_T1["logit_seed"]),
+                                         ("t32", 32, 0.0, datagen.MOE_T32["x_seed"], datagen.MOE_T32["logit_seed"]),
+                                         ("t32_skewed", 32, datagen.MOE_T32["hot_bias"],
+                                          datagen.MOE_T32["x_seed"], datagen.MOE_T32["logit_seed"])):
+        x = torch.from_numpy(datagen.activations(xseed, T, H)).to(dev)
+        routes = []
+        uniq = []
+        for r in range(16):
+            ids, w, _ = datagen.routing(lseed + 1000 * r, T, E, topk, hot_bias=bias)
+            routes.append((torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)))
+            uniq.append(len(np.unique(ids)))
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = torch.zeros(moe_q4_0_workspace_bytes(T, H, I, E, topk), dtype=torch.uint8, device=dev)
+
+        def call(r):
+            g, u, dd = dW[r % layers]
+            ids, w = routes[r % len(routes)]
+            moe_q4_0_decode(x, g, u, dd, ids, w, I, E, out=out, ws=ws)
+
+        for r in range(warmup):
+            call(r)
+        torch.cuda.synchronize()
+        n = max(steps, 16)
+        t0 = time.perf_counter()
+        for r in range(n):
+            call(warmup + r)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / n
+        U = np.mean([uniq[(warmup + r) % len(routes)] for r in range(n)])
+        b = U * 3 * mat + 2 * 4 * T * H + T * topk * 8
+        res[label] = {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 2),
+                      "GBps": round(b / dt / 1e9, 1), "hbm_frac": round(b / dt / 1e9 / HBM_PEAK_GBS, 4),
+                      "unique_experts": round(float(U), 2)}
+        log(f"[moe] {label}: {res[label]}")
+    return res
+
+
+# ---------------------------------------------------------------------------
+# prefill GEMM
+# ---------------------------------------------------------------------------
+def bench_prefill(torch, dev, steps, warmup):
+    from moe_experts_amd import datagen, q4_0_gemm
+    c = datagen.PREFILL
+    M, K = c["M"], c["K"]
+    X = torch.from_numpy(datagen.to_f16(datagen.activations(c["x_seed"], M, K))).to(dev)
+    res = {}
+    for N, seed in zip(c["Ns"], c["b_seeds"]):
+        B = torch.from_numpy(datagen.q4_0_random(seed, K, N)).to(dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            q4_0_gemm(X, B, N, Y=Y)
+        torch.cuda.synchronize()
+        timer = EventTimer(torch)
+        for _ in range(max(steps, 10)):
+            timer.run("g", lambda: q4_0_gemm(X, B, N, Y=Y))
+        torch.cuda.synchronize()
+        ms = timer.mean_ms("g")
+        tf = 2 * M * N * K / (ms * 1e-3) / 1e12
+        res[f"N{N}"] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
+                        "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+        log(f"[prefill] N={N}: {res[f'N{N}']}")
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+
+    if args.only == "moe":
+        print(json.dumps({"moe": bench_moe(torch, dev, args.steps, args.warmup)}), flush=True)
+        return
+    if args.only == "prefill":
+        print(json.dumps({"prefill": bench_prefill(torch, dev, args.steps, args.warmup)}), flush=True)
+        return
+
+    d = bench_dense(torch, dev, args.steps, args.warmup)
+    value = d["step_bytes"] / d["step_s"] / 1e9
+    log(f"[dense] step {d['step_s'] * 1e3:.3f} ms, {value:.1f} GB/s")
+    for k, v in d["per_call"].items():
+        log(f"  {k:22s} {v}")
+    roof = dense_roofline(d)
+    extras = {}
+    if not args.no_extras and args.only is None:
+        extras["moe_decode"] = bench_moe(torch, dev, args.steps, args.warmup)
+        extras["prefill_gemm"] = bench_prefill(torch, dev, args.steps, args.warmup)
+    extras["dense_per_call"] = d["per_call"]
+    extras["dense_per_batch_GBps"] = {str(M): round(b / (ms * 1e-3) / 1e9, 1)
+                                      for M, (ms, b) in d["per_M"].items()}
+    cpu = None
+    if not args.no_cpu_baseline and args.only is None:
+        log("[cpu] timing the oracle")
+        cpu = cpu_baseline_dense(d, args.cpu_seconds)
+    line = {
+        "metric": "Q4_0 decode GEMV achieved HBM GB/s (dense 7B decode linears)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(d["step_s"] * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "dense 7B-shaped decode linears: Q4_0 4096x4096, 4096x11008 (x2), "
+                               "11008x4096 at batch 1, 4 and 8 (12 GEMVs per step)",
+                   "weights": "Q4_0 (18 B per 32 weights)", "rotation_copies": d["R"],
+                   "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "also": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * q4moe — Q4_0 fused-dequantization matmul and routed-expert MoE decode for
+ * AMD Instinct MI355X (gfx950). Plain C ABI: device pointers, sizes, and a
+ * HIP stream handle passed as void*. No C++ or framework types.
+ *
+ * Q4_0 (the "2000-line C++ DeepSeek inference engine" article, §2.2 block_q4_0
+ * and dequantize; §2.3 layout; §7.1 byte order): a block is 18 little-endian
+ * bytes holding 32 weights, a binary16 scale d followed by 16 bytes qs. Weight
+ * 2i is the low nibble of qs[i] and weight 2i+1 the high nibble; its value is
+ * (nibble - 8) * d.
+ *
+ * Matrix layout (same article, §3.4 matmul_q4_0): a K x N weight matrix B is
+ * stored row-major as K rows of N/32 consecutive blocks; block (k, j) covers
+ * columns 32j..32j+31 of row k. N must be a multiple of 32 (the article pads
+ * columns to a multiple of 32 at load time). Activations and outputs are
+ * row-major; y[m][n] = sum_k x[m][k] * w[k][n]. Outputs are overwritten.
+ *
+ * Common rules for every entry point:
+ *  - Ownership: every pointer argument is device memory owned by the caller.
+ *    The library keeps no pointer after the call returns and allocates nothing.
+ *  - Asynchrony: arguments are checked on the host, the work is enqueued on
+ *    `stream` (a hipStream_t; NULL is the default stream) and the call returns
+ *    without synchronizing. Results are visible after the stream is synchronized.
+ *  - Errors: 0 (Q4_OK) on success, a negative q4_status otherwise. On a host-side
+ *    argument error nothing is enqueued and the outputs are untouched. Q4_EHIP
+ *    reports a launch failure returned by the HIP runtime.
+ *  - Workspace: entry points that take `ws` need at least the number of bytes
+ *    the matching *_workspace_bytes() returns, 256-byte aligned device memory.
+ *    Before its first use a workspace must be filled with zeros; every call
+ *    leaves it zeroed again (its completion counters reset themselves). One
+ *    workspace serves one call at a time: calls that overlap in time (for
+ *    example on two streams) need separate workspaces.
+ *  - Determinism: for the same arguments a call produces bitwise identical
+ *    results (fixed reduction order, no floating-point atomics).
+ */
+#ifndef Q4MOE_H
+#define Q4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* One Q4_0 block: 18 bytes, 2-byte aligned, little-endian. */
+typedef struct __attribute__((packed, aligned(2))) q4_0_block {
+  uint16_t d;      /* binary16 scale bit pattern */
+  uint8_t qs[16];  /* 32 packed nibbles, even weight in the low nibble */
+} q4_0_block;
+
+#ifdef __cplusplus
+static_assert(sizeof(q4_0_block) == 18, "q4_0_block must be 18 bytes");
+#else
+_Static_assert(sizeof(q4_0_block) == 18, "q4_0_block must be 18 bytes");
+#endif
+
+typedef enum q4_status {
+  Q4_OK = 0,
+  Q4_EINVAL = -1,      /* null pointer or non-positive dimension */
+  Q4_ESHAPE = -2,      /* N/H/I not a multiple of 32, or M/T/topk/E out of range */
+  Q4_EALIGN = -3,      /* pointer misaligned (blocks 2 B, fp32/fp16 arrays 4 B, ws 256 B) */
+  Q4_EWORKSPACE = -4,  /* workspace missing or smaller than required */
+  Q4_EHIP = -5,        /* the HIP runtime reported an error at launch */
+  Q4_ETOOBIG = -6      /* a size exceeds the limits of the implementation */
+} q4_status;
+
+/* Limits of the decode paths. */
+#define Q4_GEMV_MAX_M 8    /* rows of x in one q4_0_gemv call */
+#define Q4_MOE_MAX_T 64    /* tokens in one moe_q4_0_decode call */
+#define Q4_MOE_MAX_TOPK 8  /* routed experts per token */
+#define Q4_MOE_MAX_E 1024  /* experts per layer */
+
+/* Static description of a status code (never NULL). */
+const char* q4_strerror(int status);
+
+/* ---------------------------------------------------------------------------
+ * Decode GEMV (batch 1..8): y[M x N] = x[M x K] . deq(B[K x N]).
+ * The article's fused matmul_q4_0(A, B, C, M, N, K) (§3.4), for decode batches.
+ *   x   fp32 [M][K], 4-byte aligned      B  Q4_0 [K][N/32] blocks, 2-byte aligned
+ *   y   fp32 [M][N], 4-byte aligned, overwritten
+ *   1 <= M <= Q4_GEMV_MAX_M, K >= 1, N >= 32, N % 32 == 0, K*N/32 < 2^31 blocks.
+ *   ws/ws_bytes: workspace of q4_0_gemv_workspace_bytes(M, N, K) bytes.
+ * Accumulation is fp32; each product x * (q - 8) * d is formed in fp32.
+ * ------------------------------------------------------------------------- */
+size_t q4_0_gemv_workspace_bytes(int M, int N, int K);
+int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K,
+              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Prefill GEMM: Y[M x N] = X[M x K] . deq(B[K x N]) on the fp16 matrix cores.
+ * The batched-prompt matmul of the same article (§5) and the quantized
+ * tensor-core GEMM that the KTransformers tutorial uses for prefill ("Optimization
+ * 2", Marlin), as one fused kernel: B tiles are dequantized to fp16 in LDS and
+ * contracted with fp32 accumulation.
+ *   X   fp16 [M][K] (the caller rounds its activations to fp16), 4-byte aligned
+ *   B   Q4_0 [K][N/32] blocks, 2-byte aligned      Y fp32 [M][N], overwritten
+ *   M >= 1, K >= 1, N >= 32, N % 32 == 0.
+ * Each dequantized weight (q - 8) * d is rounded to fp16 before the product.
+ * ------------------------------------------------------------------------- */
+int q4_0_gemm(const uint16_t* X, const q4_0_block* B, float* Y, int M, int N, int K,
+              void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Routed-expert MoE decode (DeepSeek-V2 shape: KTransformers tutorial,
+ * "Optimization 3": top-6 of 160 routed experts evaluated as batched GEMVs;
+ * the MoE module's gate hands top-k ids and weights to the experts):
+ *   out[t] = sum_{s < topk} topk_w[t][s] * Wd_e ( SiLU(x_t . Wg_e) * (x_t . Wu_e) ),
+ *   e = topk_ids[t][s], SiLU(z) = z / (1 + exp(-z)).
+ *   x        fp32 [T][H]                     out  fp32 [T][H], overwritten
+ *   Wg, Wu   Q4_0, E consecutive H x I matrices (blocks along I)
+ *   Wd       Q4_0, E consecutive I x H matrices (blocks along H)
+ *   topk_ids int32 [T][topk]                 topk_w fp32 [T][topk]
+ *   1 <= T <= Q4_MOE_MAX_T, 1 <= topk <= Q4_MOE_MAX_TOPK, 1 <= E <= Q4_MOE_MAX_E,
+ *   H % 32 == 0, I % 32 == 0.
+ * Work is grouped by expert from the routing table on the device: each routed
+ * expert's weights are streamed once per call for all tokens that chose it
+ * (in chunks of at most 8 tokens).
+ * Data-dependent rules (not checked on the host): an id outside [0, E)
+ * contributes zero; an expert repeated within a token contributes once per slot.
+ * The slot contributions of a token are summed in slot order 0..topk-1.
+ *   ws/ws_bytes: workspace of moe_q4_0_workspace_bytes(T, H, I, E, topk) bytes.
+ * ------------------------------------------------------------------------- */
+size_t moe_q4_0_workspace_bytes(int T, int H, int I, int E, int topk);
+int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
+                    const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
+                    float* out, int T, int H, int I, int E, int topk, void* ws,
+                    size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4MOE_H */

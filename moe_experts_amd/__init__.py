@@ -1,1 +1,20 @@
-"""MI355X-native Q4_0 fused-dequantization matmul and routed-expert MoE decode."""
+"""MI355X-native Q4_0 fused-dequantization matmul and routed-expert MoE decode.
+
+Entry points (HIP kernels behind the C ABI in ``include/q4moe.h``):
+``q4_0_gemv``, ``q4_0_gemm``, ``moe_q4_0_decode`` and their workspace-size
+helpers. They are loaded from ``libq4moe.so`` on first use; there is no CPU
+fallback. ``moe_experts_amd.datagen`` (seeded synthetic inputs) does not need
+the library.
+"""
+_EXPORTS = ("q4_0_gemv", "q4_0_gemm", "moe_q4_0_decode", "q4_0_gemv_workspace_bytes",
+            "moe_q4_0_workspace_bytes", "q4_strerror", "Q4Error")
+
+
+def __getattr__(name):
+    if name in _EXPORTS:
+        from . import binding
+        return getattr(binding, name)
+    raise AttributeError(name)
+
+
+__all__ = list(_EXPORTS)

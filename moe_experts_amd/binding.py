@@ -1,0 +1,173 @@
+"""Thin Python binding of libq4moe (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libq4moe.so``. PyTorch supplies device memory and the current
+HIP stream. The library must have been built (``moe_experts_amd.build``);
+importing this module fails loudly if it is missing - there is no fallback.
+
+The functions carry the names of the C entry points in ``include/q4moe.h``.
+Before any call reaches the library, the binding checks that every tensor is a
+contiguous device tensor of the dtype and number of elements the shape
+arguments imply, so a mismatched tensor can never be read or written out of
+bounds by a kernel.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libq4moe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m moe_experts_amd.build` "
+        "(the Q4_0 kernels have no CPU fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_Z = ctypes.c_size_t
+_lib.q4_strerror.restype = ctypes.c_char_p
+_lib.q4_strerror.argtypes = [_I]
+_lib.q4_0_gemv_workspace_bytes.restype = _Z
+_lib.q4_0_gemv_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.q4_0_gemv.restype = _I
+_lib.q4_0_gemv.argtypes = [_P, _P, _P, _I, _I, _I, _P, _Z, _P]
+_lib.q4_0_gemm.restype = _I
+_lib.q4_0_gemm.argtypes = [_P, _P, _P, _I, _I, _I, _P]
+_lib.moe_q4_0_workspace_bytes.restype = _Z
+_lib.moe_q4_0_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.moe_q4_0_decode.restype = _I
+_lib.moe_q4_0_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
+
+BLOCK_BYTES = 18
+
+
+class Q4Error(RuntimeError):
+    """A non-zero status returned by libq4moe."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"libq4moe status {status}: {q4_strerror(status)}")
+
+
+def q4_strerror(status: int) -> str:
+    return _lib.q4_strerror(int(status)).decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise Q4Error(rc)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype, numel: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+# Workspaces: one zero-filled buffer per (device, stream), grown on demand.
+# The library leaves a workspace zeroed after every call, so it is reused as is.
+_ws_lock = threading.Lock()
+_ws_cache: dict = {}
+
+
+def workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+            _ws_cache[key] = buf
+        return buf
+
+
+def q4_0_gemv_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.q4_0_gemv_workspace_bytes(M, N, K))
+
+
+def moe_q4_0_workspace_bytes(T: int, H: int, I: int, E: int, topk: int) -> int:
+    return int(_lib.moe_q4_0_workspace_bytes(T, H, I, E, topk))
+
+
+def q4_0_gemv(x: torch.Tensor, B: torch.Tensor, N: int, y: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . deq(B) for a Q4_0 matrix B (uint8, K*(N/32)*18 bytes)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if N <= 0 or N % 32:
+        raise ValueError("N must be a positive multiple of 32")
+    px = _dev(x, "x", torch.float32, M * K)
+    pb = _dev(B, "B", torch.uint8, K * (N // 32) * BLOCK_BYTES)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py = _dev(y, "y", torch.float32, M * N)
+    need = q4_0_gemv_workspace_bytes(M, N, K)
+    if ws is None:
+        ws = workspace(need, x.device)
+    pw, nw = (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8, ws.numel()), ws.numel())
+    _check(_lib.q4_0_gemv(px, pb, py, M, N, K, pw, nw, _stream(x.device)))
+    return y
+
+
+def q4_0_gemm(X: torch.Tensor, B: torch.Tensor, N: int, Y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[M, N] = X[M, K] (float16) . deq(B) with fp32 accumulation, on MFMA."""
+    if X.dim() != 2:
+        raise ValueError("X must be [M, K]")
+    M, K = X.shape
+    if N <= 0 or N % 32:
+        raise ValueError("N must be a positive multiple of 32")
+    px = _dev(X, "X", torch.float16, M * K)
+    pb = _dev(B, "B", torch.uint8, K * (N // 32) * BLOCK_BYTES)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    py = _dev(Y, "Y", torch.float32, M * N)
+    _check(_lib.q4_0_gemm(px, pb, py, M, N, K, _stream(X.device)))
+    return Y
+
+
+def moe_q4_0_decode(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
+                    topk_ids: torch.Tensor, topk_w: torch.Tensor, I: int, E: int,
+                    out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed-expert MoE decode; x [T, H] fp32, ids/weights [T, topk]."""
+    if x.dim() != 2 or topk_ids.dim() != 2:
+        raise ValueError("x must be [T, H] and topk_ids [T, topk]")
+    T, H = x.shape
+    topk = topk_ids.shape[1]
+    mat = H * (I // 32) * BLOCK_BYTES
+    px = _dev(x, "x", torch.float32, T * H)
+    pg = _dev(Wg, "Wg", torch.uint8, E * mat)
+    pu = _dev(Wu, "Wu", torch.uint8, E * mat)
+    pd = _dev(Wd, "Wd", torch.uint8, E * mat)
+    pi = _dev(topk_ids, "topk_ids", torch.int32, T * topk)
+    pw_ = _dev(topk_w, "topk_w", torch.float32, T * topk)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    po = _dev(out, "out", torch.float32, T * H)
+    need = moe_q4_0_workspace_bytes(T, H, I, E, topk)
+    if ws is None:
+        ws = workspace(need, x.device)
+    pws, nws = (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8, ws.numel()), ws.numel())
+    _check(_lib.moe_q4_0_decode(px, pg, pu, pd, pi, pw_, po, T, H, I, E, topk, pws, nws,
+                                _stream(x.device)))
+    return out

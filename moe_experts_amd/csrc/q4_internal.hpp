@@ -1,0 +1,53 @@
+// Host-side plans and launchers shared between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "q4moe.h"
+
+namespace q4 {
+
+// ---- decode GEMV ---------------------------------------------------------
+struct GemvPlan {
+  int LPB;            // lanes per block (1: whole block per lane, 2: half)
+  int Jt;             // block columns per workgroup tile
+  int Lr;             // lanes per row phase (Jt * LPB)
+  int P;              // row phases per workgroup
+  int C;              // column tiles
+  int Kt;             // rows per workgroup
+  int S;              // K splits
+  size_t lds_bytes;   // dynamic LDS per workgroup
+  size_t part_offset; // byte offset of the partials in the workspace
+  size_t ws_bytes;    // workspace bytes (0 when S == 1)
+};
+
+GemvPlan plan_gemv(int M, int N, int K);
+hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N, int K,
+                       void* ws, const GemvPlan& p, hipStream_t st);
+
+// ---- routed-expert MoE decode -------------------------------------------
+struct MoePlan {
+  int T, H, I, E, topk;
+  int max_items;      // upper bound on (expert, token-chunk) work items
+  // gate/up GEMV (K = H rows, N = I columns)
+  int gu_Jt, gu_Lr, gu_P, gu_C, gu_Kt, gu_S;
+  // down GEMV (K = I rows, N = H columns)
+  int dn_Jt, dn_Lr, dn_P, dn_C, dn_Kt, dn_S;
+  size_t gu_lds, dn_lds;
+  // workspace layout (byte offsets)
+  size_t off_route, off_gu_cnt, off_dn_cnt, off_gu_part, off_dn_part, off_h, off_yd;
+  size_t ws_bytes;
+};
+
+MoePlan plan_moe(int T, int H, int I, int E, int topk);
+hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, const uint8_t* Wd,
+                      const int32_t* ids, const float* w, float* out, void* ws,
+                      const MoePlan& p, hipStream_t st);
+
+// ---- prefill GEMM --------------------------------------------------------
+hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int N, int K,
+                       hipStream_t st);
+
+}  // namespace q4

@@ -1,0 +1,109 @@
+// C ABI of libq4moe: host-side argument checks, workspace sizing and launch.
+// Every entry point validates its arguments before touching the HIP runtime,
+// so argument errors never enqueue work (and can be tested without a GPU).
+#include "q4moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "q4_internal.hpp"
+
+namespace {
+
+constexpr long long kMaxBlocks = 0x7fffffffLL;  // blocks addressed by one matrix
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_gemv(const float* x, const q4_0_block* B, const float* y, int M, int N, int K) {
+  if (!x || !B || !y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
+  if (N % 32 != 0 || M > Q4_GEMV_MAX_M) return Q4_ESHAPE;
+  if ((long long)K * (N / 32) > kMaxBlocks) return Q4_ETOOBIG;
+  if (!aligned(x, 4) || !aligned(y, 4) || !aligned(B, 2)) return Q4_EALIGN;
+  return Q4_OK;
+}
+
+int check_ws(const void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return Q4_OK;
+  if (!ws || ws_bytes < need) return Q4_EWORKSPACE;
+  if (!aligned(ws, 256)) return Q4_EALIGN;
+  return Q4_OK;
+}
+
+int check_moe_shape(int T, int H, int I, int E, int topk) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return Q4_EINVAL;
+  if (H % 32 != 0 || I % 32 != 0 || T > Q4_MOE_MAX_T || topk > Q4_MOE_MAX_TOPK ||
+      E > Q4_MOE_MAX_E)
+    return Q4_ESHAPE;
+  if ((long long)H * (I / 32) > kMaxBlocks) return Q4_ETOOBIG;  // blocks of one expert matrix
+  return Q4_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* q4_strerror(int status) {
+  switch (status) {
+    case Q4_OK: return "success";
+    case Q4_EINVAL: return "invalid argument: null pointer or non-positive dimension";
+    case Q4_ESHAPE: return "unsupported shape: N/H/I must be multiples of 32, M/T/topk/E within limits";
+    case Q4_EALIGN: return "misaligned pointer (blocks 2 B, fp32/fp16 arrays 4 B, workspace 256 B)";
+    case Q4_EWORKSPACE: return "workspace missing or too small";
+    case Q4_EHIP: return "HIP runtime error at launch";
+    case Q4_ETOOBIG: return "size exceeds implementation limits";
+    default: return "unknown status";
+  }
+}
+
+size_t q4_0_gemv_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || M > Q4_GEMV_MAX_M) return 0;
+  return q4::plan_gemv(M, N, K).ws_bytes;
+}
+
+int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc = check_gemv(x, B, y, M, N, K);
+  if (rc != Q4_OK) return rc;
+  const q4::GemvPlan p = q4::plan_gemv(M, N, K);
+  rc = check_ws(ws, ws_bytes, p.ws_bytes);
+  if (rc != Q4_OK) return rc;
+  return from_hip(q4::launch_gemv(x, reinterpret_cast<const uint8_t*>(B), y, M, N, K, ws, p,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+int q4_0_gemm(const uint16_t* X, const q4_0_block* B, float* Y, int M, int N, int K,
+              void* stream) {
+  if (!X || !B || !Y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
+  if (N % 32 != 0) return Q4_ESHAPE;
+  if ((long long)K * (N / 32) > kMaxBlocks) return Q4_ETOOBIG;
+  if (!aligned(X, 4) || !aligned(Y, 4) || !aligned(B, 2)) return Q4_EALIGN;
+  return from_hip(q4::launch_gemm(X, reinterpret_cast<const uint8_t*>(B), Y, M, N, K,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_q4_0_workspace_bytes(int T, int H, int I, int E, int topk) {
+  if (check_moe_shape(T, H, I, E, topk) != Q4_OK) return 0;
+  return q4::plan_moe(T, H, I, E, topk).ws_bytes;
+}
+
+int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
+                    const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
+                    float* out, int T, int H, int I, int E, int topk, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!x || !Wg || !Wu || !Wd || !topk_ids || !topk_w || !out) return Q4_EINVAL;
+  int rc = check_moe_shape(T, H, I, E, topk);
+  if (rc != Q4_OK) return rc;
+  if (!aligned(x, 4) || !aligned(out, 4) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      !aligned(Wg, 2) || !aligned(Wu, 2) || !aligned(Wd, 2))
+    return Q4_EALIGN;
+  const q4::MoePlan p = q4::plan_moe(T, H, I, E, topk);
+  rc = check_ws(ws, ws_bytes, p.ws_bytes);
+  if (rc != Q4_OK) return rc;
+  return from_hip(q4::launch_moe(x, reinterpret_cast<const uint8_t*>(Wg),
+                                 reinterpret_cast<const uint8_t*>(Wu),
+                                 reinterpret_cast<const uint8_t*>(Wd), topk_ids, topk_w, out, ws,
+                                 p, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+"""C-ABI checks that run without a GPU: the library loads, exports every entry
+point the header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4moe.h")
+LIB = os.path.join(ROOT, "moe_experts_amd", "libq4moe.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from moe_experts_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.q4_strerror.restype = ctypes.c_char_p
+    L.q4_strerror.argtypes = [I]
+    L.q4_0_gemv.argtypes = [P, P, P, I, I, I, P, Z, P]
+    L.q4_0_gemm.argtypes = [P, P, P, I, I, I, P]
+    L.moe_q4_0_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, Z, P]
+    L.q4_0_gemv_workspace_bytes.restype = Z
+    L.q4_0_gemv_workspace_bytes.argtypes = [I, I, I]
+    L.moe_q4_0_workspace_bytes.restype = Z
+    L.moe_q4_0_workspace_bytes.argtypes = [I, I, I, I, I]
+    return L
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if not n.startswith("_") and n != "sizeof"))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("q4_0_gemv", "q4_0_gemm", "moe_q4_0_decode", "q4_0_gemv_workspace_bytes",
+              "moe_q4_0_workspace_bytes", "q4_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in q4moe.h but not exported"
+
+
+def test_strerror(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, -99):
+        s = lib.q4_strerror(code)
+        assert isinstance(s, bytes) and len(s) > 3
+
+
+FAKE = 0x10000  # never dereferenced: every case below fails host validation
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 1, 32, 1), -1),           # null x
+    ((FAKE, FAKE, FAKE, 0, 32, 1), -1),           # M = 0
+    ((FAKE, FAKE, FAKE, 1, 32, 0), -1),           # K = 0
+    ((FAKE, FAKE, FAKE, 1, 48, 4), -2),           # N not a multiple of 32
+    ((FAKE, FAKE, FAKE, 9, 32, 4), -2),           # M > 8
+    ((FAKE + 2, FAKE, FAKE, 1, 32, 4), -3),       # misaligned x
+    ((FAKE, FAKE + 1, FAKE, 1, 32, 4), -3),       # misaligned blocks
+    ((FAKE, FAKE, FAKE, 1, 1 << 30, 1 << 30), -6),  # too many blocks
+])
+def test_gemv_rejects_bad_arguments(lib, args, code):
+    assert lib.q4_0_gemv(*args, None, 0, None) == code
+
+
+def test_gemv_requires_workspace_when_split(lib):
+    need = lib.q4_0_gemv_workspace_bytes(1, 4096, 4096)
+    assert need > 0
+    assert lib.q4_0_gemv(FAKE, FAKE, FAKE, 1, 4096, 4096, None, 0, None) == -4
+    assert lib.q4_0_gemv(FAKE, FAKE, FAKE, 1, 4096, 4096, FAKE, need - 1, None) == -4
+    assert lib.q4_0_gemv(FAKE, FAKE, FAKE, 1, 4096, 4096, FAKE + 16, need, None) == -3
+
+
+def test_workspace_sizes(lib):
+    assert lib.q4_0_gemv_workspace_bytes(0, 4096, 4096) == 0
+    assert lib.q4_0_gemv_workspace_bytes(9, 4096, 4096) == 0
+    # the split plan depends only on (N, K): the workspace grows linearly in M
+    w1 = lib.q4_0_gemv_workspace_bytes(1, 4096, 11008)
+    w8 = lib.q4_0_gemv_workspace_bytes(8, 4096, 11008)
+    assert w1 > 0 and w8 > w1
+    assert lib.moe_q4_0_workspace_bytes(1, 5120, 1536, 160, 6) > 0
+    assert lib.moe_q4_0_workspace_bytes(65, 5120, 1536, 160, 6) == 0
+    assert lib.moe_q4_0_workspace_bytes(1, 5120, 1536, 160, 9) == 0
+    assert lib.moe_q4_0_workspace_bytes(1, 5120, 1530, 160, 6) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 1, 32, 1), -1),
+    ((FAKE, FAKE, FAKE, 1, 33, 1), -2),
+    ((FAKE + 2, FAKE, FAKE, 1, 32, 1), -3),
+])
+def test_gemm_rejects_bad_arguments(lib, args, code):
+    assert lib.q4_0_gemm(*args, None) == code
+
+
+def test_moe_rejects_bad_arguments(lib):
+    f = lib.moe_q4_0_decode
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert f(None, *ok[1:], 1, 5120, 1536, 160, 6, None, 0, None) == -1
+    assert f(*ok, 0, 5120, 1536, 160, 6, None, 0, None) == -1
+    assert f(*ok, 65, 5120, 1536, 160, 6, None, 0, None) == -2
+    assert f(*ok, 1, 5120, 1536, 160, 9, None, 0, None) == -2
+    assert f(*ok, 1, 5120, 1536, 1025, 6, None, 0, None) == -2
+    assert f(*ok, 1, 5121, 1536, 160, 6, None, 0, None) == -2
+    assert f(*ok, 1, 5120, 1536, 160, 6, None, 0, None) == -4
+    need = lib.moe_q4_0_workspace_bytes(1, 5120, 1536, 160, 6)
+    assert f(*ok, 1, 5120, 1536, 160, 6, FAKE + 64, need, None) == -3

@@ -1,0 +1,128 @@
+"""GPU parity of q4_0_gemv against the CPU oracle (needs an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_experts_amd import datagen
+from tests.golden_io import gemv_cases, handworked_block
+from tests.gpu_util import check_tol, dev, guarded, guards_intact, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-4
+
+
+def gemv(x: np.ndarray, B: np.ndarray, N: int) -> np.ndarray:
+    from moe_experts_amd import q4_0_gemv
+    return to_host(q4_0_gemv(to_dev(x), to_dev(B), N))
+
+
+SMALL = [(1, 1, 32), (1, 2, 64), (2, 31, 96), (3, 33, 256), (8, 64, 288), (1, 4097, 4128),
+         (5, 300, 160), (4, 1000, 512), (8, 4097, 96), (7, 129, 1024), (6, 2, 4128)]
+
+
+@pytest.mark.parametrize("M,K,N", SMALL)
+def test_gemv_small_shapes_match_oracle(M, K, N):
+    x = datagen.activations(M * 1000 + K, M, K)
+    B = datagen.q4_0_random(N + K, K, N)
+    ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+    check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
+
+
+def test_gemv_handworked():
+    qs, _, _, _ = handworked_block()
+    blk = lambda d: np.frombuffer(bytes([d & 255, d >> 8]) + qs, dtype=np.uint8)
+    B = np.stack([blk(0x3C00), blk(0x3800)]).reshape(2, 1, 18)
+    for xs, ys in gemv_cases():
+        y = gemv(np.array([xs], dtype=np.float32), B, 32)
+        assert (y[0] == np.array(ys, dtype=np.float32)).all(), y
+
+
+@pytest.mark.parametrize("M,K,N", [(1, 4096, 4096), (8, 11008, 4096), (3, 4096, 11008)])
+def test_gemv_integer_exact_bitwise(M, K, N):
+    g = np.random.Generator(np.random.PCG64(K + N + M))
+    q = g.integers(0, 16, size=(K, N), dtype=np.uint8)
+    d_bits = g.choice(np.array([0x3C00, 0x3800, 0x4000], dtype=np.uint16), size=(K, N // 32))
+    B = datagen.assemble(d_bits, datagen.pack_nibbles(q))
+    x = g.integers(-4, 5, size=(M, K)).astype(np.float32)
+    ref, _ = oracle.q4_0_matmul(x, B, N, K)
+    assert (gemv(x, B, N) == ref).all()
+
+
+def test_gemv_invariants_bitwise():
+    M, K, N = 4, 2048, 1536
+    x = datagen.activations(5, M, K)
+    B = datagen.q4_0_random(6, K, N)
+    y = gemv(x, B, N)
+    # determinism
+    assert (gemv(x, B, N) == y).all()
+    # doubling every scale doubles y bitwise
+    d = B[..., 0:2].copy().view(np.uint16)[..., 0]
+    assert (gemv(x, datagen.assemble(d + 0x0400, B[..., 2:]), N) == 2 * y).all()
+    # x * 2^-4 scales y bitwise
+    assert (gemv(x * np.float32(0.0625), B, N) == y * np.float32(0.0625)).all()
+    # zero scales and all-8 nibbles give zeros
+    Bz = B.copy(); Bz[..., 0:2] = 0
+    assert (gemv(x, Bz, N) == 0).all()
+    B8 = B.copy(); B8[..., 2:] = 0x88
+    assert (gemv(x, B8, N) == 0).all()
+    # one-hot x selects the dequantized row bitwise
+    W = oracle.dequant_rows(B, N, 0, K)
+    oh = np.zeros((3, K), dtype=np.float32)
+    oh[0, 0] = 1; oh[1, 777] = 1; oh[2, K - 1] = 1
+    y1 = gemv(oh, B, N)
+    assert (y1[0] == W[0]).all() and (y1[1] == W[777]).all() and (y1[2] == W[K - 1]).all()
+
+
+def test_gemv_batch_invariance_bitwise():
+    K, N = 4096, 11008
+    x = datagen.activations(9, 8, K)
+    B = datagen.q4_0_random(10, K, N)
+    y8 = gemv(x, B, N)
+    for m in (0, 3, 7):
+        assert (gemv(x[m:m + 1], B, N)[0] == y8[m]).all()
+    assert (gemv(x[2:5], B, N) == y8[2:5]).all()
+
+
+def test_gemv_guard_bands_untouched():
+    from moe_experts_amd import q4_0_gemv
+    M, K, N = 3, 1000, 4128
+    x = datagen.activations(11, M, K)
+    B = datagen.q4_0_random(12, K, N)
+    full, yv = guarded(M * N)
+    q4_0_gemv(to_dev(x), to_dev(B), N, y=yv.view(M, N))
+    torch.cuda.synchronize()
+    assert guards_intact(full, M * N)
+    ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+    check_tol(to_host(yv).reshape(M, N), ref, bnd, TOL)
+
+
+def test_gemv_single_vector_4096():
+    # single GEMV, 4096 x 4096, batch 1, seeds of the small workload
+    c = datagen.GEMV_4096
+    x = datagen.activations(c["x_seed"], 1, c["K"])
+    B = datagen.q4_0_random(c["b_seed"], c["K"], c["N"])
+    ref, bnd = oracle.q4_0_matmul(x, B, c["N"], c["K"])
+    check_tol(gemv(x, B, c["N"]), ref, bnd, TOL, "gemv 4096")
+
+
+@pytest.mark.parametrize("name,K,N,seed", datagen.DENSE_7B_SHAPES)
+def test_gemv_dense_7b_shapes(name, K, N, seed):
+    B = datagen.q4_0_random(seed, K, N)
+    Bd = to_dev(B)
+    from moe_experts_amd import q4_0_gemv
+    for M in datagen.DENSE_7B_BATCHES:
+        x = datagen.activations(datagen.dense_x_seed(M), M, K)
+        ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+        got = to_host(q4_0_gemv(to_dev(x), Bd, N))
+        check_tol(got, ref, bnd, TOL, f"{name} M={M}")
+
+
+def test_gemv_rejects_mismatched_tensors():
+    from moe_experts_amd import q4_0_gemv
+    x = torch.zeros((1, 64), device=dev())
+    B = torch.zeros((64 * 2 * 18 - 1,), dtype=torch.uint8, device=dev())
+    with pytest.raises(ValueError):
+        q4_0_gemv(x, B, 64)
+    with pytest.raises(TypeError):
+        q4_0_gemv(x.double(), torch.zeros((64 * 2 * 18,), dtype=torch.uint8, device=dev()), 64)
