@@ -62,7 +62,7 @@ def parse():
 
 
 class EventTimer:
-    """Per-launch durations from HIP events recorded on the launching stream."""
+    """Durations from HIP events recorded on the launching stream."""
 
     def __init__(self, torch):
         self.torch = torch
@@ -82,6 +82,32 @@ class EventTimer:
         return sum(s.elapsed_time(e) for s, e in ps) / len(ps) if ps else float("nan")
 
 
+def capture(torch, fn):
+    """Capture fn's kernel launches (made on the current stream) into a HIP graph."""
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, graphs, reps, per_replay):
+    """Mean time per unit of work: replay the graphs round robin between two
+    events; each replay holds `per_replay` units (steps or launches)."""
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for r in range(reps):
+        graphs[r % len(graphs)].replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) * 1e-3 / (reps * per_replay)
+
+
 # ---------------------------------------------------------------------------
 # dense decode linears
 # ---------------------------------------------------------------------------
@@ -99,47 +125,56 @@ def bench_dense(torch, dev, steps, warmup):
               for K in sorted({K for _, K, _, _ in shapes})} for M in Ms}
     ys = {(M, i): torch.empty((M, N), dtype=torch.float32, device=dev)
           for M in Ms for i, (_, _, N, _) in enumerate(shapes)}
-    need = max(q4_0_gemv_workspace_bytes(M, N, K) for M in Ms for _, K, N, _ in shapes)
-    ws = torch.zeros(max(need, 256), dtype=torch.uint8, device=dev)
 
+    need = max(q4_0_gemv_workspace_bytes(M, N, K) for M in Ms for _, K, N, _ in shapes)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     calls = [(M, i) for M in Ms for i in range(len(shapes))]
     step_bytes = sum(q4_bytes(K, N) + 4 * M * K + 4 * M * N
                      for M in Ms for _, K, N, _ in shapes)
 
-    def step(r, timer=None):
-        ws_ = copies[r % R]
+    def step(r):
+        w = copies[r % R]
         for (M, i) in calls:
             _, K, N, _ = shapes[i]
-            f = lambda: q4_0_gemv(xs[M][K], ws_[i], N, y=ys[(M, i)], ws=ws)
-            if timer is None:
-                f()
-            else:
-                timer.run((M, i), f)
+            q4_0_gemv(xs[M][K], w[i], N, y=ys[(M, i)], ws=ws)
 
+    # one HIP graph per weight copy, each holding one whole step (12 GEMVs);
+    # replaying them round robin keeps the host out of the timed region
     for r in range(warmup):
         step(r)
+    graphs = [capture(torch, lambda r=r: step(r)) for r in range(R)]
+    for r in range(warmup):
+        graphs[r % R].replay()
     torch.cuda.synchronize()
-    timer = EventTimer(torch)
     t0 = time.perf_counter()
+    s_ev = torch.cuda.Event(enable_timing=True)
+    e_ev = torch.cuda.Event(enable_timing=True)
+    s_ev.record()
     for r in range(steps):
-        step(warmup + r, timer)
+        graphs[(warmup + r) % R].replay()
+    e_ev.record()
     torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+    wall = (time.perf_counter() - t0) / steps
+    dt = s_ev.elapsed_time(e_ev) * 1e-3 / steps
 
-    per_call = {}
+    # per call: graphs of 8 back-to-back launches (rotating copies) of each call
+    per_call, per_M, call_s = {}, {}, {}
     for (M, i) in calls:
         name, K, N, _ = shapes[i]
-        ms = timer.mean_ms((M, i))
+        gs = [capture(torch, lambda c=c: [q4_0_gemv(xs[M][K], copies[(c * 8 + u) % R][i], N,
+                                                    y=ys[(M, i)], ws=ws) for u in range(8)])
+              for c in range(2)]
+        t = time_graph(torch, gs, 10, 8)
+        call_s[(M, i)] = t
         b = q4_bytes(K, N) + 4 * M * K + 4 * M * N
-        per_call[f"{name}_M{M}"] = {"us": round(ms * 1e3, 2), "GBps": round(b / (ms * 1e-3) / 1e9, 1),
-                                    "TFLOPs": round(2 * M * K * N / (ms * 1e-3) / 1e12, 2)}
-    per_M = {}
+        per_call[f"{name}_M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
+                                    "TFLOPs": round(2 * M * K * N / t / 1e12, 2)}
     for M in Ms:
-        ms = sum(timer.mean_ms((M, i)) for i in range(len(shapes)))
+        t = sum(call_s[(M, i)] for i in range(len(shapes)))
         b = sum(q4_bytes(K, N) + 4 * M * K + 4 * M * N for _, K, N, _ in shapes)
-        per_M[M] = (ms, b)
-    return dict(step_s=dt, step_bytes=step_bytes, per_call=per_call, per_M=per_M, R=R,
-                host=host, timer=timer, shapes=shapes, Ms=Ms)
+        per_M[M] = (t * 1e3, b)
+    return dict(step_s=dt, wall_s=wall, step_bytes=step_bytes, per_call=per_call, per_M=per_M,
+                R=R, host=host, shapes=shapes, Ms=Ms)
 
 
 def dense_roofline(d):
@@ -236,14 +271,11 @@ def bench_moe(torch, dev, steps, warmup):
 
         for r in range(warmup):
             call(r)
-        torch.cuda.synchronize()
+        # one graph per (layer copy, routing) combination in use
         n = max(steps, 16)
-        t0 = time.perf_counter()
-        for r in range(n):
-            call(warmup + r)
-        torch.cuda.synchronize()
-        dt = (time.perf_counter() - t0) / n
-        U = np.mean([uniq[(warmup + r) % len(routes)] for r in range(n)])
+        graphs = [capture(torch, lambda r=r: call(r)) for r in range(16)]
+        dt = time_graph(torch, graphs, n, 1)
+        U = np.mean([uniq[r % len(routes)] for r in range(16)])
         b = U * 3 * mat + 2 * 4 * T * H + T * topk * 8
         res[label] = {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 2),
                       "GBps": round(b / dt / 1e9, 1), "hbm_frac": round(b / dt / 1e9 / HBM_PEAK_GBS, 4),
@@ -266,12 +298,8 @@ def bench_prefill(torch, dev, steps, warmup):
         Y = torch.empty((M, N), dtype=torch.float32, device=dev)
         for _ in range(warmup):
             q4_0_gemm(X, B, N, Y=Y)
-        torch.cuda.synchronize()
-        timer = EventTimer(torch)
-        for _ in range(max(steps, 10)):
-            timer.run("g", lambda: q4_0_gemm(X, B, N, Y=Y))
-        torch.cuda.synchronize()
-        ms = timer.mean_ms("g")
+        g = capture(torch, lambda: [q4_0_gemm(X, B, N, Y=Y) for _ in range(4)])
+        ms = time_graph(torch, [g], max(steps, 10) // 4 + 1, 4) * 1e3
         tf = 2 * M * N * K / (ms * 1e-3) / 1e12
         res[f"N{N}"] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
                         "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
@@ -298,7 +326,7 @@ def main():
 
     d = bench_dense(torch, dev, args.steps, args.warmup)
     value = d["step_bytes"] / d["step_s"] / 1e9
-    log(f"[dense] step {d['step_s'] * 1e3:.3f} ms, {value:.1f} GB/s")
+    log(f"[dense] step {d['step_s'] * 1e3:.3f} ms (wall {d['wall_s'] * 1e3:.3f} ms), {value:.1f} GB/s")
     for k, v in d["per_call"].items():
         log(f"  {k:22s} {v}")
     roof = dense_roofline(d)

@@ -26,10 +26,9 @@
  *    reports a launch failure returned by the HIP runtime.
  *  - Workspace: entry points that take `ws` need at least the number of bytes
  *    the matching *_workspace_bytes() returns, 256-byte aligned device memory.
- *    Before its first use a workspace must be filled with zeros; every call
- *    leaves it zeroed again (its completion counters reset themselves). One
- *    workspace serves one call at a time: calls that overlap in time (for
- *    example on two streams) need separate workspaces.
+ *    Its contents are scratch (no initialisation needed). One workspace serves
+ *    one call at a time: calls that overlap in time (for example on two
+ *    streams) need separate workspaces.
  *  - Determinism: for the same arguments a call produces bitwise identical
  *    results (fixed reduction order, no floating-point atomics).
  */
@@ -79,13 +78,15 @@ const char* q4_strerror(int status);
  * The article's fused matmul_q4_0(A, B, C, M, N, K) (§3.4), for decode batches.
  *   x   fp32 [M][K], 4-byte aligned      B  Q4_0 [K][N/32] blocks, 2-byte aligned
  *   y   fp32 [M][N], 4-byte aligned, overwritten
- *   1 <= M <= Q4_GEMV_MAX_M, K >= 1, N >= 32, N % 32 == 0, K*N/32 < 2^31 blocks.
- *   ws/ws_bytes: workspace of q4_0_gemv_workspace_bytes(M, N, K) bytes.
+ *   1 <= M <= Q4_GEMV_MAX_M, K >= 1, N >= 32, N % 32 == 0; B, x and y each
+ *   smaller than 2 GiB.
+ *   ws/ws_bytes: workspace of q4_0_gemv_workspace_bytes(M, N, K) bytes (K-split
+ *   partial sums; may be 0, then ws may be NULL).
  * Accumulation is fp32; each product x * (q - 8) * d is formed in fp32.
  * ------------------------------------------------------------------------- */
 size_t q4_0_gemv_workspace_bytes(int M, int N, int K);
-int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K,
-              void* ws, size_t ws_bytes, void* stream);
+int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K, void* ws,
+              size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Prefill GEMM: Y[M x N] = X[M x K] . deq(B[K x N]) on the fp16 matrix cores.

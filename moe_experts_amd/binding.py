@@ -82,8 +82,8 @@ def _dev(t: torch.Tensor, name: str, dtype, numel: int):
     return t.data_ptr()
 
 
-# Workspaces: one zero-filled buffer per (device, stream), grown on demand.
-# The library leaves a workspace zeroed after every call, so it is reused as is.
+# Workspaces: one scratch buffer per (device, stream), grown on demand. Calls
+# on one stream run in order, so they can share it.
 _ws_lock = threading.Lock()
 _ws_cache: dict = {}
 
@@ -96,7 +96,7 @@ def workspace(nbytes: int, device) -> torch.Tensor | None:
     with _ws_lock:
         buf = _ws_cache.get(key)
         if buf is None or buf.numel() < nbytes:
-            buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+            buf = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
             _ws_cache[key] = buf
         return buf
 

@@ -2,26 +2,24 @@
 //
 // The fused dequantize-inside-the-inner-loop matmul of the "2000-line C++
 // DeepSeek inference engine" article (§3.4 matmul_q4_0), re-designed for
-// gfx950. B is row-major with blocks along N, so one output column's weights
-// are spread over all K rows; the kernel therefore splits both N and K:
+// gfx950. B is row-major with blocks along N, so a column's weights are spread
+// over all K rows while each 128-byte cache line holds ~7 consecutive blocks of
+// one row. To keep memory requests full, a workgroup reads whole 16-block row
+// segments (288 bytes), and to still have hundreds of workgroups on a 4096-row
+// matrix it owns only a K range of those columns (split-K):
 //
-//   * a workgroup (256 lanes) owns a column tile of Jt blocks (32*Jt outputs)
-//     and a K range of Kt rows; its lanes form P = 256 / (Jt*LPB) row phases,
-//     and each lane owns one block column (LPB = 1) or half of one (LPB = 2),
-//     walking rows k0+phase, k0+phase+P, ...;
-//   * each lane reads its block share with one unaligned dwordx4/dwordx2 load
-//     plus one 2-byte scale load; a row's shares are adjacent, so a wave's
-//     loads cover contiguous 18*Jt-byte row segments;
-//   * x for the K range is staged once in LDS (k-major, M values per k);
-//   * nibbles are unpacked in registers (masked bytes, v_cvt_f32_ubyteN) and
-//     accumulated with one fp32 FMA per weight and activation row;
-//   * the row phases are reduced through LDS in a fixed order; split-K partials
-//     go to the workspace and the last workgroup of each column tile (completion
-//     ticket) sums them in split order and writes y. No floating-point atomics:
-//     results are deterministic.
-//
-// The tile shape depends only on (N, K), never on M, so row m of y is bitwise
-// the same whatever the batch it is computed in.
+//   1. gemv_q4_0_kernel: workgroup (c, s) owns block columns 16c..16c+15 and
+//      rows [s*Kt, (s+1)*Kt). Its lanes form row phases of 16 (or 32) lanes;
+//      each lane loads every one of its rows (one 16-byte or 8-byte unaligned
+//      buffer load plus the 2-byte scale, and the activations) before using
+//      any, unpacks the nibbles in registers (masked bytes, v_cvt_f32_ubyteN)
+//      and accumulates one fp32 FMA per weight and activation row. The row
+//      phases are summed through LDS in a fixed order; the workgroup writes its
+//      partial sums to the workspace (or y directly when K is not split).
+//   2. gemv_q4_0_reduce_kernel: y[m][n] = sum over the K splits, in split order.
+// Cross-workgroup hand-off at agent scope costs an L2 write-back per workgroup
+// on this GPU, so the split-K sum is a second kernel instead: no atomics, no
+// fences, deterministic results.
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
 
@@ -32,140 +30,160 @@ struct GemvArgs {
   const float* __restrict__ x;
   const uint8_t* __restrict__ B;
   float* __restrict__ y;
-  float* __restrict__ part;    // [C][S][M][Jt*32] split-K partials
-  unsigned* __restrict__ cnt;  // [C] completion tickets
-  int N, K, NB;
-  int Jt, Kt, S, C, Lr, P;
+  float* __restrict__ part;  // [S][M][N] split-K partials
+  int M, N, K, NB;
+  int Jt, Lr, P, C, Kt, S;
 };
 
-template <int M, int LPB, int U>
-__global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
-  constexpr int XS = x_stride<M>();
-  extern __shared__ float smem[];
-  __shared__ unsigned last_flag;
+// Rows per lane loaded before any is used, sized to the register budget.
+template <int M, int LPB>
+constexpr int rows_per_batch() {
+  return M == 1 ? 16 : (M == 2 ? 12 : (M <= 4 ? 8 : 4));
+}
 
-  const int t = threadIdx.x;
+template <int M, int LPB>
+__global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int c = L % a.C;
   const int s = L / a.C;
-  const int k0 = s * a.Kt;
-  const int rows = min(a.Kt, a.K - k0);
-  const int j0 = c * a.Jt;
-
-  // Stage x[:, k0:k0+rows] in LDS as smem[kk*XS + m] (k-major).
-  for (int idx = t; idx < M * rows; idx += kThreads) {
-    const int m = idx / rows;
-    const int kk = idx - m * rows;
-    smem[kk * XS + m] = a.x[(size_t)m * a.K + k0 + kk];
-  }
-  __syncthreads();
-
+  SplitTile g;
+  g.B = a.B;
+  g.NB = a.NB;
+  g.K = a.K;
+  g.j0 = c * a.Jt;
+  g.Jt = a.Jt;
+  g.k0 = s * a.Kt;
+  g.rows = min(a.Kt, a.K - g.k0);
+  g.Lr = a.Lr;
+  g.P = a.P;
+  int xoff[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xoff[m] = m * a.K;
   float acc[M][32 / LPB];
   float corr[M];
-  const TileGeom g{a.B, a.NB, j0, k0, rows, a.Lr, a.P};
-  tile_accumulate<M, LPB, U>(g, smem, acc, corr);
+  tile_accumulate<M, LPB, rows_per_batch<M, LPB>()>(g, a.x, (uint32_t)(4 * M * a.K), xoff, acc,
+                                                     corr);
   finish_part<M, LPB>(acc, corr);
-
-  const int width = a.Jt * kBlockWeights;  // output columns of the tile
-  const int ncols = min(width, (a.NB - j0) * kBlockWeights);
-  float* __restrict__ ycol = a.y + (size_t)j0 * kBlockWeights;
-  __syncthreads();  // the staged x is no longer needed
-  if (a.S == 1) {
-    reduce_phases<M, LPB>(acc, smem, a.Lr, a.P, ncols,
-                          [&](int m, int o, float v) { ycol[(size_t)m * a.N + o] = v; });
-    return;
-  }
-  float* __restrict__ my_part = a.part + ((size_t)c * a.S + s) * (size_t)M * width;
+  const int n0 = g.j0 * kBlockWeights;
+  const int ncols = min(a.Jt, a.NB - g.j0) * kBlockWeights;
+  float* dst = (a.S == 1) ? a.y : a.part + (size_t)s * M * a.N;
   reduce_phases<M, LPB>(acc, smem, a.Lr, a.P, ncols,
-                        [&](int m, int o, float v) { my_part[(size_t)m * width + o] = v; });
-
-  // Split-K: the last workgroup of this column tile sums the partials in
-  // split order and writes y.
-  if (!arrive_last(a.cnt + c, (unsigned)a.S, &last_flag)) return;
-  const float* __restrict__ tile_part = a.part + (size_t)c * a.S * (size_t)M * width;
-  for (int idx = t; idx < M * ncols; idx += kThreads) {
-    const int m = idx / ncols;
-    const int o = idx - m * ncols;
-    float sum = 0.0f;
-    for (int ss = 0; ss < a.S; ++ss) sum += tile_part[((size_t)ss * M + m) * width + o];
-    ycol[(size_t)m * a.N + o] = sum;
-  }
+                        [&](int m, int o, float v) { dst[(size_t)m * a.N + n0 + o] = v; });
 }
 
-#ifndef Q4_GEMV_UNROLL
-#define Q4_GEMV_UNROLL 4
-#endif
+__global__ __launch_bounds__(256) void gemv_q4_0_reduce_kernel(const float* __restrict__ part,
+                                                               float* __restrict__ y, int MN,
+                                                               int S) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= MN) return;
+  y[i] = sum_strided(part + i, (size_t)MN, S);
+}
+
+template <int M, int LPB>
+hipError_t launch_one(const GemvArgs& a, hipStream_t st) {
+  const size_t lds = sizeof(float) * phase_lds_floats<LPB>();
+  hipLaunchKernelGGL((gemv_q4_0_kernel<M, LPB>), dim3(a.C * a.S), dim3(kThreads), lds, st, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || a.S == 1) return err;
+  const int MN = M * a.N;
+  hipLaunchKernelGGL(gemv_q4_0_reduce_kernel, dim3((MN + 255) / 256), dim3(256), 0, st, a.part,
+                     a.y, MN, a.S);
+  return hipGetLastError();
+}
 
 template <int M>
-hipError_t launch_m(const GemvArgs& a, int lpb, size_t lds, hipStream_t st) {
-  const dim3 grid(a.C * a.S), block(kThreads);
-  if (lpb == 1)
-    hipLaunchKernelGGL((gemv_q4_0_kernel<M, 1, Q4_GEMV_UNROLL>), grid, block, lds, st, a);
-  else
-    hipLaunchKernelGGL((gemv_q4_0_kernel<M, 2, Q4_GEMV_UNROLL>), grid, block, lds, st, a);
-  return hipGetLastError();
+hipError_t launch_m(const GemvArgs& a, int lpb, hipStream_t st) {
+  if constexpr (M <= 4) {
+    if (lpb == 1) return launch_one<M, 1>(a, st);
+  }
+  return launch_one<M, 2>(a, st);
 }
 
 }  // namespace
 
-// Tile plan. Only (N, K) decide it, so every batch size uses the same
-// per-column summation order.
+// Tile plan: 16-block column tiles; whole blocks per lane for M <= 4, half
+// blocks for M > 4 (register budget). The K split S minimizes a simple time
+// model: the larger of the HBM time (weights plus the partial sums written and
+// read back) and the VALU time (fp32 lane operations per weight, over the CUs
+// the grid covers), divided by how evenly the workgroups spread over the 256
+// CUs (a CU holding one more workgroup than the others sets the kernel time),
+// plus a latency term per load batch and the cost of the reduce kernel.
 GemvPlan plan_gemv(int M, int N, int K) {
   GemvPlan p{};
+  constexpr int kCUs = 256;
+  constexpr double kHbm = 5.5e12;       // attainable bytes/s of a streaming read
+  constexpr double kValu = 39.3e12;     // fp32 lane operations per second (no packed math)
   const int NB = N / kBlockWeights;
-  p.LPB = 2;
+  p.LPB = (M <= 4) ? 1 : 2;
   p.Jt = NB < 16 ? NB : 16;
   p.Lr = p.Jt * p.LPB;
   p.P = kThreads / p.Lr;
   p.C = (NB + p.Jt - 1) / p.Jt;
-  // K split: aim at ~512 workgroups, at least 8 rows per lane, at most 1024
-  // rows per workgroup (x staging <= 32 KB of LDS for M = 8).
-  const int target_wg = 512;
-  int S = (target_wg + p.C - 1) / p.C;
-  const int s_max = (K + 8 * p.P - 1) / (8 * p.P);
-  if (S > s_max) S = s_max;
-  if (S < 1) S = 1;
-  int Kt = (K + S - 1) / S;
-  Kt = (Kt + p.P - 1) / p.P * p.P;
-  if (Kt > 1024) Kt = 1024;
-  p.Kt = Kt;
-  p.S = (K + Kt - 1) / Kt;
-  const size_t xs_floats = (size_t)p.Kt * 8;  // sized for the widest stride
-  const size_t red_floats = (size_t)(32 / p.LPB) * kRedStride;
-  p.lds_bytes = 4 * (xs_floats > red_floats ? xs_floats : red_floats);
-  const size_t cnt_bytes = ((size_t)p.C * 4 + 255) / 256 * 256;
-  p.part_offset = cnt_bytes;
-  p.ws_bytes = p.S > 1 ? cnt_bytes + (size_t)p.C * p.S * M * p.Jt * kBlockWeights * 4 : 0;
-  (void)M;
+  const int rb = M == 1 ? 16 : (M == 2 ? 12 : (M <= 4 ? 8 : 4));
+  // lane operations per weight: per block (LPB = 1) one scale convert, 2M
+  // scale products and corrections, 8 masks, 32 nibble converts, 32M FMAs
+  const double opw = p.LPB == 1 ? (41.0 + 34.0 * M) / 32.0 : (21.0 + 18.0 * M) / 16.0;
+  const double wbytes = (double)K * NB * kBlockBytes;
+  double best = 1e30;
+  int best_kt = ((K + p.P - 1) / p.P) * p.P;
+  int last_S = -1;
+  for (int s = 1; s <= 4096; ++s) {
+    int kt = (K + s - 1) / s;
+    kt = (kt + p.P - 1) / p.P * p.P;
+    const int S = (K + kt - 1) / kt;
+    if (S == last_S) continue;
+    last_S = S;
+    const int rows_per_lane = kt / p.P;
+    if (rows_per_lane > 4 * rb) continue;
+    const int wgs = p.C * S;
+    const int per_cu = (wgs + kCUs - 1) / kCUs;
+    const double balance = (double)wgs / ((double)per_cu * kCUs);
+    const double fill = wgs >= kCUs ? 1.0 : (double)wgs / kCUs;
+    const double pbytes = S > 1 ? (double)S * M * N * 4.0 : 0.0;
+    const double t_mem = (wbytes + 2.0 * pbytes) / kHbm;
+    const double t_valu = (double)K * N * opw / (kValu * fill);
+    const int batches = (rows_per_lane + rb - 1) / rb;
+    double t = (t_mem > t_valu ? t_mem : t_valu) / balance + 1.5e-6 + 0.5e-6 * (batches - 1);
+    if (S > 1) t += 2.0e-6 + pbytes / 5.0e12;
+    if (t < best) {
+      best = t;
+      best_kt = kt;
+    }
+    if (S >= K) break;
+  }
+  p.Kt = best_kt;
+  p.S = (K + p.Kt - 1) / p.Kt;
+  p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
   return p;
 }
 
-hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N, int K,
-                       void* ws, const GemvPlan& p, hipStream_t st) {
+hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N, int K, void* ws,
+                       const GemvPlan& p, hipStream_t st) {
   GemvArgs a;
   a.x = x;
   a.B = B;
   a.y = y;
-  a.cnt = static_cast<unsigned*>(ws);
-  a.part = ws ? reinterpret_cast<float*>(static_cast<uint8_t*>(ws) + p.part_offset) : nullptr;
+  a.part = static_cast<float*>(ws);
+  a.M = M;
   a.N = N;
   a.K = K;
   a.NB = N / kBlockWeights;
   a.Jt = p.Jt;
-  a.Kt = p.Kt;
-  a.S = p.S;
-  a.C = p.C;
   a.Lr = p.Lr;
   a.P = p.P;
+  a.C = p.C;
+  a.Kt = p.Kt;
+  a.S = p.S;
   switch (M) {
-    case 1: return launch_m<1>(a, p.LPB, p.lds_bytes, st);
-    case 2: return launch_m<2>(a, p.LPB, p.lds_bytes, st);
-    case 3: return launch_m<3>(a, p.LPB, p.lds_bytes, st);
-    case 4: return launch_m<4>(a, p.LPB, p.lds_bytes, st);
-    case 5: return launch_m<5>(a, p.LPB, p.lds_bytes, st);
-    case 6: return launch_m<6>(a, p.LPB, p.lds_bytes, st);
-    case 7: return launch_m<7>(a, p.LPB, p.lds_bytes, st);
-    case 8: return launch_m<8>(a, p.LPB, p.lds_bytes, st);
+    case 1: return launch_m<1>(a, p.LPB, st);
+    case 2: return launch_m<2>(a, p.LPB, st);
+    case 3: return launch_m<3>(a, p.LPB, st);
+    case 4: return launch_m<4>(a, p.LPB, st);
+    case 5: return launch_m<5>(a, p.LPB, st);
+    case 6: return launch_m<6>(a, p.LPB, st);
+    case 7: return launch_m<7>(a, p.LPB, st);
+    case 8: return launch_m<8>(a, p.LPB, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,20 +6,23 @@
 // expert weights are touched per token and the work is bandwidth-bound. The
 // MoE module's gate hands the experts top-k ids and weights, and the expert
 // outputs are gathered on one device. Here the whole layer runs on one GPU as
-// four kernels on one stream (no host round trip, capturable in a graph):
+// five kernels on one stream (no host round trip, capturable in a graph):
 //
-//   1. route    : one workgroup turns topk_ids into expert groups: the (token,
-//                 slot) pairs sorted by expert (stable), and work items of at
-//                 most 8 pairs of one expert; it also clears the tickets.
-//   2. gate/up  : for each work item, column tile and K split, the expert's
-//                 gate and up matrices are streamed once for all its pairs
-//                 (GEMV tiles of the dense decode kernel); the last workgroup
-//                 of a tile group applies h = SiLU(g) * u.
-//   3. down     : yd = h . Wd_e per pair, split-K with a completion ticket.
-//   4. combine  : out[t] = sum over slots in order 0..topk-1 of w[t][s] * yd.
-//
-// Tile shapes depend only on (H, I), so a token's result is bitwise the same
-// whatever other tokens share the call (batch invariance).
+//   1. route    : one workgroup groups the (token, slot) pairs by expert
+//                 (stable order) into work items of at most MC pairs of one
+//                 expert (MC = 8, or 1 for a single token).
+//   2. gate/up  : split-K GEMV tiles of the dense decode kernel over the
+//                 routed experts' gate and up matrices; a tile streams its
+//                 expert's 8-block row segments once for all pairs of its item
+//                 and writes per-pair partial sums.
+//   3. act      : h = SiLU(sum of gate partials) * (sum of up partials).
+//   4. down     : split-K tiles of h . Wd_e, per-pair partial sums.
+//   5. combine  : out[t] = sum over slots in order 0..topk-1 of
+//                 w[t][s] * (sum of the slot's down partials).
+// No atomics and no cross-workgroup hand-off inside a kernel: deterministic.
+// The tile shapes depend only on (H, I), never on T or on the item sizes, so
+// a token's result is bitwise the same whatever other tokens share the call
+// (batch invariance).
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
 
@@ -27,231 +30,234 @@ namespace q4 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kMaxChunk = 8;  // pairs per work item
-constexpr int kLPB = 2;       // lanes per block in the expert GEMV tiles
+constexpr int kMaxChunk = 8;  // pairs per work item (MC <= kMaxChunk)
+constexpr int kLPB = 2;       // half-block lane shares, for every item size
+constexpr int kJt = 8;        // block columns per tile: 144-byte row segments
 
-struct WorkItem {
-  int e, start, cnt, pad;
+struct ItemRec {
+  int e, cnt, pad0, pad1;
+  int pairs[kMaxChunk];  // pair index t * topk + slot, in stable expert order
 };
+
+template <int M>
+constexpr int moe_rows_per_batch() {
+  return M == 1 ? 20 : (M == 2 ? 12 : (M <= 4 ? 8 : 4));
+}
 
 // ---------------------------------------------------------------------------
 // 1. routing prologue
 // ---------------------------------------------------------------------------
 struct RouteArgs {
-  const int32_t* __restrict__ ids;  // [T*topk]
-  int npairs, E;
-  int* __restrict__ pair_sorted;    // [npairs]
-  WorkItem* __restrict__ items;     // [max_items]
+  const int32_t* __restrict__ ids;  // [npairs]
+  int npairs, E, MC;
+  ItemRec* __restrict__ items;      // [max_items]
   int* __restrict__ n_items;
-  unsigned* __restrict__ tickets;   // counters to clear
-  int n_tickets;
 };
 
-// Inclusive prefix sum over kRouteThreads values held one per lane.
-__device__ int block_inclusive_scan(int v, int* buf) {
-  const int t = threadIdx.x;
-  buf[t] = v;
-  __syncthreads();
-  for (int off = 1; off < kRouteThreads; off <<= 1) {
-    const int add = (t >= off) ? buf[t - off] : 0;
-    __syncthreads();
-    buf[t] += add;
-    __syncthreads();
+// Inclusive prefix sum over one value per lane of the whole workgroup.
+__device__ int block_inclusive_scan(int v, int* wsum) {
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x / kWaveSize;
+#pragma unroll
+  for (int o = 1; o < kWaveSize; o <<= 1) {
+    const int n = __shfl_up(v, o);
+    if (lane >= o) v += n;
   }
-  const int r = buf[t];
+  if (lane == kWaveSize - 1) wsum[wave] = v;
   __syncthreads();
-  return r;
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += wsum[w];
+  __syncthreads();
+  return v + add;
 }
 
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   __shared__ int s_ids[Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK];
-  __shared__ int s_rank[Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK];
-  __shared__ int s_count[kRouteThreads];
-  __shared__ int s_scan[kRouteThreads];
+  __shared__ int s_cnt[Q4_MOE_MAX_E];
+  __shared__ int s_off[Q4_MOE_MAX_E];
+  __shared__ int s_sorted[Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK];
+  __shared__ int s_wsum[kRouteThreads / kWaveSize];
   const int t = threadIdx.x;
 
-  for (int i = t; i < a.n_tickets; i += kRouteThreads) a.tickets[i] = 0u;
-  s_count[t] = 0;
+  s_cnt[t] = 0;
   for (int p = t; p < a.npairs; p += kRouteThreads) s_ids[p] = a.ids[p];
   __syncthreads();
+  for (int p = t; p < a.npairs; p += kRouteThreads) {
+    const int e = s_ids[p];
+    if (e >= 0 && e < a.E) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
 
-  // Rank of each valid pair among the earlier pairs of its expert (stable order).
+  // Per-expert offsets into the sorted pair list and into the item list.
+  const int cnt = (t < a.E) ? s_cnt[t] : 0;
+  const int nch = (cnt + a.MC - 1) / a.MC;
+  const int off = block_inclusive_scan(cnt, s_wsum) - cnt;
+  const int item_incl = block_inclusive_scan(nch, s_wsum);
+  s_off[t] = off;
+  if (t == kRouteThreads - 1) *a.n_items = item_incl;
+  __syncthreads();
+
+  // Stable placement: pair p goes after the earlier pairs of its expert.
   for (int p = t; p < a.npairs; p += kRouteThreads) {
     const int e = s_ids[p];
     if (e < 0 || e >= a.E) continue;
     int rank = 0;
     for (int q = 0; q < p; ++q) rank += (s_ids[q] == e) ? 1 : 0;
-    s_rank[p] = rank;
-    atomicAdd(&s_count[e], 1);
+    s_sorted[s_off[e] + rank] = p;
   }
   __syncthreads();
 
-  const int cnt = (t < a.E) ? s_count[t] : 0;
-  const int nch = (cnt + kMaxChunk - 1) / kMaxChunk;
-  const int off_incl = block_inclusive_scan(cnt, s_scan);
-  const int item_incl = block_inclusive_scan(nch, s_scan);
-  const int off = off_incl - cnt;
-  const int item_off = item_incl - nch;
-  s_count[t] = off;  // reuse as the expert's start in pair_sorted
-  if (t == kRouteThreads - 1) *a.n_items = item_incl;
-  __syncthreads();
-
-  for (int p = t; p < a.npairs; p += kRouteThreads) {
-    const int e = s_ids[p];
-    if (e < 0 || e >= a.E) continue;
-    a.pair_sorted[s_count[e] + s_rank[p]] = p;
-  }
+  const int item0 = item_incl - nch;
   for (int i = 0; i < nch; ++i) {
-    WorkItem w;
-    w.e = t;
-    w.start = off + i * kMaxChunk;
-    w.cnt = min(kMaxChunk, cnt - i * kMaxChunk);
-    w.pad = 0;
-    a.items[item_off + i] = w;
+    ItemRec r;
+    r.e = t;
+    r.cnt = min(a.MC, cnt - i * a.MC);
+    r.pad0 = r.pad1 = 0;
+#pragma unroll
+    for (int m = 0; m < kMaxChunk; ++m)
+      r.pairs[m] = (m < r.cnt) ? s_sorted[off + i * a.MC + m] : 0;
+    a.items[item0 + i] = r;
   }
 }
 
 // ---------------------------------------------------------------------------
-// 2./3. expert GEMV tiles
+// 2./4. expert split-K tiles
 // ---------------------------------------------------------------------------
 struct ExpertArgs {
-  const float* __restrict__ xin;       // activations: x [T][H] (gate/up) or h [pairs][I] (down)
-  const uint8_t* __restrict__ W0;      // gate (gate/up) or down matrices
-  const uint8_t* __restrict__ W1;      // up matrices (gate/up only)
-  const int* __restrict__ pair_sorted;
-  const WorkItem* __restrict__ items;
+  const float* __restrict__ x;        // activations: x [T][H] or h [npairs][I]
+  uint32_t x_bytes;
+  const uint8_t* __restrict__ W0;     // gate (or down) matrices, E consecutive
+  const uint8_t* __restrict__ W1;     // up matrices (gate/up only)
+  const ItemRec* __restrict__ items;
   const int* __restrict__ n_items;
-  float* __restrict__ part;            // [nmat][C][S][npairs][width]
-  unsigned* __restrict__ tickets;      // [max_items][C]
-  float* __restrict__ out;             // h [pairs][I] (gate/up) or yd [pairs][H] (down)
-  size_t mat_bytes;                    // bytes of one expert matrix
-  int K, N, NB;                        // rows, columns, blocks per row of one matrix
-  int Jt, Lr, P, C, Kt, S, nmat;
-  int topk, npairs;
-  int x_by_token;                      // 1: xin row = pair / topk (gate/up); 0: xin row = pair
+  float* __restrict__ part;           // [nmat][S][npairs][N] partial sums
+  size_t mat_bytes;
+  int K, N, NB;                       // rows, columns, blocks per row of one matrix
+  int C, Kt, S, nmat, npairs;
+  int x_row_div;                      // activation row = pair / x_row_div, times K
 };
 
 template <int M>
-__device__ void expert_tile(const ExpertArgs& a, const WorkItem& it, int item, int mat, int c,
-                            int s, float* smem, unsigned* flag) {
-  constexpr int XS = x_stride<M>();
-  const int t = threadIdx.x;
-  const int k0 = s * a.Kt;
-  const int rows = min(a.Kt, a.K - k0);
-  const int j0 = c * a.Jt;
-
-  // Stage the activation rows of this item's pairs.
-  for (int idx = t; idx < M * rows; idx += kThreads) {
-    const int m = idx / rows;
-    const int kk = idx - m * rows;
-    const int pair = a.pair_sorted[it.start + m];
-    const int xrow = a.x_by_token ? pair / a.topk : pair;
-    smem[kk * XS + m] = a.xin[(size_t)xrow * a.K + k0 + kk];
-  }
-  __syncthreads();
-
+__device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int c, int s,
+                            float* smem) {
+  constexpr int Lr = kJt * kLPB;
+  SplitTile g;
+  g.B = (mat == 0 ? a.W0 : a.W1) + (size_t)it.e * a.mat_bytes;
+  g.NB = a.NB;
+  g.K = a.K;
+  g.j0 = c * kJt;
+  g.Jt = kJt;
+  g.k0 = s * a.Kt;
+  g.rows = min(a.Kt, a.K - g.k0);
+  g.Lr = Lr;
+  g.P = kThreads / Lr;
+  int xoff[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) xoff[m] = (it.pairs[m] / a.x_row_div) * a.K;
   float acc[M][32 / kLPB];
   float corr[M];
-  const uint8_t* W = (mat == 0 ? a.W0 : a.W1) + (size_t)it.e * a.mat_bytes;
-  const TileGeom g{W, a.NB, j0, k0, rows, a.Lr, a.P};
-  tile_accumulate<M, kLPB, 4>(g, smem, acc, corr);
+  tile_accumulate<M, kLPB, moe_rows_per_batch<M>()>(g, a.x, a.x_bytes, xoff, acc, corr);
   finish_part<M, kLPB>(acc, corr);
-
-  const int width = a.Jt * kBlockWeights;
-  const int ncols = min(width, (a.NB - j0) * kBlockWeights);
-  __syncthreads();
-  // partial slab of (mat, c, s), rows indexed by position in pair_sorted
-  float* __restrict__ slab =
-      a.part + (((size_t)mat * a.C + c) * a.S + s) * (size_t)a.npairs * width;
-  reduce_phases<M, kLPB>(acc, smem, a.Lr, a.P, ncols, [&](int m, int o, float v) {
-    slab[(size_t)(it.start + m) * width + o] = v;
+  const int n0 = g.j0 * kBlockWeights;
+  const int ncols = min(kJt, a.NB - g.j0) * kBlockWeights;
+  float* dst = a.part + ((size_t)mat * a.S + s) * a.npairs * a.N;
+  reduce_phases<M, kLPB>(acc, smem, Lr, g.P, ncols, [&](int m, int o, float v) {
+    dst[(size_t)it.pairs[m] * a.N + n0 + o] = v;
   });
-
-  if (!arrive_last(a.tickets + (size_t)item * a.C + c, (unsigned)(a.S * a.nmat), flag)) return;
-
-  // Last workgroup of (item, column tile): sum the split partials in order.
-  for (int idx = t; idx < M * ncols; idx += kThreads) {
-    const int m = idx / ncols;
-    const int o = idx - m * ncols;
-    const size_t row = (size_t)(it.start + m) * width + o;
-    float v0 = 0.0f;
-    for (int ss = 0; ss < a.S; ++ss)
-      v0 += a.part[(((size_t)0 * a.C + c) * a.S + ss) * (size_t)a.npairs * width + row];
-    const int pair = a.pair_sorted[it.start + m];
-    float res;
-    if (a.nmat == 2) {
-      float v1 = 0.0f;
-      for (int ss = 0; ss < a.S; ++ss)
-        v1 += a.part[(((size_t)1 * a.C + c) * a.S + ss) * (size_t)a.npairs * width + row];
-      res = v0 / (1.0f + expf(-v0)) * v1;  // SiLU(gate) * up
-    } else {
-      res = v0;
-    }
-    a.out[(size_t)pair * a.N + (size_t)j0 * kBlockWeights + o] = res;
-  }
 }
 
+template <int MC>
 __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
-  extern __shared__ float smem[];
-  __shared__ unsigned flag;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
   const int per_item = a.nmat * a.C * a.S;
   const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int item = L / per_item;
-  if (item >= *a.n_items) return;
+  // Both loads are issued before either is used (one round trip); the item
+  // array always has max_items records, so the read is in bounds.
+  const int n_items = *a.n_items;
+  const ItemRec it = a.items[item];
+  if (item >= n_items) return;
   int rest = L - item * per_item;
   const int c = rest % a.C;
   rest /= a.C;
   const int mat = rest % a.nmat;
   const int s = rest / a.nmat;
-  const WorkItem it = a.items[item];
-  switch (it.cnt) {
-    case 1: expert_tile<1>(a, it, item, mat, c, s, smem, &flag); break;
-    case 2: expert_tile<2>(a, it, item, mat, c, s, smem, &flag); break;
-    case 3: expert_tile<3>(a, it, item, mat, c, s, smem, &flag); break;
-    case 4: expert_tile<4>(a, it, item, mat, c, s, smem, &flag); break;
-    case 5: expert_tile<5>(a, it, item, mat, c, s, smem, &flag); break;
-    case 6: expert_tile<6>(a, it, item, mat, c, s, smem, &flag); break;
-    case 7: expert_tile<7>(a, it, item, mat, c, s, smem, &flag); break;
-    case 8: expert_tile<8>(a, it, item, mat, c, s, smem, &flag); break;
-    default: break;
+  if (it.cnt == 1) {
+    expert_tile<1>(a, it, mat, c, s, smem);
+  } else if constexpr (MC > 1) {
+    switch (it.cnt) {
+      case 2: expert_tile<2>(a, it, mat, c, s, smem); break;
+      case 3: expert_tile<3>(a, it, mat, c, s, smem); break;
+      case 4: expert_tile<4>(a, it, mat, c, s, smem); break;
+      case 5: expert_tile<5>(a, it, mat, c, s, smem); break;
+      case 6: expert_tile<6>(a, it, mat, c, s, smem); break;
+      case 7: expert_tile<7>(a, it, mat, c, s, smem); break;
+      case 8: expert_tile<8>(a, it, mat, c, s, smem); break;
+      default: break;
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
-// 4. slot-ordered combine
+// 3. h = SiLU(gate) * up from the split-K partials (split order)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void moe_combine_kernel(const float* __restrict__ yd,
-                                                               const int32_t* __restrict__ ids,
-                                                               const float* __restrict__ w,
-                                                               float* __restrict__ out, int T,
-                                                               int H, int E, int topk) {
-  const size_t idx = (size_t)blockIdx.x * kThreads + threadIdx.x;
+__global__ __launch_bounds__(256) void moe_act_kernel(const float* __restrict__ part,
+                                                      const int32_t* __restrict__ ids,
+                                                      float* __restrict__ h, int npairs, int I,
+                                                      int S, int E) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)npairs * I) return;
+  const int pair = (int)(idx / I);
+  const int e = ids[pair];
+  if (e < 0 || e >= E) return;
+  const size_t slab = (size_t)npairs * I;
+  const float g = sum_strided(part + idx, slab, S);
+  const float u = sum_strided(part + (size_t)S * slab + idx, slab, S);
+  h[idx] = g / (1.0f + expf(-g)) * u;
+}
+
+// ---------------------------------------------------------------------------
+// 5. combine: slot order 0..topk-1, split order inside each slot
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ part,
+                                                          const int32_t* __restrict__ ids,
+                                                          const float* __restrict__ w,
+                                                          float* __restrict__ out, int T, int H,
+                                                          int E, int topk, int S) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)T * H) return;
   const int t = (int)(idx / H);
   const int n = (int)(idx - (size_t)t * H);
+  const size_t slab = (size_t)T * topk * H;
   float acc = 0.0f;
-  for (int s = 0; s < topk; ++s) {
-    const int e = ids[t * topk + s];
+  for (int sl = 0; sl < topk; ++sl) {
+    const int e = ids[t * topk + sl];
     if (e < 0 || e >= E) continue;
-    acc = __builtin_fmaf(w[t * topk + s], yd[(size_t)(t * topk + s) * H + n], acc);
+    const size_t o = (size_t)(t * topk + sl) * H + n;
+    const float yd = sum_strided(part + o, slab, S);
+    acc = __builtin_fmaf(w[t * topk + sl], yd, acc);
   }
   out[idx] = acc;
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-void plan_gemv_tiles(int K, int NB, int kt_target, int& Jt, int& Lr, int& P, int& C, int& Kt,
-                     int& S) {
-  Jt = NB < 16 ? NB : 16;
-  Lr = Jt * kLPB;
-  P = kThreads / Lr;
-  C = (NB + Jt - 1) / Jt;
-  S = (K + kt_target / 2) / kt_target;
+void plan_tiles(int K, int NB, int kt_target, int& C, int& Kt, int& S) {
+  constexpr int P = kThreads / (kJt * kLPB);
+  C = (NB + kJt - 1) / kJt;
+  S = (K + kt_target - 1) / kt_target;
   if (S < 1) S = 1;
   Kt = (K + S - 1) / S;
   Kt = (Kt + P - 1) / P * P;
-  if (Kt > 1024) Kt = 1024;
   S = (K + Kt - 1) / Kt;
+}
+
+template <int MC>
+hipError_t launch_expert(const ExpertArgs& a, int max_items, hipStream_t st) {
+  const size_t lds = sizeof(float) * phase_lds_floats<kLPB>();
+  hipLaunchKernelGGL((moe_expert_kernel<MC>), dim3(max_items * a.nmat * a.C * a.S),
+                     dim3(kThreads), lds, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -264,28 +270,24 @@ MoePlan plan_moe(int T, int H, int I, int E, int topk) {
   p.E = E;
   p.topk = topk;
   const int npairs = T * topk;
-  const int bound = E + npairs / kMaxChunk;
+  // One pair per item for a single token (only the M = 1 tiles are compiled
+  // into that variant); up to 8 pairs of one expert per item otherwise.
+  p.MC = (T == 1) ? 1 : kMaxChunk;
+  const int bound = E + npairs / p.MC;
   p.max_items = npairs < bound ? npairs : bound;
-  plan_gemv_tiles(H, I / kBlockWeights, 320, p.gu_Jt, p.gu_Lr, p.gu_P, p.gu_C, p.gu_Kt, p.gu_S);
-  plan_gemv_tiles(I, H / kBlockWeights, 192, p.dn_Jt, p.dn_Lr, p.dn_P, p.dn_C, p.dn_Kt, p.dn_S);
-  const size_t red = (size_t)(32 / kLPB) * kRedStride;
-  p.gu_lds = 4 * (((size_t)p.gu_Kt * 8) > red ? (size_t)p.gu_Kt * 8 : red);
-  p.dn_lds = 4 * (((size_t)p.dn_Kt * 8) > red ? (size_t)p.dn_Kt * 8 : red);
+  plan_tiles(H, I / kBlockWeights, 320, p.gu_C, p.gu_Kt, p.gu_S);
+  plan_tiles(I, H / kBlockWeights, 192, p.dn_C, p.dn_Kt, p.dn_S);
   size_t off = 0;
-  p.off_route = off;
-  off += align256((size_t)npairs * 4) + align256((size_t)p.max_items * sizeof(WorkItem)) + 256;
-  p.off_gu_cnt = off;
-  off += align256((size_t)p.max_items * p.gu_C * 4);
-  p.off_dn_cnt = off;
-  off += align256((size_t)p.max_items * p.dn_C * 4);
+  p.off_items = off;
+  off += align256((size_t)p.max_items * sizeof(ItemRec));
+  p.off_n_items = off;
+  off += 256;
   p.off_gu_part = off;
-  off += align256((size_t)2 * p.gu_C * p.gu_S * npairs * p.gu_Jt * kBlockWeights * 4);
-  p.off_dn_part = off;
-  off += align256((size_t)p.dn_C * p.dn_S * npairs * p.dn_Jt * kBlockWeights * 4);
+  off += align256((size_t)2 * p.gu_S * npairs * I * sizeof(float));
   p.off_h = off;
-  off += align256((size_t)npairs * I * 4);
-  p.off_yd = off;
-  off += align256((size_t)npairs * H * 4);
+  off += align256((size_t)npairs * I * sizeof(float));
+  p.off_dn_part = off;
+  off += align256((size_t)p.dn_S * npairs * H * sizeof(float));
   p.ws_bytes = off;
   return p;
 }
@@ -294,87 +296,74 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
                       const int32_t* ids, const float* w, float* out, void* ws,
                       const MoePlan& p, hipStream_t st) {
   uint8_t* base = static_cast<uint8_t*>(ws);
-  const int npairs = p.T * p.topk;
-  int* pair_sorted = reinterpret_cast<int*>(base + p.off_route);
-  WorkItem* items = reinterpret_cast<WorkItem*>(base + p.off_route + align256((size_t)npairs * 4));
-  int* n_items = reinterpret_cast<int*>(base + p.off_route + align256((size_t)npairs * 4) +
-                                        align256((size_t)p.max_items * sizeof(WorkItem)));
-  unsigned* gu_cnt = reinterpret_cast<unsigned*>(base + p.off_gu_cnt);
-  unsigned* dn_cnt = reinterpret_cast<unsigned*>(base + p.off_dn_cnt);
+  ItemRec* items = reinterpret_cast<ItemRec*>(base + p.off_items);
+  int* n_items = reinterpret_cast<int*>(base + p.off_n_items);
   float* gu_part = reinterpret_cast<float*>(base + p.off_gu_part);
-  float* dn_part = reinterpret_cast<float*>(base + p.off_dn_part);
   float* h = reinterpret_cast<float*>(base + p.off_h);
-  float* yd = reinterpret_cast<float*>(base + p.off_yd);
+  float* dn_part = reinterpret_cast<float*>(base + p.off_dn_part);
+  const int npairs = p.T * p.topk;
 
   RouteArgs ra;
   ra.ids = ids;
   ra.npairs = npairs;
   ra.E = p.E;
-  ra.pair_sorted = pair_sorted;
+  ra.MC = p.MC;
   ra.items = items;
   ra.n_items = n_items;
-  ra.tickets = gu_cnt;  // gate/up and down tickets are adjacent
-  ra.n_tickets = (int)((p.off_gu_part - p.off_gu_cnt) / 4);
   hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   const size_t mat_bytes = (size_t)p.H * (p.I / kBlockWeights) * kBlockBytes;
   ExpertArgs g;
-  g.xin = x;
+  g.x = x;
+  g.x_bytes = (uint32_t)((size_t)p.T * p.H * sizeof(float));
   g.W0 = Wg;
   g.W1 = Wu;
-  g.pair_sorted = pair_sorted;
   g.items = items;
   g.n_items = n_items;
   g.part = gu_part;
-  g.tickets = gu_cnt;
-  g.out = h;
   g.mat_bytes = mat_bytes;
   g.K = p.H;
   g.N = p.I;
   g.NB = p.I / kBlockWeights;
-  g.Jt = p.gu_Jt;
-  g.Lr = p.gu_Lr;
-  g.P = p.gu_P;
   g.C = p.gu_C;
   g.Kt = p.gu_Kt;
   g.S = p.gu_S;
   g.nmat = 2;
-  g.topk = p.topk;
   g.npairs = npairs;
-  g.x_by_token = 1;
-  hipLaunchKernelGGL(moe_expert_kernel, dim3(p.max_items * 2 * p.gu_C * p.gu_S), dim3(kThreads),
-                     p.gu_lds, st, g);
+  g.x_row_div = p.topk;
+  err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, st)
+                    : launch_expert<kMaxChunk>(g, p.max_items, st);
+  if (err != hipSuccess) return err;
+
+  const size_t nh = (size_t)npairs * p.I;
+  hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st,
+                     gu_part, ids, h, npairs, p.I, p.gu_S, p.E);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
   ExpertArgs d = g;
-  d.xin = h;
+  d.x = h;
+  d.x_bytes = (uint32_t)(nh * sizeof(float));
   d.W0 = Wd;
   d.W1 = nullptr;
   d.part = dn_part;
-  d.tickets = dn_cnt;
-  d.out = yd;
   d.K = p.I;
   d.N = p.H;
   d.NB = p.H / kBlockWeights;
-  d.Jt = p.dn_Jt;
-  d.Lr = p.dn_Lr;
-  d.P = p.dn_P;
   d.C = p.dn_C;
   d.Kt = p.dn_Kt;
   d.S = p.dn_S;
   d.nmat = 1;
-  d.x_by_token = 0;
-  hipLaunchKernelGGL(moe_expert_kernel, dim3(p.max_items * p.dn_C * p.dn_S), dim3(kThreads),
-                     p.dn_lds, st, d);
-  err = hipGetLastError();
+  d.x_row_div = 1;
+  err = (p.MC == 1) ? launch_expert<1>(d, p.max_items, st)
+                    : launch_expert<kMaxChunk>(d, p.max_items, st);
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + kThreads - 1) / kThreads)),
-                     dim3(kThreads), 0, st, yd, ids, w, out, p.T, p.H, p.E, p.topk);
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+                     dn_part, ids, w, out, p.T, p.H, p.E, p.topk, p.dn_S);
   return hipGetLastError();
 }
 

@@ -27,6 +27,7 @@ constexpr int kBlockBytes = 18;
 constexpr int kBlockWeights = 32;
 constexpr int kWaveSize = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
+constexpr int kThreads = 256;  // lanes per workgroup of the decode tiles
 
 // Workgroups are dispatched round-robin over the XCDs (block b runs on XCD
 // b % 8). Returns a logical tile index such that consecutive logical tiles
@@ -82,8 +83,12 @@ __device__ __forceinline__ void fma_part(const float (&xv)[M], const BlockPart<L
   }
 #pragma unroll
   for (int w = 0; w < BlockPart<LPB>::kWords; ++w) {
-    const uint32_t lo = b.q[w] & 0x0f0f0f0fu;
-    const uint32_t hi = b.q[w] & 0xf0f0f0f0u;
+    uint32_t lo = b.q[w] & 0x0f0f0f0fu;
+    uint32_t hi = b.q[w] & 0xf0f0f0f0u;
+    // Hide the masks from the optimizer: otherwise it folds each
+    // (masked >> 8n) & 0xff into a 4-bit field extract plus a convert, instead
+    // of one v_cvt_f32_ubyteN per nibble.
+    asm volatile("" : "+v"(lo), "+v"(hi));
 #pragma unroll
     for (int by = 0; by < 4; ++by) {
       const float fl = static_cast<float>((lo >> (8 * by)) & 0xffu);  // v_cvt_f32_ubyteN
@@ -113,138 +118,175 @@ __device__ __forceinline__ void finish_part(float (&acc)[M][32 / LPB], const flo
   }
 }
 
-// Split-K completion ticket. Every workgroup of a tile group calls this after
-// storing its partial results; it returns true in exactly one workgroup (the
-// last to arrive), which may then read all partials of the group. The counter
-// is reset by that workgroup so the workspace is zero again after the kernel.
-__device__ __forceinline__ bool arrive_last(unsigned* __restrict__ counter, unsigned expected,
-                                            unsigned* lds_flag) {
-  __threadfence();  // release this workgroup's partial stores (agent scope)
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned prev = atomicAdd(counter, 1u);
-    const bool last = (prev == expected - 1u);
-    if (last) *counter = 0u;
-    *lds_flag = last ? 1u : 0u;
+// Sum of S values src[0], src[stride], ... in index order, with the loads
+// issued in groups of 8 so that they overlap.
+__device__ __forceinline__ float sum_strided(const float* __restrict__ src, size_t stride, int S) {
+  float v = 0.0f;
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = src[(size_t)(s + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += t[u];
   }
-  __syncthreads();
-  const bool last = (*lds_flag != 0u);
-  if (last) __threadfence();  // acquire the other workgroups' partials
-  return last;
+  for (; s < S; ++s) v += src[(size_t)s * stride];
+  return v;
 }
 
 }  // namespace q4
 
 namespace q4 {
 
-constexpr int kThreads = 256;             // lanes per workgroup of the decode kernels
-constexpr int kRedStride = kThreads + 1;  // LDS stride of the row-phase reduction
-
-// LDS stride (floats per k) of staged activations for M rows.
-template <int M>
-constexpr int x_stride() {
-  return M == 1 ? 1 : (M == 2 ? 2 : (M <= 4 ? 4 : 8));
+// Buffer resource over [base, base + bytes) (raw buffer, stride 0).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
 }
 
-// Geometry of one decode tile: Jt block columns starting at j0, rows
-// [k0, k0 + rows) of a matrix with NB blocks per row; P row phases of Lr lanes.
-struct TileGeom {
-  const uint8_t* B;  // matrix base
-  int NB, j0, k0, rows, Lr, P;
+// Load lane share `part` of a block through a buffer resource: vofs is the
+// lane's byte offset of the block, sofs a workgroup-uniform byte offset.
+template <int LPB>
+__device__ __forceinline__ void load_part_buf(__amdgpu_buffer_rsrc_t r, uint32_t vofs, uint32_t sofs,
+                                              int part, BlockPart<LPB>& out) {
+  out.d = __builtin_amdgcn_raw_buffer_load_b16(r, vofs, sofs, 0);
+  const uint32_t qo = vofs + 2 + part * (16 / LPB);
+  if constexpr (LPB == 1) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, qo, sofs, 0);
+    out.q[0] = v[0];
+    out.q[1] = v[1];
+    out.q[2] = v[2];
+    out.q[3] = v[3];
+  } else if constexpr (LPB == 2) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, qo, sofs, 0);
+    out.q[0] = v[0];
+    out.q[1] = v[1];
+  } else {
+    out.q[0] = __builtin_amdgcn_raw_buffer_load_b32(r, qo, sofs, 0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split-K tile. A workgroup of T lanes owns Jt consecutive block columns
+// (j0 .. j0+Jt-1) and the rows [k0, k0 + rows) of a K x NB-block matrix. Its
+// lanes form P = T / (Jt*LPB) row phases of Lr = Jt*LPB lanes; lane t is row
+// phase r = t / Lr, block column j0 + (t % Lr) / LPB, share (t % Lr) % LPB, and
+// walks rows k0 + r, k0 + r + P, ... . The Lr lanes of a row phase read one
+// contiguous 18*Jt-byte row segment, so a wave's loads are coalesced row
+// segments. All rows of a lane (at most RB) are loaded before any is used:
+// one memory round trip per tile. Weights and activations are read through
+// buffer resources (one 32-bit lane offset, uniform per-row scalar offsets).
+//   x, x_bytes : activations; row m of the tile's activations is x + xoff[m]
+//                floats, indexed by the matrix row k
+// ---------------------------------------------------------------------------
+struct SplitTile {
+  const uint8_t* B;
+  int NB, K;        // blocks per row, rows of the whole matrix
+  int j0, Jt;       // first block column, block columns of the tile
+  int k0, rows;     // row range of the tile
+  int Lr, P;        // lanes per row phase, row phases
 };
 
-// Accumulate this lane's share of a tile. Lane t is row phase r = t / Lr and
-// block column jj = (t % Lr) / LPB, part (t % Lr) % LPB; it walks rows
-// k0 + r, k0 + r + P, ... in increasing order. xs holds the staged activations
-// (k-major, stride x_stride<M>()). Inactive lanes leave acc/corr at zero.
-template <int M, int LPB, int U>
-__device__ __forceinline__ void tile_accumulate(const TileGeom& g, const float* xs,
+template <int M, int LPB, int RB>
+__device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float* __restrict__ x,
+                                                uint32_t x_bytes, const int (&xoff)[M],
                                                 float (&acc)[M][32 / LPB], float (&corr)[M]) {
-  constexpr int XS = x_stride<M>();
   const int t = threadIdx.x;
   const int r = t / g.Lr;
   const int v = t - r * g.Lr;
   const int jj = v / LPB;
   const int part = v - jj * LPB;
-  const int j = g.j0 + jj;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
     corr[m] = 0.0f;
 #pragma unroll
-    for (int cc = 0; cc < 32 / LPB; ++cc) acc[m][cc] = 0.0f;
+    for (int c = 0; c < 32 / LPB; ++c) acc[m][c] = 0.0f;
   }
-  if (r >= g.P || j >= g.NB || r >= g.rows) return;
-
-  const size_t row_bytes = (size_t)g.NB * kBlockBytes;
-  const uint8_t* __restrict__ base = g.B + (size_t)g.k0 * row_bytes + (size_t)j * kBlockBytes;
-  const int step = g.P * U;
-  const int rows = g.rows;
-  const int P = g.P;
-  BlockPart<LPB> b0[U], b1[U];
-
-  auto load_batch = [&](BlockPart<LPB>(&b)[U], int kk) {
+  if (r >= g.P || jj >= g.Jt || g.j0 + jj >= g.NB) return;
+  const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
+  const uint32_t mat_bytes = (uint32_t)g.K * row_bytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B, mat_bytes);
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+  // lane part of the offsets: its block column and its row phase r
+  const uint32_t vw = (uint32_t)(g.j0 + jj) * kBlockBytes + (uint32_t)r * row_bytes;
+  const uint32_t vx = (uint32_t)r * 4u;
+  for (int base = 0; base < g.rows; base += g.P * RB) {  // uniform trip count
+    // this lane's rows in the batch: k0 + base + r + i*P, i < nv
+    const int nv = min(RB, (g.rows - base - r + g.P - 1) / g.P);
+    BlockPart<LPB> b[RB];
+    float xv[RB][M];
+    if (nv == RB) {
+      // Full batch: no branches between the loads and their uses, and the
+      // loads are issued in row order (scheduling barriers), so each row's
+      // FMAs wait only for that row's loads (loads complete in issue order).
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = min(kk + u * P, rows - 1);
-      load_part<LPB>(base + (size_t)k * row_bytes, part, b[u]);
+      for (int i = 0; i < RB; ++i) {
+        const uint32_t row = (uint32_t)(g.k0 + base + i * g.P);  // uniform
+        load_part_buf<LPB>(rw, vw, row * row_bytes, part, b[i]);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          xv[i][m] = __builtin_bit_cast(
+              float, __builtin_amdgcn_raw_buffer_load_b32(rx, vx, (row + (uint32_t)xoff[m]) * 4u, 0));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        fma_part<M, LPB>(xv[i], b[i], acc, corr);
+        __builtin_amdgcn_sched_barrier(0);  // keep rows in load order
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) {
+        if (i < nv) {
+          const uint32_t row = (uint32_t)(g.k0 + base + i * g.P);
+          load_part_buf<LPB>(rw, vw, row * row_bytes, part, b[i]);
+#pragma unroll
+          for (int m = 0; m < M; ++m)
+            xv[i][m] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rx, vx, (row + (uint32_t)xoff[m]) * 4u, 0));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+        if (i < nv) fma_part<M, LPB>(xv[i], b[i], acc, corr);
     }
-  };
-  auto compute_batch = [&](BlockPart<LPB>(&b)[U], int kk) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = kk + u * P;
-      const bool ok = k < rows;
-      float xv[M];
-      const float* xr = xs + (ok ? k : 0) * XS;
-#pragma unroll
-      for (int m = 0; m < M; ++m) xv[m] = ok ? xr[m] : 0.0f;
-      if (!ok) b[u].d = 0u;  // rows past the end contribute exactly zero
-      fma_part<M, LPB>(xv, b[u], acc, corr);
-    }
-  };
-
-  int kk = r;
-  load_batch(b0, kk);
-  while (true) {
-    const bool more1 = kk + step < rows;
-    if (more1) load_batch(b1, kk + step);
-    compute_batch(b0, kk);
-    if (!more1) break;
-    kk += step;
-    const bool more0 = kk + step < rows;
-    if (more0) load_batch(b0, kk + step);
-    compute_batch(b1, kk);
-    if (!more0) break;
-    kk += step;
   }
 }
 
-// Sum the P row phases of a tile through LDS in phase order 0..P-1, one
-// activation row at a time, and hand each tile output (m, o) to store(m, o, v),
-// o in [0, ncols). smem needs (32/LPB) * kRedStride floats; the caller must
-// have finished every other use of smem. Ends with a barrier.
+// LDS floats needed by reduce_phases.
+template <int LPB>
+constexpr int phase_lds_floats() {
+  return (32 / LPB) * (256 + 1);
+}
+
+// Sum a split-K tile over its P row phases through LDS, in phase order 0..P-1,
+// one activation row at a time, and hand each tile output (m, o), o in
+// [0, ncols), to store(m, o, v). Needs 256 lanes and phase_lds_floats<LPB>()
+// floats of smem; contains workgroup barriers; ends with a barrier.
 template <int M, int LPB, class Store>
 __device__ __forceinline__ void reduce_phases(float (&acc)[M][32 / LPB], float* smem, int Lr,
                                               int P, int ncols, Store store) {
   constexpr int CPL = 32 / LPB;
+  constexpr int kStride = 256 + 1;
   const int t = threadIdx.x;
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-#pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) smem[cc * kRedStride + t] = acc[m][cc];
     __syncthreads();
-    for (int o = t; o < ncols; o += kThreads) {
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) smem[cc * kStride + t] = acc[m][cc];
+    __syncthreads();
+    for (int o = t; o < ncols; o += 256) {
       const int ob = o / kBlockWeights;
       const int c32 = o - ob * kBlockWeights;
       const int pp = c32 / CPL;
       const int cc = c32 - pp * CPL;
       const int vv = ob * LPB + pp;
       float sum = 0.0f;
-      for (int rr = 0; rr < P; ++rr) sum += smem[cc * kRedStride + rr * Lr + vv];
+      for (int rr = 0; rr < P; ++rr) sum += smem[cc * kStride + rr * Lr + vv];
       store(m, o, sum);
     }
-    __syncthreads();
   }
+  __syncthreads();
 }
 
 }  // namespace q4

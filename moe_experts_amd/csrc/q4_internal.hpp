@@ -11,16 +11,14 @@ namespace q4 {
 
 // ---- decode GEMV ---------------------------------------------------------
 struct GemvPlan {
-  int LPB;            // lanes per block (1: whole block per lane, 2: half)
-  int Jt;             // block columns per workgroup tile
-  int Lr;             // lanes per row phase (Jt * LPB)
-  int P;              // row phases per workgroup
-  int C;              // column tiles
-  int Kt;             // rows per workgroup
-  int S;              // K splits
-  size_t lds_bytes;   // dynamic LDS per workgroup
-  size_t part_offset; // byte offset of the partials in the workspace
-  size_t ws_bytes;    // workspace bytes (0 when S == 1)
+  int LPB;          // lanes per block (1: whole block per lane, 2: half)
+  int Jt;           // block columns per workgroup tile
+  int Lr;           // lanes per row phase (Jt * LPB)
+  int P;            // row phases per workgroup
+  int C;            // column tiles
+  int Kt;           // rows per workgroup
+  int S;            // K splits
+  size_t ws_bytes;  // workspace bytes: S * M * N floats of partials (0 when S == 1)
 };
 
 GemvPlan plan_gemv(int M, int N, int K);
@@ -30,14 +28,12 @@ hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N,
 // ---- routed-expert MoE decode -------------------------------------------
 struct MoePlan {
   int T, H, I, E, topk;
-  int max_items;      // upper bound on (expert, token-chunk) work items
-  // gate/up GEMV (K = H rows, N = I columns)
-  int gu_Jt, gu_Lr, gu_P, gu_C, gu_Kt, gu_S;
-  // down GEMV (K = I rows, N = H columns)
-  int dn_Jt, dn_Lr, dn_P, dn_C, dn_Kt, dn_S;
-  size_t gu_lds, dn_lds;
+  int MC;                // pairs per work item (1 for a single token, else 8)
+  int max_items;         // upper bound on (expert, pair-chunk) work items
+  int gu_C, gu_Kt, gu_S; // gate/up tiles: column tiles, rows per tile, K splits
+  int dn_C, dn_Kt, dn_S; // down tiles
   // workspace layout (byte offsets)
-  size_t off_route, off_gu_cnt, off_dn_cnt, off_gu_part, off_dn_part, off_h, off_yd;
+  size_t off_items, off_n_items, off_gu_part, off_h, off_dn_part;
   size_t ws_bytes;
 };
 

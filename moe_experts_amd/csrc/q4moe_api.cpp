@@ -9,14 +9,18 @@
 
 namespace {
 
-constexpr long long kMaxBlocks = 0x7fffffffLL;  // blocks addressed by one matrix
+// The kernels address one weight matrix and the activations with 32-bit byte
+// offsets: each must stay below 2 GiB.
+constexpr long long kMaxBytes = 0x7fffffffLL;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 int check_gemv(const float* x, const q4_0_block* B, const float* y, int M, int N, int K) {
   if (!x || !B || !y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
   if (N % 32 != 0 || M > Q4_GEMV_MAX_M) return Q4_ESHAPE;
-  if ((long long)K * (N / 32) > kMaxBlocks) return Q4_ETOOBIG;
+  if ((long long)K * (N / 32) * 18 > kMaxBytes || (long long)M * K * 4 > kMaxBytes ||
+      (long long)M * N * 4 > kMaxBytes)
+    return Q4_ETOOBIG;
   if (!aligned(x, 4) || !aligned(y, 4) || !aligned(B, 2)) return Q4_EALIGN;
   return Q4_OK;
 }
@@ -33,7 +37,7 @@ int check_moe_shape(int T, int H, int I, int E, int topk) {
   if (H % 32 != 0 || I % 32 != 0 || T > Q4_MOE_MAX_T || topk > Q4_MOE_MAX_TOPK ||
       E > Q4_MOE_MAX_E)
     return Q4_ESHAPE;
-  if ((long long)H * (I / 32) > kMaxBlocks) return Q4_ETOOBIG;  // blocks of one expert matrix
+  if ((long long)H * (I / 32) * 18 > kMaxBytes) return Q4_ETOOBIG;  // one expert matrix
   return Q4_OK;
 }
 
@@ -76,7 +80,9 @@ int q4_0_gemm(const uint16_t* X, const q4_0_block* B, float* Y, int M, int N, in
               void* stream) {
   if (!X || !B || !Y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
   if (N % 32 != 0) return Q4_ESHAPE;
-  if ((long long)K * (N / 32) > kMaxBlocks) return Q4_ETOOBIG;
+  if ((long long)K * (N / 32) * 18 > kMaxBytes || (long long)M * K * 2 > kMaxBytes ||
+      (long long)M * N * 4 > kMaxBytes)
+    return Q4_ETOOBIG;
   if (!aligned(X, 4) || !aligned(Y, 4) || !aligned(B, 2)) return Q4_EALIGN;
   return from_hip(q4::launch_gemm(X, reinterpret_cast<const uint8_t*>(B), Y, M, N, K,
                                   static_cast<hipStream_t>(stream)));

@@ -21,10 +21,10 @@ def lib():
     L.q4_strerror.restype = ctypes.c_char_p
     L.q4_strerror.argtypes = [I]
     L.q4_0_gemv.argtypes = [P, P, P, I, I, I, P, Z, P]
-    L.q4_0_gemm.argtypes = [P, P, P, I, I, I, P]
-    L.moe_q4_0_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, Z, P]
     L.q4_0_gemv_workspace_bytes.restype = Z
     L.q4_0_gemv_workspace_bytes.argtypes = [I, I, I]
+    L.q4_0_gemm.argtypes = [P, P, P, I, I, I, P]
+    L.moe_q4_0_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, Z, P]
     L.moe_q4_0_workspace_bytes.restype = Z
     L.moe_q4_0_workspace_bytes.argtypes = [I, I, I, I, I]
     return L
@@ -66,7 +66,8 @@ FAKE = 0x10000  # never dereferenced: every case below fails host validation
     ((FAKE, FAKE, FAKE, 9, 32, 4), -2),           # M > 8
     ((FAKE + 2, FAKE, FAKE, 1, 32, 4), -3),       # misaligned x
     ((FAKE, FAKE + 1, FAKE, 1, 32, 4), -3),       # misaligned blocks
-    ((FAKE, FAKE, FAKE, 1, 1 << 30, 1 << 30), -6),  # too many blocks
+    ((FAKE, FAKE, FAKE, 1, 1 << 30, 1 << 30), -6),  # matrix larger than 2 GiB
+    ((FAKE, FAKE, FAKE, 8, 32, 1 << 27), -6),       # activations larger than 2 GiB
 ])
 def test_gemv_rejects_bad_arguments(lib, args, code):
     assert lib.q4_0_gemv(*args, None, 0, None) == code
@@ -83,10 +84,7 @@ def test_gemv_requires_workspace_when_split(lib):
 def test_workspace_sizes(lib):
     assert lib.q4_0_gemv_workspace_bytes(0, 4096, 4096) == 0
     assert lib.q4_0_gemv_workspace_bytes(9, 4096, 4096) == 0
-    # the split plan depends only on (N, K): the workspace grows linearly in M
-    w1 = lib.q4_0_gemv_workspace_bytes(1, 4096, 11008)
-    w8 = lib.q4_0_gemv_workspace_bytes(8, 4096, 11008)
-    assert w1 > 0 and w8 > w1
+    assert lib.q4_0_gemv_workspace_bytes(1, 4096, 11008) > 0
     assert lib.moe_q4_0_workspace_bytes(1, 5120, 1536, 160, 6) > 0
     assert lib.moe_q4_0_workspace_bytes(65, 5120, 1536, 160, 6) == 0
     assert lib.moe_q4_0_workspace_bytes(1, 5120, 1536, 160, 9) == 0
@@ -97,6 +95,7 @@ def test_workspace_sizes(lib):
     ((None, FAKE, FAKE, 1, 32, 1), -1),
     ((FAKE, FAKE, FAKE, 1, 33, 1), -2),
     ((FAKE + 2, FAKE, FAKE, 1, 32, 1), -3),
+    ((FAKE, FAKE, FAKE, 1, 1 << 20, 1 << 17), -6),
 ])
 def test_gemm_rejects_bad_arguments(lib, args, code):
     assert lib.q4_0_gemm(*args, None) == code
