@@ -35,13 +35,20 @@ struct GemvArgs {
   int Jt, Lr, P, C, Kt, S;
 };
 
-// Rows per lane loaded before any is used, sized to the register budget.
+// Rows per lane in one pipelined batch (two batches are held in registers).
 template <int M, int LPB>
 constexpr int rows_per_batch() {
-  return M == 1 ? 16 : (M == 2 ? 12 : (M <= 4 ? 8 : 4));
+  return M <= 2 ? 8 : (M <= 4 ? (LPB == 1 ? 6 : 8) : 4);
 }
 
+// Rows per lane in one batch of the staged path.
 template <int M, int LPB>
+constexpr int staged_rows_per_batch() {
+  return LPB == 1 ? 4 : 8;
+}
+constexpr int kStagedJt = 16;
+
+template <int M, int LPB, bool STAGED>
 __global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
@@ -62,8 +69,12 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
   for (int m = 0; m < M; ++m) xoff[m] = m * a.K;
   float acc[M][32 / LPB];
   float corr[M];
-  tile_accumulate<M, LPB, rows_per_batch<M, LPB>()>(g, a.x, (uint32_t)(4 * M * a.K), xoff, acc,
-                                                     corr);
+  if constexpr (STAGED)
+    tile_accumulate_staged<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt>(
+        g, a.x, (uint32_t)(4 * M * a.K), xoff, reinterpret_cast<uint8_t*>(smem), acc, corr);
+  else
+    tile_accumulate<M, LPB, rows_per_batch<M, LPB>()>(g, a.x, (uint32_t)(4 * M * a.K), xoff,
+                                                       smem, acc, corr);
   finish_part<M, LPB>(acc, corr);
   const int n0 = g.j0 * kBlockWeights;
   const int ncols = min(a.Jt, a.NB - g.j0) * kBlockWeights;
@@ -81,9 +92,20 @@ __global__ __launch_bounds__(256) void gemv_q4_0_reduce_kernel(const float* __re
 }
 
 template <int M, int LPB>
-hipError_t launch_one(const GemvArgs& a, hipStream_t st) {
-  const size_t lds = sizeof(float) * phase_lds_floats<LPB>();
-  hipLaunchKernelGGL((gemv_q4_0_kernel<M, LPB>), dim3(a.C * a.S), dim3(kThreads), lds, st, a);
+hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
+  const int rf = 4 * phase_lds_floats<LPB>();
+  int lds;
+  if (staged) {
+    const int sb = staged_lds_bytes<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt>(a.Kt);
+    lds = sb > rf ? sb : rf;
+    hipLaunchKernelGGL((gemv_q4_0_kernel<M, LPB, true>), dim3(a.C * a.S), dim3(kThreads), lds, st,
+                       a);
+  } else {
+    const int xf = 4 * tile_x_floats<M>(a.Kt, a.P, rows_per_batch<M, LPB>());
+    lds = xf > rf ? xf : rf;
+    hipLaunchKernelGGL((gemv_q4_0_kernel<M, LPB, false>), dim3(a.C * a.S), dim3(kThreads), lds,
+                       st, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.S == 1) return err;
   const int MN = M * a.N;
@@ -93,11 +115,11 @@ hipError_t launch_one(const GemvArgs& a, hipStream_t st) {
 }
 
 template <int M>
-hipError_t launch_m(const GemvArgs& a, int lpb, hipStream_t st) {
+hipError_t launch_m(const GemvArgs& a, int lpb, bool staged, hipStream_t st) {
   if constexpr (M <= 4) {
-    if (lpb == 1) return launch_one<M, 1>(a, st);
+    if (lpb == 1) return launch_one<M, 1>(a, staged, st);
   }
-  return launch_one<M, 2>(a, st);
+  return launch_one<M, 2>(a, staged, st);
 }
 
 }  // namespace
@@ -175,15 +197,18 @@ hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N,
   a.C = p.C;
   a.Kt = p.Kt;
   a.S = p.S;
+  // Wave-private staging needs 16-byte aligned 16-block row segments.
+  const bool staged = p.Jt == kStagedJt && a.NB % 8 == 0 &&
+                      (reinterpret_cast<uintptr_t>(B) & 15) == 0;
   switch (M) {
-    case 1: return launch_m<1>(a, p.LPB, st);
-    case 2: return launch_m<2>(a, p.LPB, st);
-    case 3: return launch_m<3>(a, p.LPB, st);
-    case 4: return launch_m<4>(a, p.LPB, st);
-    case 5: return launch_m<5>(a, p.LPB, st);
-    case 6: return launch_m<6>(a, p.LPB, st);
-    case 7: return launch_m<7>(a, p.LPB, st);
-    case 8: return launch_m<8>(a, p.LPB, st);
+    case 1: return launch_m<1>(a, p.LPB, staged, st);
+    case 2: return launch_m<2>(a, p.LPB, staged, st);
+    case 3: return launch_m<3>(a, p.LPB, staged, st);
+    case 4: return launch_m<4>(a, p.LPB, staged, st);
+    case 5: return launch_m<5>(a, p.LPB, staged, st);
+    case 6: return launch_m<6>(a, p.LPB, staged, st);
+    case 7: return launch_m<7>(a, p.LPB, staged, st);
+    case 8: return launch_m<8>(a, p.LPB, staged, st);
     default: return hipErrorInvalidValue;
   }
 }

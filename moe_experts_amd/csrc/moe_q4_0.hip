@@ -39,9 +39,12 @@ struct ItemRec {
   int pairs[kMaxChunk];  // pair index t * topk + slot, in stable expert order
 };
 
+constexpr int kMaxRB = 8;     // rows per lane in one pipelined batch (M <= 4)
+constexpr int kStagedRB = 8;  // rows per lane in one batch of the staged path
+
 template <int M>
 constexpr int moe_rows_per_batch() {
-  return M == 1 ? 20 : (M == 2 ? 12 : (M <= 4 ? 8 : 4));
+  return M <= 4 ? kMaxRB : kMaxRB / 2;
 }
 
 // ---------------------------------------------------------------------------
@@ -137,7 +140,7 @@ struct ExpertArgs {
   int x_row_div;                      // activation row = pair / x_row_div, times K
 };
 
-template <int M>
+template <int M, bool STAGED>
 __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int c, int s,
                             float* smem) {
   constexpr int Lr = kJt * kLPB;
@@ -156,7 +159,11 @@ __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int
   for (int m = 0; m < M; ++m) xoff[m] = (it.pairs[m] / a.x_row_div) * a.K;
   float acc[M][32 / kLPB];
   float corr[M];
-  tile_accumulate<M, kLPB, moe_rows_per_batch<M>()>(g, a.x, a.x_bytes, xoff, acc, corr);
+  if constexpr (STAGED)
+    tile_accumulate_staged<M, kLPB, kStagedRB, kJt>(g, a.x, a.x_bytes, xoff,
+                                                    reinterpret_cast<uint8_t*>(smem), acc, corr);
+  else
+    tile_accumulate<M, kLPB, moe_rows_per_batch<M>()>(g, a.x, a.x_bytes, xoff, smem, acc, corr);
   finish_part<M, kLPB>(acc, corr);
   const int n0 = g.j0 * kBlockWeights;
   const int ncols = min(kJt, a.NB - g.j0) * kBlockWeights;
@@ -166,7 +173,7 @@ __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int
   });
 }
 
-template <int MC>
+template <int MC, bool STAGED>
 __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int per_item = a.nmat * a.C * a.S;
@@ -183,16 +190,16 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
   const int mat = rest % a.nmat;
   const int s = rest / a.nmat;
   if (it.cnt == 1) {
-    expert_tile<1>(a, it, mat, c, s, smem);
+    expert_tile<1, STAGED>(a, it, mat, c, s, smem);
   } else if constexpr (MC > 1) {
     switch (it.cnt) {
-      case 2: expert_tile<2>(a, it, mat, c, s, smem); break;
-      case 3: expert_tile<3>(a, it, mat, c, s, smem); break;
-      case 4: expert_tile<4>(a, it, mat, c, s, smem); break;
-      case 5: expert_tile<5>(a, it, mat, c, s, smem); break;
-      case 6: expert_tile<6>(a, it, mat, c, s, smem); break;
-      case 7: expert_tile<7>(a, it, mat, c, s, smem); break;
-      case 8: expert_tile<8>(a, it, mat, c, s, smem); break;
+      case 2: expert_tile<2, STAGED>(a, it, mat, c, s, smem); break;
+      case 3: expert_tile<3, STAGED>(a, it, mat, c, s, smem); break;
+      case 4: expert_tile<4, STAGED>(a, it, mat, c, s, smem); break;
+      case 5: expert_tile<5, STAGED>(a, it, mat, c, s, smem); break;
+      case 6: expert_tile<6, STAGED>(a, it, mat, c, s, smem); break;
+      case 7: expert_tile<7, STAGED>(a, it, mat, c, s, smem); break;
+      case 8: expert_tile<8, STAGED>(a, it, mat, c, s, smem); break;
       default: break;
     }
   }
@@ -253,10 +260,19 @@ void plan_tiles(int K, int NB, int kt_target, int& C, int& Kt, int& S) {
 }
 
 template <int MC>
-hipError_t launch_expert(const ExpertArgs& a, int max_items, hipStream_t st) {
-  const size_t lds = sizeof(float) * phase_lds_floats<kLPB>();
-  hipLaunchKernelGGL((moe_expert_kernel<MC>), dim3(max_items * a.nmat * a.C * a.S),
-                     dim3(kThreads), lds, st, a);
+hipError_t launch_expert(const ExpertArgs& a, int max_items, bool staged, hipStream_t st) {
+  constexpr int P = kThreads / (kJt * kLPB);
+  const int rf = 4 * phase_lds_floats<kLPB>();
+  const dim3 grid(max_items * a.nmat * a.C * a.S);
+  if (staged) {
+    const int sb = staged_lds_bytes<MC, kLPB, kStagedRB, kJt>(a.Kt);  // covers every M <= MC
+    hipLaunchKernelGGL((moe_expert_kernel<MC, true>), grid, dim3(kThreads), sb > rf ? sb : rf,
+                       st, a);
+  } else {
+    const int xf = 4 * tile_x_floats<MC>(a.Kt, P, kMaxRB);  // covers every item size M <= MC
+    hipLaunchKernelGGL((moe_expert_kernel<MC, false>), grid, dim3(kThreads), xf > rf ? xf : rf,
+                       st, a);
+  }
   return hipGetLastError();
 }
 
@@ -275,8 +291,8 @@ MoePlan plan_moe(int T, int H, int I, int E, int topk) {
   p.MC = (T == 1) ? 1 : kMaxChunk;
   const int bound = E + npairs / p.MC;
   p.max_items = npairs < bound ? npairs : bound;
-  plan_tiles(H, I / kBlockWeights, 320, p.gu_C, p.gu_Kt, p.gu_S);
-  plan_tiles(I, H / kBlockWeights, 192, p.dn_C, p.dn_Kt, p.dn_S);
+  plan_tiles(H, I / kBlockWeights, 1280, p.gu_C, p.gu_Kt, p.gu_S);
+  plan_tiles(I, H / kBlockWeights, 768, p.dn_C, p.dn_Kt, p.dn_S);
   size_t off = 0;
   p.off_items = off;
   off += align256((size_t)p.max_items * sizeof(ItemRec));
@@ -315,6 +331,11 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   if (err != hipSuccess) return err;
 
   const size_t mat_bytes = (size_t)p.H * (p.I / kBlockWeights) * kBlockBytes;
+  // Wave-private staging needs 16-byte aligned row segments: pitches of a
+  // multiple of 8 blocks and 16-byte aligned matrices.
+  auto al16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  const bool staged_gu = (p.I / kBlockWeights) % 8 == 0 && al16(Wg) && al16(Wu);
+  const bool staged_dn = (p.H / kBlockWeights) % 8 == 0 && al16(Wd);
   ExpertArgs g;
   g.x = x;
   g.x_bytes = (uint32_t)((size_t)p.T * p.H * sizeof(float));
@@ -333,8 +354,8 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   g.nmat = 2;
   g.npairs = npairs;
   g.x_row_div = p.topk;
-  err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, st)
-                    : launch_expert<kMaxChunk>(g, p.max_items, st);
+  err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, staged_gu, st)
+                    : launch_expert<kMaxChunk>(g, p.max_items, staged_gu, st);
   if (err != hipSuccess) return err;
 
   const size_t nh = (size_t)npairs * p.I;
@@ -357,8 +378,8 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   d.S = p.dn_S;
   d.nmat = 1;
   d.x_row_div = 1;
-  err = (p.MC == 1) ? launch_expert<1>(d, p.max_items, st)
-                    : launch_expert<kMaxChunk>(d, p.max_items, st);
+  err = (p.MC == 1) ? launch_expert<1>(d, p.max_items, staged_dn, st)
+                    : launch_expert<kMaxChunk>(d, p.max_items, staged_dn, st);
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;

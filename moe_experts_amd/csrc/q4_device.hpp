@@ -167,17 +167,35 @@ __device__ __forceinline__ void load_part_buf(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 // ---------------------------------------------------------------------------
-// Split-K tile. A workgroup of T lanes owns Jt consecutive block columns
+// Split-K tile. A workgroup of 256 lanes owns Jt consecutive block columns
 // (j0 .. j0+Jt-1) and the rows [k0, k0 + rows) of a K x NB-block matrix. Its
-// lanes form P = T / (Jt*LPB) row phases of Lr = Jt*LPB lanes; lane t is row
+// lanes form P = 256 / (Jt*LPB) row phases of Lr = Jt*LPB lanes; lane t is row
 // phase r = t / Lr, block column j0 + (t % Lr) / LPB, share (t % Lr) % LPB, and
-// walks rows k0 + r, k0 + r + P, ... . The Lr lanes of a row phase read one
+// walks tile rows r, r + P, r + 2P, ... . The Lr lanes of a row phase read one
 // contiguous 18*Jt-byte row segment, so a wave's loads are coalesced row
-// segments. All rows of a lane (at most RB) are loaded before any is used:
-// one memory round trip per tile. Weights and activations are read through
-// buffer resources (one 32-bit lane offset, uniform per-row scalar offsets).
-//   x, x_bytes : activations; row m of the tile's activations is x + xoff[m]
+// segments.
+//
+// Pipeline: a lane's rows go in batches of RB. Two register sets hold two
+// batches; while one batch is unpacked and accumulated, the loads of the next
+// are in flight (the loop is unrolled by two so the sets alternate without
+// register copies). Loads are never predicated, so the compiler's memory
+// waits count only the loads of the batch in use: a row past the tile end
+// (and every row of an idle lane) is given a lane offset of 2^31, beyond the
+// buffer's range (matrices are smaller than 2 GiB, and offset plus scalar
+// offset stays below 2^32), so the load returns zeros without a memory
+// access. Rows past the busiest lane's last row are skipped; a lane whose last
+// row is past the tile adds zeros (zero scale, zero activation).
+//
+// Activations: the tile's activation rows are staged in LDS as
+// xs[m * rows_pad + row] (rows_pad = rows rounded up to whole batches, the
+// padding zeroed) by LDS-DMA loads (buffer_load_dword ... lds): no registers,
+// all issued before the weight batches, one round trip. All lanes of a row
+// phase read the same LDS word (broadcast).
+//   x, x_bytes : activations; activation row m of the tile is x + xoff[m]
 //                floats, indexed by the matrix row k
+//   xs         : LDS of tile_x_floats<M>(rows, P, RB) floats
+//                (may alias the scratch of reduce_phases, which starts with a
+//                barrier)
 // ---------------------------------------------------------------------------
 struct SplitTile {
   const uint8_t* B;
@@ -187,11 +205,36 @@ struct SplitTile {
   int Lr, P;        // lanes per row phase, row phases
 };
 
+// Tile rows rounded up to whole batches of RB rows per lane.
+__host__ __device__ constexpr int tile_rows_padded(int rows, int P, int RB) {
+  return ((rows + P - 1) / P + RB - 1) / RB * RB * P;
+}
+
+// LDS floats of the staged activation tile, rounded up to whole staging
+// passes of 256 words (every DMA lane of the last pass writes inside it).
+template <int M>
+__host__ __device__ constexpr int tile_x_floats(int rows, int P, int RB) {
+  return (tile_rows_padded(rows, P, RB) * M + 255) / 256 * 256;
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (n < 64); LDS and export counters are not waited on.
+constexpr int vmcnt_imm(int n) {
+  return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
+}
+
 template <int M, int LPB, int RB>
 __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float* __restrict__ x,
                                                 uint32_t x_bytes, const int (&xoff)[M],
+                                                float* __restrict__ xs,
                                                 float (&acc)[M][32 / LPB], float (&corr)[M]) {
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  constexpr int kLoadsPerBatch = 2 * RB;  // scale + nibble load per row
+  static_assert(2 * kLoadsPerBatch < 64, "vmcnt range");
   const int t = threadIdx.x;
+  const int wave = t / kWaveSize;
   const int r = t / g.Lr;
   const int v = t - r * g.Lr;
   const int jj = v / LPB;
@@ -202,55 +245,272 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
 #pragma unroll
     for (int c = 0; c < 32 / LPB; ++c) acc[m][c] = 0.0f;
   }
-  if (r >= g.P || jj >= g.Jt || g.j0 + jj >= g.NB) return;
+  const bool active = r < g.P && jj < g.Jt && g.j0 + jj < g.NB;
+  const int nl = (g.rows + g.P - 1) / g.P;  // rows of the busiest lane (uniform)
+  const int nb = (nl + RB - 1) / RB;         // batches (uniform)
+  const int rows_pad = nb * RB * g.P;
   const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
-  const uint32_t mat_bytes = (uint32_t)g.K * row_bytes;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B, mat_bytes);
-  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
-  // lane part of the offsets: its block column and its row phase r
-  const uint32_t vw = (uint32_t)(g.j0 + jj) * kBlockBytes + (uint32_t)r * row_bytes;
-  const uint32_t vx = (uint32_t)r * 4u;
-  for (int base = 0; base < g.rows; base += g.P * RB) {  // uniform trip count
-    // this lane's rows in the batch: k0 + base + r + i*P, i < nv
-    const int nv = min(RB, (g.rows - base - r + g.P - 1) / g.P);
-    BlockPart<LPB> b[RB];
-    float xv[RB][M];
-    if (nv == RB) {
-      // Full batch: no branches between the loads and their uses, and the
-      // loads are issued in row order (scheduling barriers), so each row's
-      // FMAs wait only for that row's loads (loads complete in issue order).
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B, (uint32_t)g.K * row_bytes);
+  const uint32_t vcol = (uint32_t)(g.j0 + jj) * kBlockBytes;  // lane's block in row 0
+  const uint32_t sbase = (uint32_t)g.k0 * row_bytes;           // uniform
+  const int rows = active ? g.rows : 0;
+
+  // Stage the activation tile: element q of the [M][rows_pad] layout is
+  // loaded by lane q % 256 of pass q / 256 and lands at LDS word q (the DMA
+  // writes lane l of a wave at M0 + 4*l, M0 = xs + q0 + 64*wave words).
+  {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+    for (int q0 = 0; q0 < M * rows_pad; q0 += kThreads) {
+      const int q = q0 + t;
+      const int m = q / rows_pad;
+      const int i = q - m * rows_pad;
+      int xo = 0;
 #pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const uint32_t row = (uint32_t)(g.k0 + base + i * g.P);  // uniform
-        load_part_buf<LPB>(rw, vw, row * row_bytes, part, b[i]);
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-          xv[i][m] = __builtin_bit_cast(
-              float, __builtin_amdgcn_raw_buffer_load_b32(rx, vx, (row + (uint32_t)xoff[m]) * 4u, 0));
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        fma_part<M, LPB>(xv[i], b[i], acc, corr);
-        __builtin_amdgcn_sched_barrier(0);  // keep rows in load order
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        if (i < nv) {
-          const uint32_t row = (uint32_t)(g.k0 + base + i * g.P);
-          load_part_buf<LPB>(rw, vw, row * row_bytes, part, b[i]);
-#pragma unroll
-          for (int m = 0; m < M; ++m)
-            xv[i][m] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rx, vx, (row + (uint32_t)xoff[m]) * 4u, 0));
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < RB; ++i)
-        if (i < nv) fma_part<M, LPB>(xv[i], b[i], acc, corr);
+      for (int mm = 0; mm < M; ++mm)
+        if (mm == m) xo = xoff[mm];
+      const uint32_t off = (m < M && i < g.rows) ? (uint32_t)(xo + g.k0 + i) * 4u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
+                                               off, 0, 0, 0);
     }
   }
+  // The wait below counts on every staging load being issued before the
+  // weight loads.
+  __builtin_amdgcn_sched_barrier(0);
+
+  BlockPart<LPB> A[RB], Bs[RB];
+  auto load_batch = [&](int b, BlockPart<LPB>(&R)[RB]) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int tr = (b * RB + i) * g.P + r;  // tile row of this lane
+      const uint32_t vo = tr < rows ? vcol + (uint32_t)tr * row_bytes : kOutOfRange;
+      load_part_buf<LPB>(rw, vo, sbase, part, R[i]);
+    }
+  };
+  auto compute_batch = [&](int b, BlockPart<LPB>(&R)[RB]) {
+    float xv[RB][M];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int tr = (b * RB + i) * g.P + r;
+#pragma unroll
+      for (int m = 0; m < M; ++m) xv[i][m] = xs[m * rows_pad + tr];
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (b * RB + i < nl) fma_part<M, LPB>(xv[i], R[i], acc, corr);
+      __builtin_amdgcn_sched_barrier(0);  // one row's unpacked values live at a time
+    }
+  };
+
+  load_batch(0, A);
+  load_batch(1, Bs);
+  __builtin_amdgcn_sched_barrier(0);
+  // The staged activations have landed once at most the two weight batches'
+  // loads are outstanding; then zero the padding rows and share the tile.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerBatch));
+  {
+    const int pad = rows_pad - g.rows;
+    for (int idx = t; idx < M * pad; idx += kThreads) {
+      const int m = idx / pad;
+      xs[m * rows_pad + g.rows + (idx - m * pad)] = 0.0f;
+    }
+  }
+  __syncthreads();
+  if (!active) return;
+
+  // Pairs of batches, then an odd last batch. Loads of batches past the end
+  // are out of range (no memory access) rather than skipped by a branch, so
+  // every iteration issues the same loads in the same order.
+  int b = 0;
+  for (; b + 2 <= nb; b += 2) {
+    compute_batch(b, A);
+    load_batch(b + 2, A);
+    compute_batch(b + 1, Bs);
+    load_batch(b + 3, Bs);
+  }
+  if (b < nb) compute_batch(b, A);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K tile with wave-private weight staging (same lane roles and row
+// order as tile_accumulate). Requires 16-byte aligned row segments: the
+// matrix base and the row pitch (18*NB bytes, NB % 8 == 0) are multiples of
+// 16 and the tile is JT = 8 or 16 blocks wide (144 or 288 bytes).
+//
+// A wave's lanes cover WP = 64 / Lr row phases, so for one batch of RB rows
+// per lane the wave consumes WP*RB row segments of CPS = 18*JT/16 chunks of
+// 16 bytes. The wave copies exactly those chunks into its own LDS buffer
+// with LDS-DMA loads (buffer_load_dwordx4 ... lds): consecutive lanes fetch
+// consecutive 16-byte chunks of a segment, so every request is an aligned,
+// contiguous piece of a row and no registers hold the data in flight. Lanes
+// then read their block share (scale and nibbles) from LDS. Two buffers per
+// wave: batch b+1 streams in while batch b is computed. Producer and consumer
+// are the same wave, so a vmcnt wait (in issue order) is the only
+// synchronisation; a buffer is refilled only after the reads of its previous
+// batch have returned. Chunks of rows past the tile (and of batches past the
+// end) get an out-of-range offset: no memory access.
+// LDS layout: [activation tile][4 waves][2 buffers][stage_buf_bytes].
+// ---------------------------------------------------------------------------
+template <int LPB, int RB, int JT>
+struct StageShape {
+  static constexpr int Lr = JT * LPB;               // lanes per row phase
+  static constexpr int WP = kWaveSize / Lr;         // row phases per wave
+  static constexpr int CPS = JT * kBlockBytes / 16; // chunks per row segment
+  static constexpr int NCH = WP * RB * CPS;         // chunks per wave and batch
+  static constexpr int NI = (NCH + kWaveSize - 1) / kWaveSize;  // DMA instructions
+  // buffer: the DMA slots plus at least 4 bytes of read slack
+  // (read_block_part_lds reads one dword past a share)
+  static constexpr int kBufBytes = (NCH * 16 + 4 + 1023) / 1024 * 1024;
+  static_assert(JT == 8 || JT == 16, "segments of whole 16-byte chunks");
+  static_assert(kWaveSize % Lr == 0, "row phases must not straddle waves");
+};
+
+// LDS bytes of the staged tile: activation tile plus the weight buffers.
+template <int M, int LPB, int RB, int JT>
+__host__ __device__ constexpr int staged_lds_bytes(int rows) {
+  return tile_x_floats<M>(rows, kThreads / (JT * LPB), RB) * 4 +
+         (kThreads / kWaveSize) * 2 * StageShape<LPB, RB, JT>::kBufBytes;
+}
+
+// Read lane share `part` of the block at byte offset blk of a staged buffer.
+// The nibble bytes sit at a 2-byte but not always 4-byte aligned offset, and
+// unaligned LDS reads stall, so the covering dwords are read at 4-byte
+// aligned addresses and shifted into place (v_alignbyte_b32, shift 0 or 2).
+// Reads up to 4 bytes past the share (staging buffers have that slack).
+template <int LPB>
+__device__ __forceinline__ void read_block_part_lds(const uint8_t* __restrict__ buf, uint32_t blk,
+                                                    int part, BlockPart<LPB>& bp) {
+  constexpr int NW = BlockPart<LPB>::kWords;
+  bp.d = *reinterpret_cast<const uint16_t*>(__builtin_assume_aligned(buf + blk, 2));
+  const uint32_t o = blk + 2 + (uint32_t)part * (16 / LPB);
+  const uint32_t sh = o & 3u;
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(__builtin_assume_aligned(buf + (o - sh), 4));
+  uint32_t t[NW + 1];
+#pragma unroll
+  for (int k = 0; k <= NW; ++k) t[k] = w[k];
+#pragma unroll
+  for (int k = 0; k < NW; ++k) bp.q[k] = __builtin_amdgcn_alignbyte(t[k + 1], t[k], sh);
+}
+
+template <int M, int LPB, int RB, int JT>
+__device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
+                                                       const float* __restrict__ x,
+                                                       uint32_t x_bytes, const int (&xoff)[M],
+                                                       uint8_t* __restrict__ lds,
+                                                       float (&acc)[M][32 / LPB],
+                                                       float (&corr)[M]) {
+  using SS = StageShape<LPB, RB, JT>;
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  static_assert(2 * SS::NI < 64, "vmcnt range");
+  const int t = threadIdx.x;
+  const int lane = t % kWaveSize;
+  const int wave = t / kWaveSize;
+  const int P = kThreads / SS::Lr;
+  const int r = t / SS::Lr;
+  const int v = t - r * SS::Lr;
+  const int jj = v / LPB;
+  const int part = v - jj * LPB;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    corr[m] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32 / LPB; ++c) acc[m][c] = 0.0f;
+  }
+  const int nl = (g.rows + P - 1) / P;  // rows of the busiest lane (uniform)
+  const int nb = (nl + RB - 1) / RB;     // batches (uniform)
+  const int rows_pad = nb * RB * P;
+  float* xs = reinterpret_cast<float*>(lds);
+  uint8_t* wbuf = lds + tile_x_floats<M>(g.rows, P, RB) * 4 + wave * 2 * SS::kBufBytes;
+  const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B, (uint32_t)g.K * row_bytes);
+
+  // Chunk q = 64*i + lane of a batch: segment s = q / CPS (row phase
+  // wave*WP + s % WP, batch row s / WP), piece q % CPS. Its tile row in batch
+  // b is b*RB*P + trow[i]; the scalar offset carries the batch.
+  int trow[SS::NI];
+  uint32_t voff[SS::NI];
+#pragma unroll
+  for (int i = 0; i < SS::NI; ++i) {
+    const int q = i * kWaveSize + lane;
+    const int sg = q / SS::CPS;
+    const int pc = q - sg * SS::CPS;
+    trow[i] = q < SS::NCH ? (sg / SS::WP) * P + wave * SS::WP + sg % SS::WP : 0x40000000;
+    voff[i] = (uint32_t)g.j0 * kBlockBytes + (uint32_t)trow[i] * row_bytes + (uint32_t)pc * 16u;
+  }
+  auto stage_batch = [&](int b) {
+    uint8_t* buf = wbuf + (b & 1) * SS::kBufBytes;
+    const int brow = b * RB * P;
+    const uint32_t soff = (uint32_t)(g.k0 + brow) * row_bytes;
+#pragma unroll
+    for (int i = 0; i < SS::NI; ++i) {
+      const uint32_t vo = brow + trow[i] < g.rows ? voff[i] : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rw, (lds_void_t*)(buf + i * kWaveSize * 16), 16, vo, brow < g.rows ? soff : 0u, 0, 0);
+    }
+  };
+
+  // activation tile, as in tile_accumulate
+  {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+    for (int q0 = 0; q0 < M * rows_pad; q0 += kThreads) {
+      const int q = q0 + t;
+      const int m = q / rows_pad;
+      const int i = q - m * rows_pad;
+      int xo = 0;
+#pragma unroll
+      for (int mm = 0; mm < M; ++mm)
+        if (mm == m) xo = xoff[mm];
+      const uint32_t off = (m < M && i < g.rows) ? (uint32_t)(xo + g.k0 + i) * 4u : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
+                                               off, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  stage_batch(0);
+  stage_batch(1);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * SS::NI));  // activations landed
+  {
+    const int pad = rows_pad - g.rows;
+    for (int idx = t; idx < M * pad; idx += kThreads) {
+      const int m = idx / pad;
+      xs[m * rows_pad + g.rows + (idx - m * pad)] = 0.0f;
+    }
+  }
+  // Share the activation tile. A plain __syncthreads() would also wait for
+  // the weight copies in flight (its release fence waits on every memory
+  // operation); the tile's own copies have landed (vmcnt above), so only the
+  // LDS stores need a wait before the barrier.
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // lane's block share inside a staged segment, and its segment in a batch
+  const int seg0 = (lane / SS::Lr);  // row phase within the wave
+  const int in_seg = jj * kBlockBytes;
+  for (int b = 0; b < nb; ++b) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(SS::NI));  // batch b landed (b+1 in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* buf = wbuf + (b & 1) * SS::kBufBytes;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if (b * RB + i < nl) {  // uniform
+        BlockPart<LPB> bp;
+        read_block_part_lds<LPB>(buf, (i * SS::WP + seg0) * (SS::CPS * 16) + in_seg, part, bp);
+        const int tr = (b * RB + i) * P + r;
+        float xv[M];
+#pragma unroll
+        for (int m = 0; m < M; ++m) xv[m] = xs[m * rows_pad + tr];
+        fma_part<M, LPB>(xv, bp, acc, corr);
+      }
+    }
+    // every read of this buffer has returned before it is refilled
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+    stage_batch(b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the tile
 }
 
 // LDS floats needed by reduce_phases.

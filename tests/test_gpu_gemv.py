@@ -19,6 +19,11 @@ def gemv(x: np.ndarray, B: np.ndarray, N: int) -> np.ndarray:
 
 SMALL = [(1, 1, 32), (1, 2, 64), (2, 31, 96), (3, 33, 256), (8, 64, 288), (1, 4097, 4128),
          (5, 300, 160), (4, 1000, 512), (8, 4097, 96), (7, 129, 1024), (6, 2, 4128)]
+# Shapes whose rows are whole 16-byte chunks (N % 256 == 0, N >= 512) take the
+# LDS-staged weight path: a single row, a partial last column tile
+# (N % 512 == 256), odd row counts, every batch size.
+STAGED = [(1, 1, 512), (2, 17, 768), (3, 5, 1280), (8, 3000, 768), (5, 4097, 2304),
+          (1, 257, 512), (4, 63, 1792), (6, 1111, 1280)]
 
 
 @pytest.mark.parametrize("M,K,N", SMALL)
@@ -27,6 +32,29 @@ def test_gemv_small_shapes_match_oracle(M, K, N):
     B = datagen.q4_0_random(N + K, K, N)
     ref, bnd = oracle.q4_0_matmul(x, B, N, K)
     check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
+
+
+@pytest.mark.parametrize("M,K,N", STAGED)
+def test_gemv_staged_shapes_match_oracle(M, K, N):
+    x = datagen.activations(M * 1000 + K + 7, M, K)
+    B = datagen.q4_0_random(N + K + 7, K, N)
+    ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+    check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
+
+
+def test_gemv_misaligned_matrix_takes_generic_path():
+    """A matrix that is only 2-byte aligned cannot be staged in 16-byte
+    chunks; the per-lane path must give the same bits as the staged one."""
+    from moe_experts_amd import q4_0_gemv
+    M, K, N = 3, 700, 1024
+    x = datagen.activations(11, M, K)
+    B = datagen.q4_0_random(12, K, N)
+    ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+    raw = torch.zeros(B.size + 16, dtype=torch.uint8, device=dev())
+    Bmis = raw[2:2 + B.size]
+    Bmis.copy_(torch.from_numpy(B.reshape(-1)))
+    y = to_host(q4_0_gemv(to_dev(x), Bmis, N))
+    check_tol(y, ref, bnd, TOL, "misaligned B")
 
 
 def test_gemv_handworked():
