@@ -56,8 +56,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the MoE and prefill measurements")
-    ap.add_argument("--only", choices=["dense", "moe", "prefill"], default=None,
+    ap.add_argument("--only", choices=["dense", "moe", "prefill", "traffic-probe"], default=None,
                     help="run a single workload (for profiling); prints its own JSON line")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write the HBM traffic summary from two counter passes of the probe")
     return ap.parse_args()
 
 
@@ -174,40 +176,183 @@ def bench_dense(torch, dev, steps, warmup):
         b = sum(q4_bytes(K, N) + 4 * M * K + 4 * M * N for _, K, N, _ in shapes)
         per_M[M] = (t * 1e3, b)
     return dict(step_s=dt, wall_s=wall, step_bytes=step_bytes, per_call=per_call, per_M=per_M,
+                call_s=call_s,
                 R=R, host=host, shapes=shapes, Ms=Ms)
 
 
+# The dominant unit of the headline step: q4_0_gemv at batch 8 on the
+# 4096 x 11008 gate matrix. Batch 8 takes the largest share of the step, and
+# its gate, up and down calls are the longest launches. One call is two
+# dispatches: gemv_q4_0_kernel<8,2,staged> and its split-K reduce kernel.
+DOMINANT = {"M": 8, "shape": "ffn_gate"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_M8_4096x11008_traffic.md")
+KERNEL_SOURCES = ["moe_experts_amd/csrc/q4_device.hpp", "moe_experts_amd/csrc/gemv_q4_0.hip",
+                  "moe_experts_amd/csrc/q4moe_api.cpp"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per call of the dominant unit from the committed counter
+    summary, or None when it is missing or was taken on other kernel code."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    start = text.find("```json")
+    if start < 0:
+        return None
+    blob = json.loads(text[start + 7:text.index("```", start + 7)])
+    if blob.get("source_hash") != kernel_source_hash():
+        return None
+    return blob.get("hbm_bytes_per_call")
+
+
 def dense_roofline(d):
-    """Roofline of the dominant kernel: the batch size whose gemv launches take
-    the most time per step (each batch size is its own kernel instantiation)."""
-    Ms = d["Ms"]
-    tot = {M: d["per_M"][M][0] for M in Ms}
-    Mdom = max(Ms, key=lambda M: tot[M])
-    ms, b = d["per_M"][Mdom]
-    n = len(d["shapes"])
-    flops = sum(2 * Mdom * K * N for _, K, N, _ in d["shapes"])
-    gbs = b / (ms * 1e-3) / 1e9
-    tflops = flops / (ms * 1e-3) / 1e12
-    # VALU lane-ops per weight of the fused kernel (half a block per lane):
-    # 16 nibble converts + 4 masks + 1 scale convert per 16 weights, plus M FMAs
-    # and 2M scale products/corrections per 16 weights -> the ALU-bound time.
-    ops_per_weight = (21 + 18 * Mdom) / 16.0
-    alu_time_at_peak = sum(K * N for _, K, N, _ in d["shapes"]) * ops_per_weight / 39.3e12
-    hbm_time_at_peak = b / (HBM_PEAK_GBS * 1e9)
-    if alu_time_at_peak > hbm_time_at_peak:
+    """Roofline of the dominant unit (see DOMINANT)."""
+    M = DOMINANT["M"]
+    shapes = d["shapes"]
+    i = [k for k, sh in enumerate(shapes) if sh[0] == DOMINANT["shape"]][0]
+    _, K, N, _ = shapes[i]
+    t = d["call_s"][(M, i)]
+    flops = 2 * M * K * N
+    algo_bytes = q4_bytes(K, N) + 4 * M * K + 4 * M * N
+    # fp32 VALU lane operations per weight of the unpack-and-FMA loop at this
+    # batch (half a block per lane): 16 nibble converts, 4 masks, 1 scale
+    # convert, 8 scale products and corrections ... per 16 weights, plus M FMAs
+    ops_per_weight = (21 + 18 * M) / 16.0
+    alu_s = K * N * ops_per_weight / (VALU_F32_PEAK_TFLOPS * 1e12 / 2)
+    hbm_s = algo_bytes / (HBM_PEAK_GBS * 1e9)
+    tflops = flops / t / 1e12
+    gbs = algo_bytes / t / 1e9
+    common = {"traffic": measured_traffic(),
+              "kernel": f"q4_0_gemv M={M} on 4096x11008 (gemv_q4_0_kernel<{M},2,staged> + "
+                        "gemv_q4_0_reduce_kernel)",
+              "avg_launch_us": round(t * 1e6, 2),
+              "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
+              "alu_bound_us": round(alu_s * 1e6, 2), "hbm_bound_us": round(hbm_s * 1e6, 2)}
+    if alu_s > hbm_s:
         roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / VALU_F32_PEAK_TFLOPS, 4), "traffic": None,
-                "kernel": f"gemv_q4_0_kernel<M={Mdom}>",
-                "note": "useful FMA flops 2MKN only; unpack and scale work not counted",
-                "alu_ops_frac": round(alu_time_at_peak / (ms * 1e-3), 4),
-                "hbm_GBps": round(gbs, 1)}
+                "unit": "TFLOP/s", "frac": round(tflops / VALU_F32_PEAK_TFLOPS, 4),
+                "note": "achieved counts the 2MKN useful flops; the VALU also unpacks nibbles "
+                        "(alu_ops_frac: all lane operations vs the VALU peak)",
+                "alu_ops_frac": round(alu_s / t, 4), "hbm_GBps": round(gbs, 1)}
     else:
         roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": f"gemv_q4_0_kernel<M={Mdom}>"}
-    roof["launches_per_step"] = n
-    roof["avg_launch_us"] = round(ms * 1e3 / n, 2)
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof.update(common)
     return roof
+
+
+def traffic_probe(torch, dev):
+    """Workload for the FETCH_SIZE / WRITE_SIZE counter passes: 24 calls of the
+    dominant unit on rotating weight copies, then 4 device copies of a known
+    512 MiB buffer (calibration: bytes the counter reports for a plain copy)."""
+    from moe_experts_amd import datagen, q4_0_gemv
+    M = DOMINANT["M"]
+    name, K, N, seed = [sh for sh in datagen.DENSE_7B_SHAPES if sh[0] == DOMINANT["shape"]][0]
+    B0 = torch.from_numpy(datagen.q4_0_random(seed, K, N)).to(dev)
+    copies = [B0] + [B0.clone() for _ in range(max(2, math.ceil(GIB / B0.numel())) - 1)]
+    x = torch.from_numpy(datagen.activations(datagen.dense_x_seed(M), M, K)).to(dev)
+    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    for r in range(24):
+        q4_0_gemv(x, copies[r % len(copies)], N, y=y)
+    torch.cuda.synchronize()
+    del copies
+    src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "traffic", "calls": 24, "copy_bytes": src.numel()}), flush=True)
+
+
+def traffic_summary(fetch_csv, write_csv, command):
+    """Turn the two counter passes of traffic_probe into TRAFFIC_FILE."""
+    import csv
+
+    def per_kernel(path, counter):
+        out = {}
+        for row in csv.DictReader(open(path)):
+            if row["Counter_Name"] != counter:
+                continue
+            out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]) * 1024.0)
+        return out
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = 512 << 20
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        if not ks:
+            raise SystemExit(f"no dispatch of {key} in the counter file")
+        return d[ks[0]]
+
+    def med(v):
+        v = sorted(v)
+        return v[len(v) // 2]
+
+    # the probe's last four copies are the 512 MiB calibration copies (earlier
+    # copy dispatches clone the weight matrix)
+    cf = med(pick(fetch, "copyBuffer")[-4:])
+    cw = med(pick(write, "copyBuffer")[-4:])
+    f_fetch = copy_bytes / cf
+    f_write = copy_bytes / cw
+    main_f = med(pick(fetch, "gemv_q4_0_kernel")[4:])
+    main_w = med(pick(write, "gemv_q4_0_kernel")[4:])
+    red_f = med(pick(fetch, "gemv_q4_0_reduce_kernel")[4:])
+    red_w = med(pick(write, "gemv_q4_0_reduce_kernel")[4:])
+    M = DOMINANT["M"]
+    K, N = 4096, 11008
+    algo = q4_bytes(K, N) + 4 * M * K + 4 * M * N
+    total = (main_f + red_f) * f_fetch + (main_w + red_w) * f_write
+    blob = {"source_hash": kernel_source_hash(), "hbm_bytes_per_call": round(total),
+            "algorithmic_bytes_per_call": algo,
+            "main_kernel": {"fetch_bytes": round(main_f * f_fetch), "write_bytes": round(main_w * f_write)},
+            "reduce_kernel": {"fetch_bytes": round(red_f * f_fetch), "write_bytes": round(red_w * f_write)},
+            "calibration": {"copy_bytes": copy_bytes, "fetch_counter_bytes": round(cf),
+                            "write_counter_bytes": round(cw), "fetch_factor": round(f_fetch, 4),
+                            "write_factor": round(f_write, 4)}}
+    text = f"""# HBM traffic of q4_0_gemv, batch 8, 4096 x 11008 (gate shape of the dense decode step)
+
+Counters: `FETCH_SIZE` and `WRITE_SIZE` (KiB per dispatch, rocprofv3 `--pmc`), one pass each,
+over the workload of `python bench.py --only traffic-probe` (24 calls on rotating weight copies,
+then 4 device copies of 512 MiB). Median over the calls after the first four.
+
+Calibration: a plain 512 MiB device copy reads {cf / 2**20:.1f} MiB by `FETCH_SIZE` and writes
+{cw / 2**20:.1f} MiB by `WRITE_SIZE`; the factors {f_fetch:.4f} (fetch) and {f_write:.4f} (write)
+scale the kernel's counter values to bytes.
+
+| dispatch | fetched (B) | written (B) |
+|---|---|---|
+| gemv_q4_0_kernel<8,2,staged> | {round(main_f * f_fetch)} | {round(main_w * f_write)} |
+| gemv_q4_0_reduce_kernel | {round(red_f * f_fetch)} | {round(red_w * f_write)} |
+| **call** | {round((main_f + red_f) * f_fetch)} | {round((main_w + red_w) * f_write)} |
+
+Algorithmic bytes per call: {algo} (weights once, activations, outputs). Measured / algorithmic:
+{total / algo:.3f}.
+
+Commands:
+```
+{command}
+```
+
+```json
+{json.dumps(blob, indent=1)}
+```
+"""
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write(text)
+    print(text)
 
 
 def cpu_baseline_dense(d, seconds):
@@ -309,6 +454,9 @@ def bench_prefill(torch, dev, steps, warmup):
 
 def main():
     args = parse()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path)", file=sys.stderr)
@@ -317,6 +465,9 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
 
+    if args.only == "traffic-probe":
+        traffic_probe(torch, dev)
+        return
     if args.only == "moe":
         print(json.dumps({"moe": bench_moe(torch, dev, args.steps, args.warmup)}), flush=True)
         return
