@@ -20,6 +20,8 @@
 // Cross-workgroup hand-off at agent scope costs an L2 write-back per workgroup
 // on this GPU, so the split-K sum is a second kernel instead: no atomics, no
 // fences, deterministic results.
+#include <cstdlib>
+
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
 
@@ -75,11 +77,10 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
   else
     tile_accumulate<M, LPB, rows_per_batch<M, LPB>()>(g, a.x, (uint32_t)(4 * M * a.K), xoff,
                                                        smem, acc, corr);
-  finish_part<M, LPB>(acc, corr);
   const int n0 = g.j0 * kBlockWeights;
   const int ncols = min(a.Jt, a.NB - g.j0) * kBlockWeights;
   float* dst = (a.S == 1) ? a.y : a.part + (size_t)s * M * a.N;
-  reduce_phases<M, LPB>(acc, smem, a.Lr, a.P, ncols,
+  reduce_phases<M, LPB>(acc, corr, smem, a.Lr, a.P, ncols,
                         [&](int m, int o, float v) { dst[(size_t)m * a.N + n0 + o] = v; });
 }
 
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void gemv_q4_0_reduce_kernel(const float* __re
 
 template <int M, int LPB>
 hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
-  const int rf = 4 * phase_lds_floats<LPB>();
+  const int rf = 4 * phase_lds_floats<M, LPB>();
   int lds;
   if (staged) {
     const int sb = staged_lds_bytes<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt>(a.Kt);
@@ -125,54 +126,33 @@ hipError_t launch_m(const GemvArgs& a, int lpb, bool staged, hipStream_t st) {
 }  // namespace
 
 // Tile plan: 16-block column tiles; whole blocks per lane for M <= 4, half
-// blocks for M > 4 (register budget). The K split S minimizes a simple time
-// model: the larger of the HBM time (weights plus the partial sums written and
-// read back) and the VALU time (fp32 lane operations per weight, over the CUs
-// the grid covers), divided by how evenly the workgroups spread over the 256
-// CUs (a CU holding one more workgroup than the others sets the kernel time),
-// plus a latency term per load batch and the cost of the reduce kernel.
+// blocks for M > 4 (register budget). The K split S sets the grid size C*S.
+// Measured on MI355X over the dense 7B shapes, the best grid is at most one
+// full round of resident workgroups: up to 512 (two per CU) for M >= 4, where
+// the VALU sets the pace and every SIMD needs two waves, and up to 352 for
+// M <= 3, where more splits only add partial-sum traffic; a grid just past a
+// round costs a whole second round. Tiles keep at least 128 rows (8 or 16 per
+// lane), or their fixed cost dominates. S is the largest split within both.
 GemvPlan plan_gemv(int M, int N, int K) {
   GemvPlan p{};
-  constexpr int kCUs = 256;
-  constexpr double kHbm = 5.5e12;       // attainable bytes/s of a streaming read
-  constexpr double kValu = 39.3e12;     // fp32 lane operations per second (no packed math)
+  constexpr int kMinTileRows = 128;
   const int NB = N / kBlockWeights;
   p.LPB = (M <= 4) ? 1 : 2;
   p.Jt = NB < 16 ? NB : 16;
   p.Lr = p.Jt * p.LPB;
   p.P = kThreads / p.Lr;
   p.C = (NB + p.Jt - 1) / p.Jt;
-  const int rb = M == 1 ? 16 : (M == 2 ? 12 : (M <= 4 ? 8 : 4));
-  // lane operations per weight: per block (LPB = 1) one scale convert, 2M
-  // scale products and corrections, 8 masks, 32 nibble converts, 32M FMAs
-  const double opw = p.LPB == 1 ? (41.0 + 34.0 * M) / 32.0 : (21.0 + 18.0 * M) / 16.0;
-  const double wbytes = (double)K * NB * kBlockBytes;
-  double best = 1e30;
-  int best_kt = ((K + p.P - 1) / p.P) * p.P;
+  const int target = M >= 4 ? 512 : 352;
+  int best_kt = ((K + p.P - 1) / p.P) * p.P;  // S = 1
   int last_S = -1;
-  for (int s = 1; s <= 4096; ++s) {
+  for (int s = 2; s <= K; ++s) {
     int kt = (K + s - 1) / s;
     kt = (kt + p.P - 1) / p.P * p.P;
     const int S = (K + kt - 1) / kt;
     if (S == last_S) continue;
     last_S = S;
-    const int rows_per_lane = kt / p.P;
-    if (rows_per_lane > 4 * rb) continue;
-    const int wgs = p.C * S;
-    const int per_cu = (wgs + kCUs - 1) / kCUs;
-    const double balance = (double)wgs / ((double)per_cu * kCUs);
-    const double fill = wgs >= kCUs ? 1.0 : (double)wgs / kCUs;
-    const double pbytes = S > 1 ? (double)S * M * N * 4.0 : 0.0;
-    const double t_mem = (wbytes + 2.0 * pbytes) / kHbm;
-    const double t_valu = (double)K * N * opw / (kValu * fill);
-    const int batches = (rows_per_lane + rb - 1) / rb;
-    double t = (t_mem > t_valu ? t_mem : t_valu) / balance + 1.5e-6 + 0.5e-6 * (batches - 1);
-    if (S > 1) t += 2.0e-6 + pbytes / 5.0e12;
-    if (t < best) {
-      best = t;
-      best_kt = kt;
-    }
-    if (S >= K) break;
+    if (kt < kMinTileRows || p.C * S > target) break;
+    best_kt = kt;
   }
   p.Kt = best_kt;
   p.S = (K + p.Kt - 1) / p.Kt;

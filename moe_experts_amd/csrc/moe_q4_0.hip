@@ -13,16 +13,17 @@
 //                 expert (MC = 8, or 1 for a single token).
 //   2. gate/up  : split-K GEMV tiles of the dense decode kernel over the
 //                 routed experts' gate and up matrices; a tile streams its
-//                 expert's 8-block row segments once for all pairs of its item
-//                 and writes per-pair partial sums.
+//                 expert's 16-block row segments once for all pairs of its
+//                 item and writes per-pair partial sums.
 //   3. act      : h = SiLU(sum of gate partials) * (sum of up partials).
 //   4. down     : split-K tiles of h . Wd_e, per-pair partial sums.
 //   5. combine  : out[t] = sum over slots in order 0..topk-1 of
 //                 w[t][s] * (sum of the slot's down partials).
 // No atomics and no cross-workgroup hand-off inside a kernel: deterministic.
-// The tile shapes depend only on (H, I), never on T or on the item sizes, so
-// a token's result is bitwise the same whatever other tokens share the call
-// (batch invariance).
+// For T >= 2 the tile shapes depend only on (H, I), never on T or on the item
+// sizes, so a token's result is bitwise the same whatever other tokens share
+// the call (batch invariance); a single token uses finer K splits, so it
+// matches its batched result to rounding, not bitwise.
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
 
@@ -32,7 +33,7 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxChunk = 8;  // pairs per work item (MC <= kMaxChunk)
 constexpr int kLPB = 2;       // half-block lane shares, for every item size
-constexpr int kJt = 8;        // block columns per tile: 144-byte row segments
+constexpr int kJt = 16;       // block columns per tile: 288-byte row segments
 
 struct ItemRec {
   int e, cnt, pad0, pad1;
@@ -164,11 +165,10 @@ __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int
                                                     reinterpret_cast<uint8_t*>(smem), acc, corr);
   else
     tile_accumulate<M, kLPB, moe_rows_per_batch<M>()>(g, a.x, a.x_bytes, xoff, smem, acc, corr);
-  finish_part<M, kLPB>(acc, corr);
   const int n0 = g.j0 * kBlockWeights;
   const int ncols = min(kJt, a.NB - g.j0) * kBlockWeights;
   float* dst = a.part + ((size_t)mat * a.S + s) * a.npairs * a.N;
-  reduce_phases<M, kLPB>(acc, smem, Lr, g.P, ncols, [&](int m, int o, float v) {
+  reduce_phases<M, kLPB>(acc, corr, smem, Lr, g.P, ncols, [&](int m, int o, float v) {
     dst[(size_t)it.pairs[m] * a.N + n0 + o] = v;
   });
 }
@@ -262,7 +262,7 @@ void plan_tiles(int K, int NB, int kt_target, int& C, int& Kt, int& S) {
 template <int MC>
 hipError_t launch_expert(const ExpertArgs& a, int max_items, bool staged, hipStream_t st) {
   constexpr int P = kThreads / (kJt * kLPB);
-  const int rf = 4 * phase_lds_floats<kLPB>();
+  const int rf = 4 * phase_lds_floats<MC, kLPB>();
   const dim3 grid(max_items * a.nmat * a.C * a.S);
   if (staged) {
     const int sb = staged_lds_bytes<MC, kLPB, kStagedRB, kJt>(a.Kt);  // covers every M <= MC
@@ -291,8 +291,12 @@ MoePlan plan_moe(int T, int H, int I, int E, int topk) {
   p.MC = (T == 1) ? 1 : kMaxChunk;
   const int bound = E + npairs / p.MC;
   p.max_items = npairs < bound ? npairs : bound;
-  plan_tiles(H, I / kBlockWeights, 1280, p.gu_C, p.gu_Kt, p.gu_S);
-  plan_tiles(I, H / kBlockWeights, 768, p.dn_C, p.dn_Kt, p.dn_S);
+  // K tiles: a single token has only 6 experts' worth of tiles, so it splits
+  // K finer (more workgroups); batches use long tiles (less partial-sum
+  // traffic, fewer tile epilogues). The choice depends only on whether T is 1.
+  const bool single = (T == 1);
+  plan_tiles(H, I / kBlockWeights, single ? 640 : 1280, p.gu_C, p.gu_Kt, p.gu_S);
+  plan_tiles(I, H / kBlockWeights, single ? 384 : 768, p.dn_C, p.dn_Kt, p.dn_S);
   size_t off = 0;
   p.off_items = off;
   off += align256((size_t)p.max_items * sizeof(ItemRec));

@@ -103,21 +103,6 @@ __device__ __forceinline__ void fma_part(const float (&xv)[M], const BlockPart<L
   }
 }
 
-// Finish a lane's accumulators: even columns acc - 8*corr, odd columns
-// acc/16 - 8*corr (both exact rescalings, one rounding in the subtraction).
-template <int M, int LPB>
-__device__ __forceinline__ void finish_part(float (&acc)[M][32 / LPB], const float (&corr)[M]) {
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const float c8 = 8.0f * corr[m];
-#pragma unroll
-    for (int c = 0; c < 32 / LPB; c += 2) {
-      acc[m][c] = acc[m][c] - c8;
-      acc[m][c + 1] = acc[m][c + 1] * 0.0625f - c8;
-    }
-  }
-}
-
 // Sum of S values src[0], src[stride], ... in index order, with the loads
 // issued in groups of 8 so that they overlap.
 __device__ __forceinline__ float sum_strided(const float* __restrict__ src, size_t stride, int S) {
@@ -513,40 +498,72 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the tile
 }
 
-// LDS floats needed by reduce_phases.
-template <int LPB>
+// LDS floats needed by reduce_phases: one activation row's accumulators,
+// the raw corrections of all rows and their phase sums.
+template <int M, int LPB>
 constexpr int phase_lds_floats() {
-  return (32 / LPB) * (256 + 1);
+  return (32 / LPB) * (256 + 1) + M * (256 + 1) + M * 256;
 }
 
 // Sum a split-K tile over its P row phases through LDS, in phase order 0..P-1,
-// one activation row at a time, and hand each tile output (m, o), o in
-// [0, ncols), to store(m, o, v). Needs 256 lanes and phase_lds_floats<LPB>()
-// floats of smem; contains workgroup barriers; ends with a barrier.
+// then finish each output once: even columns sum - 8*csum, odd columns
+// sum/16 - 8*csum (csum = the phase sum of the corrections; both rescalings
+// are exact). The phase sum is linear, so finishing after it equals finishing
+// every lane first, at 1/P of the work; the sums of acc and of 8*corr still
+// run in the same order, so all-8 nibbles still give exactly zero.
+// Hands each tile output (m, o), o in [0, ncols) with ncols <= 512, to
+// store(m, o, v). Needs 256 lanes and phase_lds_floats<M, LPB>() floats of
+// smem; contains workgroup barriers; ends with a barrier.
 template <int M, int LPB, class Store>
-__device__ __forceinline__ void reduce_phases(float (&acc)[M][32 / LPB], float* smem, int Lr,
-                                              int P, int ncols, Store store) {
+__device__ __forceinline__ void reduce_phases(const float (&acc)[M][32 / LPB],
+                                              const float (&corr)[M], float* smem, int Lr, int P,
+                                              int ncols, Store store) {
   constexpr int CPL = 32 / LPB;
   constexpr int kStride = 256 + 1;
+  float* A = smem;                  // [CPL][kStride] accumulators of one row m
+  float* C = A + CPL * kStride;     // [M][kStride] corrections
+  float* CS = C + M * kStride;      // [M][256] phase sums of the corrections
   const int t = threadIdx.x;
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < M; ++m) C[m * kStride + t] = corr[m];
+  __syncthreads();
+  for (int q = t; q < M * Lr; q += 256) {
+    const int m = q / Lr;
+    const int v = q - m * Lr;
+    float sum = 0.0f;
+    for (int rr = 0; rr < P; ++rr) sum += C[m * kStride + rr * Lr + v];
+    CS[m * 256 + v] = sum;
+  }
+  // this thread's outputs o = t and t + 256
+  int cc_[2], vv_[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int o = t + 256 * k;
+    const int ob = o / kBlockWeights;
+    const int c32 = o - ob * kBlockWeights;
+    const int pp = c32 / CPL;
+    cc_[k] = c32 - pp * CPL;
+    vv_[k] = ob * LPB + pp;
+  }
 #pragma unroll
   for (int m = 0; m < M; ++m) {
+#pragma unroll
+    for (int cc = 0; cc < CPL; ++cc) A[cc * kStride + t] = acc[m][cc];
     __syncthreads();
 #pragma unroll
-    for (int cc = 0; cc < CPL; ++cc) smem[cc * kStride + t] = acc[m][cc];
-    __syncthreads();
-    for (int o = t; o < ncols; o += 256) {
-      const int ob = o / kBlockWeights;
-      const int c32 = o - ob * kBlockWeights;
-      const int pp = c32 / CPL;
-      const int cc = c32 - pp * CPL;
-      const int vv = ob * LPB + pp;
-      float sum = 0.0f;
-      for (int rr = 0; rr < P; ++rr) sum += smem[cc * kStride + rr * Lr + vv];
-      store(m, o, sum);
+    for (int k = 0; k < 2; ++k) {
+      const int o = t + 256 * k;
+      if (o < ncols) {
+        const float* src = A + cc_[k] * kStride + vv_[k];
+        float sum = 0.0f;
+        for (int rr = 0; rr < P; ++rr) sum += src[rr * Lr];
+        const float c8 = 8.0f * CS[m * 256 + vv_[k]];
+        store(m, o, ((cc_[k] & 1) ? sum * 0.0625f : sum) - c8);
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 }
 
 }  // namespace q4

