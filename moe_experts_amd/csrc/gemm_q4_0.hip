@@ -5,17 +5,29 @@
 // article (§5.2: all prompt tokens in one large matmul) and the quantized
 // tensor-core GEMM the KTransformers DeepSeek-V2 tutorial uses for prefill
 // ("Optimization 2", Marlin). This is a dense contraction, so it runs on MFMA
-// (v_mfma_f32_32x32x16_f16):
+// (v_mfma_f32_32x32x16_f16). The weights keep the pages' layout (blocks of
+// 32 along N within a row), so a column's K values sit in different rows and
+// the B operand is dequantized into LDS transposed ([n][k]).
 //
-//   * workgroup tile BM x BN = 128 x 128, 4 waves in a 2 x 2 grid, each wave
-//     a 64 x 64 block of four 32 x 32 accumulators;
-//   * per K step of BK = 32: the X tile is copied to LDS ([m][k], k contiguous);
-//     the B tile is read as Q4_0 (each lane: two rows x one 8-column quarter
-//     block) and dequantized in registers to fp16 with packed half arithmetic,
-//     w = fp16((q - 8) * d) rounded once, then written to LDS transposed
-//     ([n][k], k contiguous) so that both MFMA operands are 16-byte LDS reads;
-//   * two LDS stages: the next tile's global loads are in flight while the
-//     current one is contracted; one barrier per K step.
+// gemm_q4_0_kernel (K % 8 == 0, N % 256 == 0, X and B 16-byte aligned):
+//   * workgroup tile 128 x 256 and 512 lanes: 4 consumer waves in a 2 x 2
+//     grid, each 64 x 128 (eight 32 x 32 accumulators), only issue MFMAs; 4
+//     producer waves issue the copies and dequantize, so the VALU work runs
+//     beside the MFMAs on each SIMD; K steps of 64;
+//   * X tiles and raw Q4_0 row segments (8 blocks = 144 aligned bytes per
+//     row) are copied global -> LDS by LDS-DMA loads (no registers), X three
+//     and B four steps deep, issued two and three steps ahead;
+//   * each step the lanes dequantize the next step's raw B into an fp16 tile
+//     [n][k]: w = fp16((q - 8) * d) with packed half arithmetic, one rounding;
+//   * both LDS tiles are XOR-swizzled in 16-byte chunks, so the MFMA operand
+//     reads (16 bytes per lane, 32 rows) and the dequant stores spread over
+//     the LDS banks; for X the swizzle is applied on the source side of the
+//     copy;
+//   * one barrier per step, preceded by explicit waits for this wave's copies
+//     and LDS stores (a plain __syncthreads would also drain the copies that
+//     are meant to stay in flight).
+// gemm_q4_0_generic_kernel handles every other shape: 128 x 128 tiles, K
+// steps of 32, X through registers, B read block by block.
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
 
@@ -120,7 +132,7 @@ __device__ __forceinline__ void store_stage(const Stage& st, _Float16* As, _Floa
   }
 }
 
-__global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_generic_kernel(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) _Float16 As[2][BM * LDA];
   __shared__ __attribute__((aligned(16))) _Float16 Bs[2][BN * LDB];
 
@@ -190,6 +202,280 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_kernel(GemmArgs g) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Aligned-shape kernel
+// ---------------------------------------------------------------------------
+namespace fast {
+constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int kXStages = 3, kRStages = 4;
+constexpr int kXChunks = BM * BK / 8;                     // 16-byte chunks per X stage: 1024
+constexpr int kXBytes = kXChunks * 16;                    // 16 KiB
+constexpr int kRowChunks = (BN / kBlockWeights) * kBlockBytes / 16;  // 9 per raw row
+constexpr int kRChunks = BK * kRowChunks;                 // 576
+constexpr int kRInstr = (kRChunks + kGemmThreads - 1) / kGemmThreads;  // 3
+constexpr int kRBytes = kRInstr * kGemmThreads * 16;      // 12 KiB
+constexpr int kBBytes = BN * BK * 2;                      // 32 KiB fp16 tile
+constexpr int kXInstr = kXChunks / kGemmThreads;          // 4
+constexpr int kGroup = kXInstr + kRInstr;                 // copies issued per step
+constexpr int kLdsBytes = kXStages * kXBytes + kRStages * kRBytes + 2 * kBBytes;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+struct Args {
+  const uint16_t* X;
+  const uint8_t* B;
+  float* Y;
+  int M, N, K, NB, tiles_n, nk;
+};
+
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
+
+__device__ __forceinline__ uint8_t* xstage(uint8_t* lds, int s) { return lds + s * kXBytes; }
+__device__ __forceinline__ uint8_t* rstage(uint8_t* lds, int s) {
+  return lds + kXStages * kXBytes + s * kRBytes;
+}
+__device__ __forceinline__ uint8_t* bstage(uint8_t* lds, int s) {
+  return lds + kXStages * kXBytes + kRStages * kRBytes + s * kBBytes;
+}
+
+// LDS tiles hold rows of 64 halves (128 bytes = 8 chunks of 16 bytes); chunk
+// c of row r is stored at position c ^ swz(r). A 16-byte read is served 16
+// lanes at a time: with rows of 32 banks, lanes on consecutive rows hit
+// disjoint banks when the even rows and the odd rows each take 8 different
+// positions, which (r >> 1) & 7 gives. The B tile adds r >> 5 (the block
+// column), which spreads the dequant stores of one instruction (8 blocks of
+// the same column offset) over the banks too.
+__device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_b(int n) { return ((n >> 1) ^ (n >> 5)) & 7; }
+
+// Issue the copies of K step ks: X into stage ks % 3 and raw B into stage
+// ks % 4. Steps past the end (and rows/columns past M, K) read out of range:
+// zeros, no memory access.
+__device__ __forceinline__ void issue_x(const Args& g, uint8_t* lds, __amdgpu_buffer_rsrc_t rx,
+                                        int m0, int ks, int t) {
+  constexpr uint32_t kOut = 0x80000000u;
+  const int wave = t / kWaveSize;
+  uint8_t* dst = xstage(lds, ks % kXStages);
+  const int k0 = ks * BK;
+#pragma unroll
+  for (int i = 0; i < kXInstr; ++i) {
+    const int slot = i * kGemmThreads + t;  // row r = slot / 8, stored position slot % 8
+    const int r = slot >> 3;
+    const int c = (slot & 7) ^ swz_x(r);   // source chunk landing in that position
+    const int m = m0 + r;
+    const int k = k0 + 8 * c;
+    const uint32_t off = (m < g.M && k < g.K) ? ((uint32_t)m * (uint32_t)g.K + k) * 2u : kOut;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rx, (lds_void_t*)(dst + (i * kGemmThreads + wave * kWaveSize) * 16), 16, off, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ void issue_r(const Args& g, uint8_t* lds, __amdgpu_buffer_rsrc_t rb,
+                                        int j0, int ks, int t) {
+  constexpr uint32_t kOut = 0x80000000u;
+  const int wave = t / kWaveSize;
+  uint8_t* dst = rstage(lds, ks % kRStages);
+  const int k0 = ks * BK;
+  const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
+#pragma unroll
+  for (int i = 0; i < kRInstr; ++i) {
+    const int q = i * kGemmThreads + t;  // raw row q / 9, piece q % 9
+    const int row = q / kRowChunks;
+    const int pc = q - row * kRowChunks;
+    const int k = k0 + row;
+    const uint32_t off = (q < kRChunks && k < g.K)
+                             ? (uint32_t)k * row_bytes + (uint32_t)j0 * kBlockBytes + 16u * pc
+                             : kOut;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_void_t*)(dst + (i * kGemmThreads + wave * kWaveSize) * 16), 16, off, 0, 0, 0);
+  }
+}
+
+// Byte offset of the fp16 pair (k, k+1), k = 2*kp, of column n in a B tile.
+__device__ __forceinline__ uint32_t bpos(int n, int kp) {
+  return (uint32_t)n * (BK * 2) + (uint32_t)(((kp >> 2) ^ swz_b(n)) << 4) +
+         (uint32_t)((kp & 3) << 2);
+}
+
+// Dequantization of raw stage rs into fp16 tile bs, split so it can be
+// interleaved with the MFMAs. Unit u = t + 256*i (4 per lane) covers row pair
+// kp (rows 2kp, 2kp+1), block jb and quarter qq (8 columns), with bits
+// u[0:2] = kp % 8, u[3:5] = jb, u[6:7] = kp / 8, u[8:9] = qq: the 64 lanes of
+// a wave span 8 row pairs x 8 blocks, so the raw reads (rows 288 bytes apart,
+// blocks 18 bytes apart) and the tile stores spread over the LDS banks.
+struct RawUnit {
+  uint32_t d0, d1;      // scale bits of rows 2kp, 2kp+1
+  uint32_t w0[2], w1[2];  // aligned dwords covering the 4 nibble bytes
+};
+
+__device__ __forceinline__ int unit_kp(int u) { return (u & 7) | (((u >> 6) & 3) << 3); }
+__device__ __forceinline__ int unit_jb(int u) { return (u >> 3) & 7; }
+__device__ __forceinline__ int unit_qq(int u) { return (u >> 8) & 3; }
+
+__device__ __forceinline__ uint32_t unit_blk(int t, int i, int r) {
+  const int u = t + i * kGemmThreads;
+  return (uint32_t)(2 * unit_kp(u) + r) * (kRowChunks * 16) + unit_jb(u) * kBlockBytes;
+}
+
+__device__ __forceinline__ uint32_t unit_qoff(int t, int i, int r) {
+  const int u = t + i * kGemmThreads;
+  return unit_blk(t, i, r) + 2 + 4 * unit_qq(u);  // 2-byte aligned
+}
+
+__device__ __forceinline__ void read_unit(const uint8_t* __restrict__ rs, int t, int i,
+                                          RawUnit& ru) {
+  ru.d0 = *reinterpret_cast<const uint16_t*>(rs + unit_blk(t, i, 0));
+  ru.d1 = *reinterpret_cast<const uint16_t*>(rs + unit_blk(t, i, 1));
+  const uint32_t o0 = unit_qoff(t, i, 0) & ~3u, o1 = unit_qoff(t, i, 1) & ~3u;
+  ru.w0[0] = *reinterpret_cast<const uint32_t*>(rs + o0);
+  ru.w0[1] = *reinterpret_cast<const uint32_t*>(rs + o0 + 4);
+  ru.w1[0] = *reinterpret_cast<const uint32_t*>(rs + o1);
+  ru.w1[1] = *reinterpret_cast<const uint32_t*>(rs + o1 + 4);
+}
+
+__device__ __forceinline__ void convert_unit(const RawUnit& ru, int t, int i,
+                                             uint8_t* __restrict__ bs) {
+  const int u = t + i * kGemmThreads;
+  const int kp = unit_kp(u);
+  const int nb = unit_jb(u) * 32 + unit_qq(u) * 8;
+  const uint32_t q0 = __builtin_amdgcn_alignbyte(ru.w0[1], ru.w0[0], unit_qoff(t, i, 0) & 3u);
+  const uint32_t q1 = __builtin_amdgcn_alignbyte(ru.w1[1], ru.w1[0], unit_qoff(t, i, 1) & 3u);
+  const half2v d2 = __builtin_bit_cast(half2v, ru.d0 | (ru.d1 << 16));
+  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+#pragma unroll
+  for (int by = 0; by < 4; ++by) {
+    // bytes [q0.by, 0, q1.by, 0]: row k's byte in the low half, row k+1's in
+    // the high half (v_perm_b32; selector 0x0c gives a zero byte)
+    const uint32_t sel = 0x0c000c00u | ((4u + by) << 16) | by;
+    const uint32_t pair = __builtin_amdgcn_perm(q1, q0, sel);
+    // binary16 0x6400 | v is 1024 + v exactly (v < 1024)
+    const uint32_t lo = (pair & 0x000f000fu) | 0x64006400u;
+    const uint32_t hi = ((pair >> 4) & 0x000f000fu) | 0x64006400u;
+    const half2v wlo = (__builtin_bit_cast(half2v, lo) - off) * d2;  // (q - 8) * d, one rounding
+    const half2v whi = (__builtin_bit_cast(half2v, hi) - off) * d2;
+    *reinterpret_cast<half2v*>(bs + bpos(nb + 2 * by, kp)) = wlo;
+    *reinterpret_cast<half2v*>(bs + bpos(nb + 2 * by + 1, kp)) = whi;
+  }
+}
+
+__device__ __forceinline__ void dequant(const uint8_t* __restrict__ rs, uint8_t* __restrict__ bs,
+                                        int t) {
+  RawUnit ru[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_unit(rs, t, i, ru[i]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) convert_unit(ru[i], t, i, bs);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 512 lanes: waves 0-3 contract (MFMA only), waves 4-7 produce (copies and
+// dequantization). Both roles pass one barrier per K step, so a step's
+// dequant (VALU) runs on the same SIMDs while the matrix cores run the MFMAs.
+__global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int tm = L / g.tiles_n;
+  const int tn = L - tm * g.tiles_n;
+  const int m0 = tm * BM;
+  const int j0 = tn * (BN / kBlockWeights);
+  const int wave = threadIdx.x >> 6;
+
+  if (wave >= 4) {
+    // ------------------------------------------------------------ producer
+    const int pt = threadIdx.x - kGemmThreads;  // 0..255
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(g.X), (short)0, (int)((uint32_t)g.M * (uint32_t)g.K * 2u),
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(g.B), (short)0, (int)((uint32_t)g.K * (uint32_t)g.NB * kBlockBytes),
+        0x00020000);
+    // Prologue: X(0), raw(0), raw(1) | X(1), raw(2); then raw(0) -> B(0).
+    issue_x(g, lds, rx, m0, 0, pt);
+    issue_r(g, lds, rb, j0, 0, pt);
+    issue_r(g, lds, rb, j0, 1, pt);
+    issue_x(g, lds, rx, m0, 1, pt);
+    issue_r(g, lds, rb, j0, 2, pt);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup + kRInstr));  // X(0), raw(0) landed
+    lds_barrier();                                           // barrier A: visible to producers
+    dequant(rstage(lds, 0), bstage(lds, 0), pt);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);  // raw(1); B(0) stores done
+    lds_barrier();                                           // barrier B: X(0), B(0) ready
+    for (int ks = 0; ks < g.nk; ++ks) {
+      issue_x(g, lds, rx, m0, ks + 2, pt);
+      issue_r(g, lds, rb, j0, ks + 3, pt);
+      __builtin_amdgcn_sched_barrier(0);
+      // B(ks+1) from raw(ks+1); on the last step the raw stage holds
+      // out-of-range zeros and the tile is never read
+      dequant(rstage(lds, (ks + 1) % kRStages), bstage(lds, (ks + 1) & 1), pt);
+      // X(ks+1), raw(ks+2) landed; B(ks+1) stores done
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);
+      lds_barrier();
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy lands after the workgroup ends
+    return;
+  }
+
+  // -------------------------------------------------------------- consumer
+  const int lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  float16v acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  lds_barrier();  // barrier A
+  lds_barrier();  // barrier B
+  for (int ks = 0; ks < g.nk; ++ks) {
+    const uint8_t* xs = xstage(lds, ks % kXStages);
+    const uint8_t* bs = bstage(lds, ks & 1);
+#pragma unroll
+    for (int kk = 0; kk < BK / 16; ++kk) {
+      const int kc = 2 * kk + (lane >> 5);  // 16-byte k chunk of this lane
+      half8 af[2], bf[4];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int r = wm * 64 + i * 32 + (lane & 31);
+        af[i] = *reinterpret_cast<const half8*>(xs + (r * 8 + (kc ^ swz_x(r))) * 16);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = wn * 128 + j * 32 + (lane & 31);
+        bf[j] = *reinterpret_cast<const half8*>(bs + n * (BK * 2) + ((kc ^ swz_b(n)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS reads done before the stage is reused
+    lds_barrier();
+  }
+
+  // Accumulator layout of a 32 x 32 fp32 MFMA result: lane l holds column
+  // l % 32; register r holds row 8*(r/4) + 4*(l/32) + r%4.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = j0 * kBlockWeights + wn * 128 + j * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < g.M) g.Y[(size_t)row * g.N + col] = acc[i][j][r];
+      }
+    }
+}
+}  // namespace fast
+
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int N, int K,
@@ -203,10 +489,29 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
   g.K = K;
   g.NB = N / kBlockWeights;
   g.tiles_n = (N + BN - 1) / BN;
+  const bool aligned16 = ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
+  if (K % 8 == 0 && N % fast::BN == 0 && aligned16) {
+    fast::Args f;
+    f.X = X;
+    f.B = B;
+    f.Y = Y;
+    f.M = M;
+    f.N = N;
+    f.K = K;
+    f.NB = N / kBlockWeights;
+    f.tiles_n = N / fast::BN;
+    f.nk = (K + fast::BK - 1) / fast::BK;
+    const long long tiles = (long long)((M + fast::BM - 1) / fast::BM) * f.tiles_n;
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fast::gemm_q4_0_kernel, dim3((unsigned)tiles), dim3(2 * kGemmThreads),
+                       fast::kLdsBytes, st, f);
+    return hipGetLastError();
+  }
   const int tiles_m = (M + BM - 1) / BM;
   const long long tiles = (long long)tiles_m * g.tiles_n;
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_q4_0_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, st, g);
+  hipLaunchKernelGGL(gemm_q4_0_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, st,
+                     g);
   return hipGetLastError();
 }
 

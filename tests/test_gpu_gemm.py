@@ -24,6 +24,37 @@ def test_gemm_small_match_oracle(M, K, N):
     check_tol(gemm(X16, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
 
 
+# K % 8 == 0, N % 256 == 0 and 16-byte aligned operands take the LDS-DMA
+# pipelined kernel (128 x 256 tiles, K steps of 64): single rows and steps,
+# ragged M and K tails.
+ALIGNED = [(1, 8, 256), (130, 72, 512), (129, 1000, 768), (300, 136, 256), (2, 4096, 1024),
+           (128, 64, 256)]
+
+
+@pytest.mark.parametrize("M,K,N", ALIGNED)
+def test_gemm_aligned_shapes_match_oracle(M, K, N):
+    X16 = datagen.to_f16(datagen.activations(M + K + 11, M, K))
+    B = datagen.q4_0_random(N * 5 + K, K, N)
+    ref, bnd = oracle.q4_0_matmul_f16(X16, B, N, K)
+    check_tol(gemm(X16, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
+
+
+def test_gemm_misaligned_x_takes_generic_path():
+    """X only 4-byte aligned: the per-lane kernel must agree with the oracle on
+    a shape that would otherwise take the pipelined one."""
+    import torch
+    from moe_experts_amd import q4_0_gemm
+    from tests.gpu_util import dev
+    M, K, N = 96, 256, 512
+    X16 = datagen.to_f16(datagen.activations(21, M, K))
+    B = datagen.q4_0_random(22, K, N)
+    ref, bnd = oracle.q4_0_matmul_f16(X16, B, N, K)
+    raw = torch.zeros(M * K + 8, dtype=torch.float16, device=dev())
+    Xmis = raw[2:2 + M * K].view(M, K)
+    Xmis.copy_(torch.from_numpy(X16))
+    check_tol(to_host(q4_0_gemm(Xmis, to_dev(B), N)), ref, bnd, TOL, "misaligned X")
+
+
 def test_gemm_integer_exact_bitwise():
     M, K, N = 256, 4096, 512
     g = np.random.Generator(np.random.PCG64(77))
