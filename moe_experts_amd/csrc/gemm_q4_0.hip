@@ -9,7 +9,7 @@
 // 32 along N within a row), so a column's K values sit in different rows and
 // the B operand is dequantized into LDS transposed ([n][k]).
 //
-// gemm_q4_0_kernel (K % 8 == 0, N % 256 == 0, X and B 16-byte aligned):
+// gemm_q4_0_kernel (K % 64 == 0, N % 256 == 0, X and B 16-byte aligned):
 //   * workgroup tile 128 x 256 and 512 lanes: 4 consumer waves in a 2 x 2
 //     grid, each 64 x 128 (eight 32 x 32 accumulators), only issue MFMAs; 4
 //     producer waves issue the copies and dequantize, so the VALU work runs
@@ -249,129 +249,148 @@ __device__ __forceinline__ uint8_t* bstage(uint8_t* lds, int s) {
 __device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_b(int n) { return ((n >> 1) ^ (n >> 5)) & 7; }
 
-// Issue the copies of K step ks: X into stage ks % 3 and raw B into stage
-// ks % 4. Steps past the end (and rows/columns past M, K) read out of range:
-// zeros, no memory access.
-__device__ __forceinline__ void issue_x(const Args& g, uint8_t* lds, __amdgpu_buffer_rsrc_t rx,
-                                        int m0, int ks, int t) {
-  constexpr uint32_t kOut = 0x80000000u;
-  const int wave = t / kWaveSize;
-  uint8_t* dst = xstage(lds, ks % kXStages);
-  const int k0 = ks * BK;
-#pragma unroll
-  for (int i = 0; i < kXInstr; ++i) {
-    const int slot = i * kGemmThreads + t;  // row r = slot / 8, stored position slot % 8
-    const int r = slot >> 3;
-    const int c = (slot & 7) ^ swz_x(r);   // source chunk landing in that position
-    const int m = m0 + r;
-    const int k = k0 + 8 * c;
-    const uint32_t off = (m < g.M && k < g.K) ? ((uint32_t)m * (uint32_t)g.K + k) * 2u : kOut;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rx, (lds_void_t*)(dst + (i * kGemmThreads + wave * kWaveSize) * 16), 16, off, 0, 0, 0);
-  }
-}
-
-__device__ __forceinline__ void issue_r(const Args& g, uint8_t* lds, __amdgpu_buffer_rsrc_t rb,
-                                        int j0, int ks, int t) {
-  constexpr uint32_t kOut = 0x80000000u;
-  const int wave = t / kWaveSize;
-  uint8_t* dst = rstage(lds, ks % kRStages);
-  const int k0 = ks * BK;
-  const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
-#pragma unroll
-  for (int i = 0; i < kRInstr; ++i) {
-    const int q = i * kGemmThreads + t;  // raw row q / 9, piece q % 9
-    const int row = q / kRowChunks;
-    const int pc = q - row * kRowChunks;
-    const int k = k0 + row;
-    const uint32_t off = (q < kRChunks && k < g.K)
-                             ? (uint32_t)k * row_bytes + (uint32_t)j0 * kBlockBytes + 16u * pc
-                             : kOut;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (lds_void_t*)(dst + (i * kGemmThreads + wave * kWaveSize) * 16), 16, off, 0, 0, 0);
-  }
-}
-
 // Byte offset of the fp16 pair (k, k+1), k = 2*kp, of column n in a B tile.
 __device__ __forceinline__ uint32_t bpos(int n, int kp) {
   return (uint32_t)n * (BK * 2) + (uint32_t)(((kp >> 2) ^ swz_b(n)) << 4) +
          (uint32_t)((kp & 3) << 2);
 }
 
-// Dequantization of raw stage rs into fp16 tile bs, split so it can be
-// interleaved with the MFMAs. Unit u = t + 256*i (4 per lane) covers row pair
+// Dequantization units: unit u = t + 256*i (4 per producer lane) covers row pair
 // kp (rows 2kp, 2kp+1), block jb and quarter qq (8 columns), with bits
 // u[0:2] = kp % 8, u[3:5] = jb, u[6:7] = kp / 8, u[8:9] = qq: the 64 lanes of
 // a wave span 8 row pairs x 8 blocks, so the raw reads (rows 288 bytes apart,
 // blocks 18 bytes apart) and the tile stores spread over the LDS banks.
-struct RawUnit {
-  uint32_t d0, d1;      // scale bits of rows 2kp, 2kp+1
-  uint32_t w0[2], w1[2];  // aligned dwords covering the 4 nibble bytes
-};
-
 __device__ __forceinline__ int unit_kp(int u) { return (u & 7) | (((u >> 6) & 3) << 3); }
 __device__ __forceinline__ int unit_jb(int u) { return (u >> 3) & 7; }
 __device__ __forceinline__ int unit_qq(int u) { return (u >> 8) & 3; }
-
-__device__ __forceinline__ uint32_t unit_blk(int t, int i, int r) {
-  const int u = t + i * kGemmThreads;
-  return (uint32_t)(2 * unit_kp(u) + r) * (kRowChunks * 16) + unit_jb(u) * kBlockBytes;
-}
-
-__device__ __forceinline__ uint32_t unit_qoff(int t, int i, int r) {
-  const int u = t + i * kGemmThreads;
-  return unit_blk(t, i, r) + 2 + 4 * unit_qq(u);  // 2-byte aligned
-}
-
-__device__ __forceinline__ void read_unit(const uint8_t* __restrict__ rs, int t, int i,
-                                          RawUnit& ru) {
-  ru.d0 = *reinterpret_cast<const uint16_t*>(rs + unit_blk(t, i, 0));
-  ru.d1 = *reinterpret_cast<const uint16_t*>(rs + unit_blk(t, i, 1));
-  const uint32_t o0 = unit_qoff(t, i, 0) & ~3u, o1 = unit_qoff(t, i, 1) & ~3u;
-  ru.w0[0] = *reinterpret_cast<const uint32_t*>(rs + o0);
-  ru.w0[1] = *reinterpret_cast<const uint32_t*>(rs + o0 + 4);
-  ru.w1[0] = *reinterpret_cast<const uint32_t*>(rs + o1);
-  ru.w1[1] = *reinterpret_cast<const uint32_t*>(rs + o1 + 4);
-}
-
-__device__ __forceinline__ void convert_unit(const RawUnit& ru, int t, int i,
-                                             uint8_t* __restrict__ bs) {
-  const int u = t + i * kGemmThreads;
-  const int kp = unit_kp(u);
-  const int nb = unit_jb(u) * 32 + unit_qq(u) * 8;
-  const uint32_t q0 = __builtin_amdgcn_alignbyte(ru.w0[1], ru.w0[0], unit_qoff(t, i, 0) & 3u);
-  const uint32_t q1 = __builtin_amdgcn_alignbyte(ru.w1[1], ru.w1[0], unit_qoff(t, i, 1) & 3u);
-  const half2v d2 = __builtin_bit_cast(half2v, ru.d0 | (ru.d1 << 16));
-  const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
-#pragma unroll
-  for (int by = 0; by < 4; ++by) {
-    // bytes [q0.by, 0, q1.by, 0]: row k's byte in the low half, row k+1's in
-    // the high half (v_perm_b32; selector 0x0c gives a zero byte)
-    const uint32_t sel = 0x0c000c00u | ((4u + by) << 16) | by;
-    const uint32_t pair = __builtin_amdgcn_perm(q1, q0, sel);
-    // binary16 0x6400 | v is 1024 + v exactly (v < 1024)
-    const uint32_t lo = (pair & 0x000f000fu) | 0x64006400u;
-    const uint32_t hi = ((pair >> 4) & 0x000f000fu) | 0x64006400u;
-    const half2v wlo = (__builtin_bit_cast(half2v, lo) - off) * d2;  // (q - 8) * d, one rounding
-    const half2v whi = (__builtin_bit_cast(half2v, hi) - off) * d2;
-    *reinterpret_cast<half2v*>(bs + bpos(nb + 2 * by, kp)) = wlo;
-    *reinterpret_cast<half2v*>(bs + bpos(nb + 2 * by + 1, kp)) = whi;
-  }
-}
-
-__device__ __forceinline__ void dequant(const uint8_t* __restrict__ rs, uint8_t* __restrict__ bs,
-                                        int t) {
-  RawUnit ru[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) read_unit(rs, t, i, ru[i]);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) convert_unit(ru[i], t, i, bs);
-}
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// A producer lane's loop-invariant offsets. Copies: lane byte offsets of its
+// chunks at K step 0 (the step goes into the scalar offset; chunks past M or
+// past the tile read out of range), and the wave's LDS slot offsets.
+// Dequant: per unit, the offsets of the scale and of the aligned nibble
+// dwords inside a raw stage, the alignbyte shift, and the store offsets of
+// its four column pairs inside a B tile (column n+1 is 128 bytes after n).
+struct Producer {
+  __amdgpu_buffer_rsrc_t rx, rb;
+  uint32_t xoff[kXInstr], roff[kRInstr];
+  uint32_t wslot;                 // wave's first DMA slot byte offset (uniform)
+  uint32_t x_step, r_step;        // bytes per K step in X and B (uniform)
+  uint32_t rd[4], rw[4], sh[4];
+  uint32_t st[4][4];
+  int nk;
+
+  __device__ __forceinline__ void init(const Args& g, int m0, int j0, int t) {
+    constexpr uint32_t kOut = 0x80000000u;
+    nk = g.nk;
+    rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g.X), (short)0,
+                                           (int)((uint32_t)g.M * (uint32_t)g.K * 2u), 0x00020000);
+    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.B), (short)0,
+                                           (int)((uint32_t)g.K * (uint32_t)g.NB * kBlockBytes),
+                                           0x00020000);
+    const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
+    x_step = BK * 2;
+    r_step = BK * row_bytes;
+    wslot = (uint32_t)__builtin_amdgcn_readfirstlane(t >> 6) * (kWaveSize * 16);
+#pragma unroll
+    for (int i = 0; i < kXInstr; ++i) {
+      const int slot = i * kGemmThreads + t;  // row r = slot / 8, stored position slot % 8
+      const int r = slot >> 3;
+      const int c = (slot & 7) ^ swz_x(r);   // source chunk landing in that position
+      const int m = m0 + r;
+      xoff[i] = m < g.M ? ((uint32_t)m * (uint32_t)g.K + 8u * c) * 2u : kOut;
+    }
+#pragma unroll
+    for (int i = 0; i < kRInstr; ++i) {
+      const int q = i * kGemmThreads + t;  // raw row q / 9, piece q % 9
+      const int row = q / kRowChunks;
+      const int pc = q - row * kRowChunks;
+      roff[i] = q < kRChunks
+                    ? (uint32_t)row * row_bytes + (uint32_t)j0 * kBlockBytes + 16u * pc
+                    : kOut;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = t + i * kGemmThreads;
+      const int kp = unit_kp(u), jb = unit_jb(u), qq = unit_qq(u);
+      rd[i] = (uint32_t)(2 * kp) * (kRowChunks * 16) + jb * kBlockBytes;
+      const uint32_t o = rd[i] + 2 + 4 * qq;  // 2-byte aligned; row 2kp+1 is 144 bytes on
+      sh[i] = o & 3u;
+      rw[i] = o - sh[i];
+      const int nb = jb * 32 + qq * 8;
+#pragma unroll
+      for (int by = 0; by < 4; ++by) st[i][by] = bpos(nb + 2 * by, kp);
+    }
+  }
+
+  // Copies of K step ks: X into stage ks % 3, raw B into stage ks % 4. A
+  // step past the end reads out of range in every lane (zeros, no memory
+  // access; its scalar offset is zero, so no lane offset plus scalar offset
+  // can point past the buffer).
+  __device__ __forceinline__ void issue_x(uint8_t* lds, int ks) const {
+    constexpr uint32_t kOut = 0x80000000u;
+    const bool valid = ks < nk;
+    const uint32_t so = valid ? (uint32_t)ks * x_step : 0u;
+    uint8_t* dst = xstage(lds, ks % kXStages) + wslot;
+#pragma unroll
+    for (int i = 0; i < kXInstr; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + i * kGemmThreads * 16), 16,
+                                               valid ? xoff[i] : kOut, so, 0, 0);
+  }
+  __device__ __forceinline__ void issue_r(uint8_t* lds, int ks) const {
+    constexpr uint32_t kOut = 0x80000000u;
+    const bool valid = ks < nk;
+    const uint32_t so = valid ? (uint32_t)ks * r_step : 0u;
+    uint8_t* dst = rstage(lds, ks % kRStages) + wslot;
+#pragma unroll
+    for (int i = 0; i < kRInstr; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + i * kGemmThreads * 16), 16,
+                                               valid ? roff[i] : kOut, so, 0, 0);
+  }
+
+  // Raw stage -> fp16 B tile, w = fp16((q - 8) * d).
+  __device__ __forceinline__ void dequant(const uint8_t* __restrict__ rsb,
+                                          uint8_t* __restrict__ bsb) const {
+    const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
+    uint32_t d0[4], d1[4], q0[4], q1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint8_t* pd = rsb + rd[i];
+      const uint8_t* pw = rsb + rw[i];
+      d0[i] = *reinterpret_cast<const uint16_t*>(pd);
+      d1[i] = *reinterpret_cast<const uint16_t*>(pd + kRowChunks * 16);
+      const uint32_t a0 = *reinterpret_cast<const uint32_t*>(pw);
+      const uint32_t a1 = *reinterpret_cast<const uint32_t*>(pw + 4);
+      const uint32_t b0 = *reinterpret_cast<const uint32_t*>(pw + kRowChunks * 16);
+      const uint32_t b1 = *reinterpret_cast<const uint32_t*>(pw + kRowChunks * 16 + 4);
+      q0[i] = __builtin_amdgcn_alignbyte(a1, a0, sh[i]);
+      q1[i] = __builtin_amdgcn_alignbyte(b1, b0, sh[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const half2v d2 = __builtin_bit_cast(half2v, d0[i] | (d1[i] << 16));
+#pragma unroll
+      for (int by = 0; by < 4; ++by) {
+        // bytes [q0.by, 0, q1.by, 0]: row 2kp's byte in the low half, row
+        // 2kp+1's in the high half (v_perm_b32; selector 0x0c gives zero)
+        const uint32_t sel = 0x0c000c00u | ((4u + by) << 16) | by;
+        const uint32_t pair = __builtin_amdgcn_perm(q1[i], q0[i], sel);
+        // binary16 0x6400 | v is 1024 + v exactly (v < 1024)
+        const uint32_t lo = (pair & 0x000f000fu) | 0x64006400u;
+        const uint32_t hi = ((pair >> 4) & 0x000f000fu) | 0x64006400u;
+        const half2v wlo = (__builtin_bit_cast(half2v, lo) - off) * d2;  // one rounding
+        const half2v whi = (__builtin_bit_cast(half2v, hi) - off) * d2;
+        uint8_t* pst = bsb + st[i][by];
+        *reinterpret_cast<half2v*>(pst) = wlo;
+        *reinterpret_cast<half2v*>(pst + BK * 2) = whi;
+      }
+    }
+  }
+};
 
 // 512 lanes: waves 0-3 contract (MFMA only), waves 4-7 produce (copies and
 // dequantization). Both roles pass one barrier per K step, so a step's
@@ -387,33 +406,30 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 
   if (wave >= 4) {
     // ------------------------------------------------------------ producer
-    const int pt = threadIdx.x - kGemmThreads;  // 0..255
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(g.X), (short)0, (int)((uint32_t)g.M * (uint32_t)g.K * 2u),
-        0x00020000);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(g.B), (short)0, (int)((uint32_t)g.K * (uint32_t)g.NB * kBlockBytes),
-        0x00020000);
+    Producer pr;
+    pr.init(g, m0, j0, (int)threadIdx.x - kGemmThreads);
     // Prologue: X(0), raw(0), raw(1) | X(1), raw(2); then raw(0) -> B(0).
-    issue_x(g, lds, rx, m0, 0, pt);
-    issue_r(g, lds, rb, j0, 0, pt);
-    issue_r(g, lds, rb, j0, 1, pt);
-    issue_x(g, lds, rx, m0, 1, pt);
-    issue_r(g, lds, rb, j0, 2, pt);
+    pr.issue_x(lds, 0);
+    pr.issue_r(lds, 0);
+    pr.issue_r(lds, 1);
+    pr.issue_x(lds, 1);
+    pr.issue_r(lds, 2);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup + kRInstr));  // X(0), raw(0) landed
-    lds_barrier();                                           // barrier A: visible to producers
-    dequant(rstage(lds, 0), bstage(lds, 0), pt);
+    lds_barrier();                                           // barrier A
+    pr.dequant(rstage(lds, 0), bstage(lds, 0));
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);  // raw(1); B(0) stores done
     lds_barrier();                                           // barrier B: X(0), B(0) ready
     for (int ks = 0; ks < g.nk; ++ks) {
-      issue_x(g, lds, rx, m0, ks + 2, pt);
-      issue_r(g, lds, rb, j0, ks + 3, pt);
+      // X two steps ahead, raw B three (the stages they overwrite were last
+      // read before the previous barrier)
+      pr.issue_x(lds, ks + 2);
+      pr.issue_r(lds, ks + 3);
       __builtin_amdgcn_sched_barrier(0);
       // B(ks+1) from raw(ks+1); on the last step the raw stage holds
       // out-of-range zeros and the tile is never read
-      dequant(rstage(lds, (ks + 1) % kRStages), bstage(lds, (ks + 1) & 1), pt);
-      // X(ks+1), raw(ks+2) landed; B(ks+1) stores done
+      pr.dequant(rstage(lds, (ks + 1) % kRStages), bstage(lds, (ks + 1) & 1));
+      // X(ks+1), raw(ks+2) (issued one step ago) landed; B(ks+1) stores done
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);
       lds_barrier();
     }
@@ -490,7 +506,7 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
   g.NB = N / kBlockWeights;
   g.tiles_n = (N + BN - 1) / BN;
   const bool aligned16 = ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-  if (K % 8 == 0 && N % fast::BN == 0 && aligned16) {
+  if (K % fast::BK == 0 && N % fast::BN == 0 && aligned16) {
     fast::Args f;
     f.X = X;
     f.B = B;
