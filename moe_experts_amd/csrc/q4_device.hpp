@@ -172,10 +172,11 @@ __device__ __forceinline__ void load_part_buf(__amdgpu_buffer_rsrc_t r, uint32_t
 // row is past the tile adds zeros (zero scale, zero activation).
 //
 // Activations: the tile's activation rows are staged in LDS as
-// xs[m * rows_pad + row] (rows_pad = rows rounded up to whole batches, the
-// padding zeroed) by LDS-DMA loads (buffer_load_dword ... lds): no registers,
-// all issued before the weight batches, one round trip. All lanes of a row
-// phase read the same LDS word (broadcast).
+// xs[row * XW + m] (XW = M rounded up to 1, 2, 4 or 8; rows_pad = rows
+// rounded up to whole batches, the padding zeroed) by LDS-DMA loads
+// (buffer_load_dword ... lds): no registers, all issued before the weight
+// batches, one round trip. A row's M values are one or two aligned LDS reads,
+// the same address for all lanes of a row phase (broadcast).
 //   x, x_bytes : activations; activation row m of the tile is x + xoff[m]
 //                floats, indexed by the matrix row k
 //   xs         : LDS of tile_x_floats<M>(rows, P, RB) floats
@@ -195,14 +196,79 @@ __host__ __device__ constexpr int tile_rows_padded(int rows, int P, int RB) {
   return ((rows + P - 1) / P + RB - 1) / RB * RB * P;
 }
 
+// Floats per staged activation row (a power of two >= M).
+template <int M>
+__host__ __device__ constexpr int xs_width() {
+  return M <= 2 ? M : (M <= 4 ? 4 : 8);
+}
+
 // LDS floats of the staged activation tile, rounded up to whole staging
 // passes of 256 words (every DMA lane of the last pass writes inside it).
 template <int M>
 __host__ __device__ constexpr int tile_x_floats(int rows, int P, int RB) {
-  return (tile_rows_padded(rows, P, RB) * M + 255) / 256 * 256;
+  return (tile_rows_padded(rows, P, RB) * xs_width<M>() + 255) / 256 * 256;
 }
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Issue the LDS-DMA copies of an activation tile: word q = row * XW + m of
+// xs holds x[xoff[m] + k0 + row] for m < M and row < rows (lane q % 256 of
+// pass q / 256 loads it; the DMA writes lane l of a wave at M0 + 4*l). Other
+// words read out of range (no memory access).
+template <int M>
+__device__ __forceinline__ void stage_x_tile(const float* __restrict__ x, uint32_t x_bytes,
+                                             const int (&xoff)[M], int k0, int rows, int rows_pad,
+                                             float* __restrict__ xs) {
+  constexpr int XW = xs_width<M>();
+  constexpr uint32_t kOutOfRange = 0x80000000u;
+  const int t = threadIdx.x;
+  const int wave = t / kWaveSize;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+  for (int q0 = 0; q0 < XW * rows_pad; q0 += kThreads) {
+    const int q = q0 + t;
+    const int row = q / XW;
+    const int m = q - row * XW;
+    int xo = 0;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm)
+      if (mm == m) xo = xoff[mm];
+    const uint32_t off = (m < M && row < rows) ? (uint32_t)(xo + k0 + row) * 4u : kOutOfRange;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4, off,
+                                             0, 0, 0);
+  }
+}
+
+// Zero the padding rows [rows, rows_pad) of a staged activation tile.
+template <int M>
+__device__ __forceinline__ void zero_x_pad(float* __restrict__ xs, int rows, int rows_pad) {
+  constexpr int XW = xs_width<M>();
+  for (int idx = threadIdx.x; idx < (rows_pad - rows) * XW; idx += kThreads)
+    xs[rows * XW + idx] = 0.0f;
+}
+
+// The M activations of tile row `row`.
+template <int M>
+__device__ __forceinline__ void read_x_row(const float* __restrict__ xs, int row,
+                                           float (&xv)[M]) {
+  constexpr int XW = xs_width<M>();
+  const float* p = xs + row * XW;
+  if constexpr (XW == 1) {
+    xv[0] = p[0];
+  } else if constexpr (XW == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    xv[0] = v.x;
+    xv[1] = v.y;
+  } else {
+#pragma unroll
+    for (int q = 0; q < XW / 4; ++q) {
+      const float4 v = *reinterpret_cast<const float4*>(p + 4 * q);
+      const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (4 * q + u < M) xv[4 * q + u] = e[u];
+    }
+  }
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations of
 // the wave are outstanding (n < 64); LDS and export counters are not waited on.
@@ -240,24 +306,7 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
   const uint32_t sbase = (uint32_t)g.k0 * row_bytes;           // uniform
   const int rows = active ? g.rows : 0;
 
-  // Stage the activation tile: element q of the [M][rows_pad] layout is
-  // loaded by lane q % 256 of pass q / 256 and lands at LDS word q (the DMA
-  // writes lane l of a wave at M0 + 4*l, M0 = xs + q0 + 64*wave words).
-  {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
-    for (int q0 = 0; q0 < M * rows_pad; q0 += kThreads) {
-      const int q = q0 + t;
-      const int m = q / rows_pad;
-      const int i = q - m * rows_pad;
-      int xo = 0;
-#pragma unroll
-      for (int mm = 0; mm < M; ++mm)
-        if (mm == m) xo = xoff[mm];
-      const uint32_t off = (m < M && i < g.rows) ? (uint32_t)(xo + g.k0 + i) * 4u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
-                                               off, 0, 0, 0);
-    }
-  }
+  stage_x_tile<M>(x, x_bytes, xoff, g.k0, g.rows, rows_pad, xs);
   // The wait below counts on every staging load being issued before the
   // weight loads.
   __builtin_amdgcn_sched_barrier(0);
@@ -274,11 +323,7 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
   auto compute_batch = [&](int b, BlockPart<LPB>(&R)[RB]) {
     float xv[RB][M];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int tr = (b * RB + i) * g.P + r;
-#pragma unroll
-      for (int m = 0; m < M; ++m) xv[i][m] = xs[m * rows_pad + tr];
-    }
+    for (int i = 0; i < RB; ++i) read_x_row<M>(xs, (b * RB + i) * g.P + r, xv[i]);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (b * RB + i < nl) fma_part<M, LPB>(xv[i], R[i], acc, corr);
@@ -292,13 +337,7 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
   // The staged activations have landed once at most the two weight batches'
   // loads are outstanding; then zero the padding rows and share the tile.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kLoadsPerBatch));
-  {
-    const int pad = rows_pad - g.rows;
-    for (int idx = t; idx < M * pad; idx += kThreads) {
-      const int m = idx / pad;
-      xs[m * rows_pad + g.rows + (idx - m * pad)] = 0.0f;
-    }
-  }
+  zero_x_pad<M>(xs, g.rows, rows_pad);
   __syncthreads();
   if (!active) return;
 
@@ -433,34 +472,13 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
     }
   };
 
-  // activation tile, as in tile_accumulate
-  {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
-    for (int q0 = 0; q0 < M * rows_pad; q0 += kThreads) {
-      const int q = q0 + t;
-      const int m = q / rows_pad;
-      const int i = q - m * rows_pad;
-      int xo = 0;
-#pragma unroll
-      for (int mm = 0; mm < M; ++mm)
-        if (mm == m) xo = xoff[mm];
-      const uint32_t off = (m < M && i < g.rows) ? (uint32_t)(xo + g.k0 + i) * 4u : kOutOfRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
-                                               off, 0, 0, 0);
-    }
-  }
+  stage_x_tile<M>(x, x_bytes, xoff, g.k0, g.rows, rows_pad, xs);
   __builtin_amdgcn_sched_barrier(0);
   stage_batch(0);
   stage_batch(1);
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * SS::NI));  // activations landed
-  {
-    const int pad = rows_pad - g.rows;
-    for (int idx = t; idx < M * pad; idx += kThreads) {
-      const int m = idx / pad;
-      xs[m * rows_pad + g.rows + (idx - m * pad)] = 0.0f;
-    }
-  }
+  zero_x_pad<M>(xs, g.rows, rows_pad);
   // Share the activation tile. A plain __syncthreads() would also wait for
   // the weight copies in flight (its release fence waits on every memory
   // operation); the tile's own copies have landed (vmcnt above), so only the
@@ -482,10 +500,8 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
       if (b * RB + i < nl) {  // uniform
         BlockPart<LPB> bp;
         read_block_part_lds<LPB>(buf, (i * SS::WP + seg0) * (SS::CPS * 16) + in_seg, part, bp);
-        const int tr = (b * RB + i) * P + r;
         float xv[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) xv[m] = xs[m * rows_pad + tr];
+        read_x_row<M>(xs, (b * RB + i) * P + r, xv);
         fma_part<M, LPB>(xv, bp, acc, corr);
       }
     }
