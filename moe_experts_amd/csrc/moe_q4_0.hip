@@ -9,8 +9,8 @@
 // five kernels on one stream (no host round trip, capturable in a graph):
 //
 //   1. route    : one workgroup groups the (token, slot) pairs by expert
-//                 (stable order) into work items of at most MC pairs of one
-//                 expert (MC = 8, or 1 for a single token).
+//                 (stable order) into work items of at most 8 pairs of one
+//                 expert. A single token skips it: its 6 pairs are the items.
 //   2. gate/up  : split-K GEMV tiles of the dense decode kernel over the
 //                 routed experts' gate and up matrices; a tile streams its
 //                 expert's 16-block row segments once for all pairs of its
@@ -32,6 +32,8 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kMaxChunk = 8;  // pairs per work item (MC <= kMaxChunk)
+constexpr int kSplitLoads = 8;     // act: splits summed with all loads in flight
+constexpr int kCombineSplits = 4;  // combine: same, per slot
 constexpr int kLPB = 2;       // half-block lane shares, for every item size
 constexpr int kJt = 16;       // block columns per tile: 288-byte row segments
 
@@ -139,6 +141,8 @@ struct ExpertArgs {
   int K, N, NB;                       // rows, columns, blocks per row of one matrix
   int C, Kt, S, nmat, npairs;
   int x_row_div;                      // activation row = pair / x_row_div, times K
+  const int32_t* __restrict__ ids;    // [npairs] expert ids (single-token items)
+  int E;
 };
 
 template <int M, bool STAGED>
@@ -179,11 +183,23 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
   const int per_item = a.nmat * a.C * a.S;
   const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int item = L / per_item;
-  // Both loads are issued before either is used (one round trip); the item
-  // array always has max_items records, so the read is in bounds.
-  const int n_items = *a.n_items;
-  const ItemRec it = a.items[item];
-  if (item >= n_items) return;
+  ItemRec it;
+  if constexpr (MC == 1) {
+    // One pair per item (a single token): item p is pair p, read straight
+    // from the routing ids; no routing table.
+    if (item >= a.npairs) return;
+    const int e = a.ids[item];
+    if (e < 0 || e >= a.E) return;  // an invalid slot contributes nothing
+    it.e = e;
+    it.cnt = 1;
+    it.pairs[0] = item;
+  } else {
+    // Both loads are issued before either is used (one round trip); the item
+    // array always has max_items records, so the read is in bounds.
+    const int n_items = *a.n_items;
+    it = a.items[item];
+    if (item >= n_items) return;
+  }
   int rest = L - item * per_item;
   const int c = rest % a.C;
   rest /= a.C;
@@ -209,17 +225,35 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
 // 3. h = SiLU(gate) * up from the split-K partials (split order)
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void moe_act_kernel(const float* __restrict__ part,
-                                                      const int32_t* __restrict__ ids,
                                                       float* __restrict__ h, int npairs, int I,
-                                                      int S, int E) {
+                                                      int S) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (size_t)npairs * I) return;
-  const int pair = (int)(idx / I);
-  const int e = ids[pair];
-  if (e < 0 || e >= E) return;
+  // Pairs with an invalid expert id have no partial sums; their h is never
+  // read, so they are not filtered here (no dependent id load).
   const size_t slab = (size_t)npairs * I;
-  const float g = sum_strided(part + idx, slab, S);
-  const float u = sum_strided(part + (size_t)S * slab + idx, slab, S);
+  float g, u;
+  if (S <= kSplitLoads) {
+    // all 2S loads in flight at once (indices clamped; extra values unused)
+    float tg[kSplitLoads], tu[kSplitLoads];
+#pragma unroll
+    for (int k = 0; k < kSplitLoads; ++k) {
+      const size_t sk = (size_t)min(k, S - 1);
+      tg[k] = part[sk * slab + idx];
+      tu[k] = part[((size_t)S + sk) * slab + idx];
+    }
+    g = 0.0f;
+    u = 0.0f;
+#pragma unroll
+    for (int k = 0; k < kSplitLoads; ++k)
+      if (k < S) {
+        g += tg[k];
+        u += tu[k];
+      }
+  } else {
+    g = sum_strided(part + idx, slab, S);
+    u = sum_strided(part + (size_t)S * slab + idx, slab, S);
+  }
   h[idx] = g / (1.0f + expf(-g)) * u;
 }
 
@@ -237,12 +271,37 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   const int n = (int)(idx - (size_t)t * H);
   const size_t slab = (size_t)T * topk * H;
   float acc = 0.0f;
-  for (int sl = 0; sl < topk; ++sl) {
-    const int e = ids[t * topk + sl];
-    if (e < 0 || e >= E) continue;
-    const size_t o = (size_t)(t * topk + sl) * H + n;
-    const float yd = sum_strided(part + o, slab, S);
-    acc = __builtin_fmaf(w[t * topk + sl], yd, acc);
+  if (S <= kCombineSplits) {
+    // ids, weights and every split partial of every slot in flight at once
+    // (indices clamped; values of invalid slots are loaded but not used)
+    int ev[Q4_MOE_MAX_TOPK];
+    float wv[Q4_MOE_MAX_TOPK], pv[Q4_MOE_MAX_TOPK][kCombineSplits];
+#pragma unroll
+    for (int sl = 0; sl < Q4_MOE_MAX_TOPK; ++sl) {
+      const int p = t * topk + min(sl, topk - 1);
+      ev[sl] = ids[p];
+      wv[sl] = w[p];
+#pragma unroll
+      for (int k = 0; k < kCombineSplits; ++k)
+        pv[sl][k] = part[(size_t)min(k, S - 1) * slab + (size_t)p * H + n];
+    }
+#pragma unroll
+    for (int sl = 0; sl < Q4_MOE_MAX_TOPK; ++sl) {
+      if (sl >= topk || ev[sl] < 0 || ev[sl] >= E) continue;
+      float yd = 0.0f;
+#pragma unroll
+      for (int k = 0; k < kCombineSplits; ++k)
+        if (k < S) yd += pv[sl][k];
+      acc = __builtin_fmaf(wv[sl], yd, acc);
+    }
+  } else {
+    for (int sl = 0; sl < topk; ++sl) {
+      const int e = ids[t * topk + sl];
+      if (e < 0 || e >= E) continue;
+      const size_t o = (size_t)(t * topk + sl) * H + n;
+      const float yd = sum_strided(part + o, slab, S);
+      acc = __builtin_fmaf(w[t * topk + sl], yd, acc);
+    }
   }
   out[idx] = acc;
 }
@@ -330,9 +389,12 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   ra.MC = p.MC;
   ra.items = items;
   ra.n_items = n_items;
-  hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (p.MC > 1) {  // single token: items are the pairs themselves
+    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
 
   const size_t mat_bytes = (size_t)p.H * (p.I / kBlockWeights) * kBlockBytes;
   // Wave-private staging needs 16-byte aligned row segments: pitches of a
@@ -358,13 +420,15 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   g.nmat = 2;
   g.npairs = npairs;
   g.x_row_div = p.topk;
+  g.ids = ids;
+  g.E = p.E;
   err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, staged_gu, st)
                     : launch_expert<kMaxChunk>(g, p.max_items, staged_gu, st);
   if (err != hipSuccess) return err;
 
   const size_t nh = (size_t)npairs * p.I;
   hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st,
-                     gu_part, ids, h, npairs, p.I, p.gu_S, p.E);
+                     gu_part, h, npairs, p.I, p.gu_S);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
 
