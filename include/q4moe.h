@@ -90,7 +90,7 @@ int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K
 
 /* ---------------------------------------------------------------------------
  * Prefill GEMM: Y[M x N] = X[M x K] . deq(B[K x N]) on the fp16 matrix cores.
- * The batched-prompt matmul of the same article (§5) and the quantized
+ * The batched-prompt matmul of the same article (§5.2) and the quantized
  * tensor-core GEMM that the KTransformers tutorial uses for prefill ("Optimization
  * 2", Marlin), as one fused kernel: B tiles are dequantized to fp16 in LDS and
  * contracted with fp32 accumulation.

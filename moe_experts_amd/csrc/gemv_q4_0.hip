@@ -84,12 +84,45 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
                         [&](int m, int o, float v) { dst[(size_t)m * a.N + n0 + o] = v; });
 }
 
+// y[i] = part[0][i] + part[1][i] + ... + part[S-1][i], in split order. With
+// SMAX > 0 (S <= SMAX) all SMAX loads are issued before the first add, so the
+// sum costs one memory round trip: split indices past S - 1 are clamped (the
+// repeated values are loaded but not added; adding +0.0 instead leaves the
+// sum bitwise unchanged, since a sum started at +0.0 is never -0.0). SMAX = 0
+// takes any S in groups of 8.
+template <int SMAX>
 __global__ __launch_bounds__(256) void gemv_q4_0_reduce_kernel(const float* __restrict__ part,
                                                                float* __restrict__ y, int MN,
                                                                int S) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= MN) return;
-  y[i] = sum_strided(part + i, (size_t)MN, S);
+  if constexpr (SMAX == 0) {
+    y[i] = sum_strided(part + i, (size_t)MN, S);
+  } else {
+    __builtin_assume(S >= 1);
+    float t[SMAX];
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) t[s] = part[(size_t)min(s, S - 1) * MN + i];
+    float v = 0.0f;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) v += s < S ? t[s] : 0.0f;
+    y[i] = v;
+  }
+}
+
+hipError_t launch_reduce(const float* part, float* y, int MN, int S, hipStream_t st) {
+  const dim3 grid((MN + 255) / 256), block(256);
+  if (S <= 8)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<8>, grid, block, 0, st, part, y, MN, S);
+  else if (S <= 16)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<16>, grid, block, 0, st, part, y, MN, S);
+  else if (S <= 32)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<32>, grid, block, 0, st, part, y, MN, S);
+  else if (S <= 64)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<64>, grid, block, 0, st, part, y, MN, S);
+  else
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<0>, grid, block, 0, st, part, y, MN, S);
+  return hipGetLastError();
 }
 
 template <int M, int LPB>
@@ -109,10 +142,7 @@ hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.S == 1) return err;
-  const int MN = M * a.N;
-  hipLaunchKernelGGL(gemv_q4_0_reduce_kernel, dim3((MN + 255) / 256), dim3(256), 0, st, a.part,
-                     a.y, MN, a.S);
-  return hipGetLastError();
+  return launch_reduce(a.part, a.y, M * a.N, a.S, st);
 }
 
 template <int M>

@@ -42,6 +42,22 @@ def test_gemv_staged_shapes_match_oracle(M, K, N):
     check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
 
 
+def test_gemv_every_split_count_range():
+    """The split-K sum is compiled for at most 8, 16, 32 and 64 splits and for
+    any count; a narrow matrix with a growing K walks through all five."""
+    from moe_experts_amd import q4_0_gemv_workspace_bytes
+    M, N = 2, 512
+    seen = set()
+    for K in (1024, 2048, 3000, 4096, 6000, 8192, 16384):
+        S = max(1, q4_0_gemv_workspace_bytes(M, N, K) // (4 * M * N))
+        seen.add(next(c for c in (8, 16, 32, 64, 1 << 30) if S <= c))
+        x = datagen.activations(K + 3, M, K)
+        B = datagen.q4_0_random(K + 4, K, N)
+        ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+        check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N} S={S}")
+    assert seen == {8, 16, 32, 64, 1 << 30}, seen
+
+
 def test_gemv_misaligned_matrix_takes_generic_path():
     """A matrix that is only 2-byte aligned cannot be staged in 16-byte
     chunks; the per-lane path must give the same bits as the staged one."""
