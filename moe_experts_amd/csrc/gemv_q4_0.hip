@@ -43,10 +43,14 @@ constexpr int rows_per_batch() {
   return M <= 2 ? 8 : (M <= 4 ? (LPB == 1 ? 6 : 8) : 4);
 }
 
-// Rows per lane in one batch of the staged path.
+// Rows per lane in one batch of the staged path, and weight buffers per wave.
 template <int M, int LPB>
 constexpr int staged_rows_per_batch() {
   return LPB == 1 ? 4 : 8;
+}
+template <int M, int LPB>
+constexpr int staged_buffers() {
+  return 2;
 }
 constexpr int kStagedJt = 16;
 
@@ -72,7 +76,8 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_kernel(GemvArgs a) {
   float acc[M][32 / LPB];
   float corr[M];
   if constexpr (STAGED)
-    tile_accumulate_staged<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt>(
+    tile_accumulate_staged<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt,
+                           staged_buffers<M, LPB>()>(
         g, a.x, (uint32_t)(4 * M * a.K), xoff, reinterpret_cast<uint8_t*>(smem), acc, corr);
   else
     tile_accumulate<M, LPB, rows_per_batch<M, LPB>()>(g, a.x, (uint32_t)(4 * M * a.K), xoff,
@@ -130,7 +135,8 @@ hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
   const int rf = 4 * phase_lds_floats<M, LPB>();
   int lds;
   if (staged) {
-    const int sb = staged_lds_bytes<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt>(a.Kt);
+    const int sb = staged_lds_bytes<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt,
+                                    staged_buffers<M, LPB>()>(a.Kt);
     lds = sb > rf ? sb : rf;
     hipLaunchKernelGGL((gemv_q4_0_kernel<M, LPB, true>), dim3(a.C * a.S), dim3(kThreads), lds, st,
                        a);

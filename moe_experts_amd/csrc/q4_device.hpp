@@ -366,13 +366,13 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
 // with LDS-DMA loads (buffer_load_dwordx4 ... lds): consecutive lanes fetch
 // consecutive 16-byte chunks of a segment, so every request is an aligned,
 // contiguous piece of a row and no registers hold the data in flight. Lanes
-// then read their block share (scale and nibbles) from LDS. Two buffers per
-// wave: batch b+1 streams in while batch b is computed. Producer and consumer
-// are the same wave, so a vmcnt wait (in issue order) is the only
-// synchronisation; a buffer is refilled only after the reads of its previous
-// batch have returned. Chunks of rows past the tile (and of batches past the
-// end) get an out-of-range offset: no memory access.
-// LDS layout: [activation tile][4 waves][2 buffers][stage_buf_bytes].
+// then read their block share (scale and nibbles) from LDS. NBUF buffers per
+// wave: batches b+1 .. b+NBUF-1 stream in while batch b is computed. Producer
+// and consumer are the same wave, so a vmcnt wait (in issue order) is the
+// only synchronisation; a buffer is refilled only after the reads of its
+// previous batch have returned. Chunks of rows past the tile (and of batches
+// past the end) get an out-of-range offset: no memory access.
+// LDS layout: [activation tile][4 waves][NBUF buffers][kBufBytes].
 // ---------------------------------------------------------------------------
 template <int LPB, int RB, int JT>
 struct StageShape {
@@ -388,11 +388,12 @@ struct StageShape {
   static_assert(kWaveSize % Lr == 0, "row phases must not straddle waves");
 };
 
-// LDS bytes of the staged tile: activation tile plus the weight buffers.
-template <int M, int LPB, int RB, int JT>
+// LDS bytes of the staged tile: activation tile plus NBUF weight buffers per
+// wave.
+template <int M, int LPB, int RB, int JT, int NBUF>
 __host__ __device__ constexpr int staged_lds_bytes(int rows) {
   return tile_x_floats<M>(rows, kThreads / (JT * LPB), RB) * 4 +
-         (kThreads / kWaveSize) * 2 * StageShape<LPB, RB, JT>::kBufBytes;
+         (kThreads / kWaveSize) * NBUF * StageShape<LPB, RB, JT>::kBufBytes;
 }
 
 // Read lane share `part` of the block at byte offset blk of a staged buffer.
@@ -415,7 +416,7 @@ __device__ __forceinline__ void read_block_part_lds(const uint8_t* __restrict__ 
   for (int k = 0; k < NW; ++k) bp.q[k] = __builtin_amdgcn_alignbyte(t[k + 1], t[k], sh);
 }
 
-template <int M, int LPB, int RB, int JT>
+template <int M, int LPB, int RB, int JT, int NBUF>
 __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
                                                        const float* __restrict__ x,
                                                        uint32_t x_bytes, const int (&xoff)[M],
@@ -424,7 +425,7 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
                                                        float (&corr)[M]) {
   using SS = StageShape<LPB, RB, JT>;
   constexpr uint32_t kOutOfRange = 0x80000000u;
-  static_assert(2 * SS::NI < 64, "vmcnt range");
+  static_assert(NBUF >= 2 && NBUF * SS::NI < 64, "vmcnt range");
   const int t = threadIdx.x;
   const int lane = t % kWaveSize;
   const int wave = t / kWaveSize;
@@ -443,7 +444,7 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
   const int nb = (nl + RB - 1) / RB;     // batches (uniform)
   const int rows_pad = nb * RB * P;
   float* xs = reinterpret_cast<float*>(lds);
-  uint8_t* wbuf = lds + tile_x_floats<M>(g.rows, P, RB) * 4 + wave * 2 * SS::kBufBytes;
+  uint8_t* wbuf = lds + tile_x_floats<M>(g.rows, P, RB) * 4 + wave * NBUF * SS::kBufBytes;
   const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B, (uint32_t)g.K * row_bytes);
 
@@ -461,7 +462,7 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
     voff[i] = (uint32_t)g.j0 * kBlockBytes + (uint32_t)trow[i] * row_bytes + (uint32_t)pc * 16u;
   }
   auto stage_batch = [&](int b) {
-    uint8_t* buf = wbuf + (b & 1) * SS::kBufBytes;
+    uint8_t* buf = wbuf + (b % NBUF) * SS::kBufBytes;
     const int brow = b * RB * P;
     const uint32_t soff = (uint32_t)(g.k0 + brow) * row_bytes;
 #pragma unroll
@@ -474,10 +475,10 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
 
   stage_x_tile<M>(x, x_bytes, xoff, g.k0, g.rows, rows_pad, xs);
   __builtin_amdgcn_sched_barrier(0);
-  stage_batch(0);
-  stage_batch(1);
+#pragma unroll
+  for (int b = 0; b < NBUF; ++b) stage_batch(b);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * SS::NI));  // activations landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF * SS::NI));  // activations landed
   zero_x_pad<M>(xs, g.rows, rows_pad);
   // Share the activation tile. A plain __syncthreads() would also wait for
   // the weight copies in flight (its release fence waits on every memory
@@ -492,9 +493,10 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
   const int seg0 = (lane / SS::Lr);  // row phase within the wave
   const int in_seg = jj * kBlockBytes;
   for (int b = 0; b < nb; ++b) {
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(SS::NI));  // batch b landed (b+1 in flight)
+    // batch b landed (b+1 .. b+NBUF-1 in flight)
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 1) * SS::NI));
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* buf = wbuf + (b & 1) * SS::kBufBytes;
+    const uint8_t* buf = wbuf + (b % NBUF) * SS::kBufBytes;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if (b * RB + i < nl) {  // uniform
@@ -508,7 +510,7 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
     // every read of this buffer has returned before it is refilled
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
-    stage_batch(b + 2);
+    stage_batch(b + NBUF);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the tile

@@ -42,7 +42,7 @@ def test_moe_duplicates_out_of_range_and_crowded_expert():
     Wg, Wu, Wd = small_experts(7, H, I, E)
     g = np.random.Generator(np.random.PCG64(3))
     ids = g.integers(0, E, size=(T, topk)).astype(np.int32)
-    ids[:, 0] = 2                    # every token uses expert 2: 20 pairs -> chunks of 8, 8, 4
+    ids[:, 0] = 2                    # every token uses expert 2: 20 pairs -> 10 work items
     ids[0, 1] = ids[0, 2] = 5        # a duplicate within a token
     ids[1, 3] = E + 3                # out of range -> contributes nothing
     ids[2, 2] = -1
