@@ -9,14 +9,19 @@
 // 32 along N within a row), so a column's K values sit in different rows and
 // the B operand is dequantized into LDS transposed ([n][k]).
 //
-// gemm_q4_0_kernel (K % 64 == 0, N % 256 == 0, X and B 16-byte aligned):
-//   * workgroup tile 128 x 256 and 512 lanes: 4 consumer waves in a 2 x 2
-//     grid, each 64 x 128 (eight 32 x 32 accumulators), only issue MFMAs; 4
+// gemm_q4_0_kernel (K % 64 == 0, N % 128 == 0, X 16-byte and B 4-byte aligned):
+//   * workgroup tile 256 x 128 and 512 lanes: 4 consumer waves, each 64 rows
+//     x all 128 columns (eight 32 x 32 accumulators), only issue MFMAs; 4
 //     producer waves issue the copies and dequantize, so the VALU work runs
-//     beside the MFMAs on each SIMD; K steps of 64;
-//   * X tiles and raw Q4_0 row segments (8 blocks = 144 aligned bytes per
-//     row) are copied global -> LDS by LDS-DMA loads (no registers), X three
-//     and B four steps deep, issued two and three steps ahead;
+//     beside the MFMAs on each SIMD; K steps of 64. The dequantization per
+//     step scales with the tile's columns and the MFMA work with its area,
+//     so the tall tile halves the dequant per MFMA of a 128 x 256 tile at
+//     the same LDS traffic and grid size (measured: the dequant, not the
+//     MFMAs, set the pace of the 128 x 256 tile);
+//   * X tiles (16-byte chunks) and raw Q4_0 row segments (4 blocks = 72
+//     bytes per row, in dwords) are copied global -> LDS by LDS-DMA loads (no
+//     registers), X three and B four steps deep, issued two and three steps
+//     ahead;
 //   * each step the lanes dequantize the next step's raw B into an fp16 tile
 //     [n][k]: w = fp16((q - 8) * d) with packed half arithmetic, one rounding;
 //   * both LDS tiles are XOR-swizzled in 16-byte chunks, so the MFMA operand
@@ -206,17 +211,20 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_generic_kernel(GemmArg
 // Aligned-shape kernel
 // ---------------------------------------------------------------------------
 namespace fast {
-constexpr int BM = 128, BN = 256, BK = 64;
+constexpr int BM = 256, BN = 128, BK = 64;
 constexpr int kXStages = 3, kRStages = 4;
-constexpr int kXChunks = BM * BK / 8;                     // 16-byte chunks per X stage: 1024
-constexpr int kXBytes = kXChunks * 16;                    // 16 KiB
-constexpr int kRowChunks = (BN / kBlockWeights) * kBlockBytes / 16;  // 9 per raw row
-constexpr int kRChunks = BK * kRowChunks;                 // 576
-constexpr int kRInstr = (kRChunks + kGemmThreads - 1) / kGemmThreads;  // 3
-constexpr int kRBytes = kRInstr * kGemmThreads * 16;      // 12 KiB
-constexpr int kBBytes = BN * BK * 2;                      // 32 KiB fp16 tile
-constexpr int kXInstr = kXChunks / kGemmThreads;          // 4
+constexpr int kXChunks = BM * BK / 8;                     // 16-byte chunks per X stage: 2048
+constexpr int kXBytes = kXChunks * 16;                    // 32 KiB
+constexpr int kRowBytes = (BN / kBlockWeights) * kBlockBytes;  // 72 bytes of raw row segment
+constexpr int kRowWords = kRowBytes / 4;                  // 18 dwords (copied 4 bytes at a time)
+constexpr int kRWords = BK * kRowWords;                   // 1152
+constexpr int kRInstr = (kRWords + kGemmThreads - 1) / kGemmThreads;  // 5
+constexpr int kRBytes = kRInstr * kGemmThreads * 4;       // 5 KiB
+constexpr int kBBytes = BN * BK * 2;                      // 16 KiB fp16 tile
+constexpr int kXInstr = kXChunks / kGemmThreads;          // 8
 constexpr int kGroup = kXInstr + kRInstr;                 // copies issued per step
+constexpr int kUnits = BN * BK / 16;                      // dequant units (2 rows x 8 columns)
+constexpr int kUL = kUnits / kGemmThreads;                // 2 per producer lane
 constexpr int kLdsBytes = kXStages * kXBytes + kRStages * kRBytes + 2 * kBBytes;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 
@@ -244,7 +252,7 @@ __device__ __forceinline__ uint8_t* bstage(uint8_t* lds, int s) {
 // lanes at a time: with rows of 32 banks, lanes on consecutive rows hit
 // disjoint banks when the even rows and the odd rows each take 8 different
 // positions, which (r >> 1) & 7 gives. The B tile adds r >> 5 (the block
-// column), which spreads the dequant stores of one instruction (8 blocks of
+// column), which spreads the dequant stores of one instruction (4 blocks of
 // the same column offset) over the banks too.
 __device__ __forceinline__ int swz_x(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int swz_b(int n) { return ((n >> 1) ^ (n >> 5)) & 7; }
@@ -255,14 +263,15 @@ __device__ __forceinline__ uint32_t bpos(int n, int kp) {
          (uint32_t)((kp & 3) << 2);
 }
 
-// Dequantization units: unit u = t + 256*i (4 per producer lane) covers row pair
+// Dequantization units: unit u = t + 256*i (2 per producer lane) covers row pair
 // kp (rows 2kp, 2kp+1), block jb and quarter qq (8 columns), with bits
-// u[0:2] = kp % 8, u[3:5] = jb, u[6:7] = kp / 8, u[8:9] = qq: the 64 lanes of
-// a wave span 8 row pairs x 8 blocks, so the raw reads (rows 288 bytes apart,
-// blocks 18 bytes apart) and the tile stores spread over the LDS banks.
-__device__ __forceinline__ int unit_kp(int u) { return (u & 7) | (((u >> 6) & 3) << 3); }
-__device__ __forceinline__ int unit_jb(int u) { return (u >> 3) & 7; }
-__device__ __forceinline__ int unit_qq(int u) { return (u >> 8) & 3; }
+// u[0:2] = kp % 8, u[3:4] = jb, u[5:6] = qq, u[7:8] = kp / 8: the 64 lanes of
+// a wave span 8 row pairs x 4 blocks x 2 quarters, so the raw reads (rows 72
+// bytes apart, blocks 18 bytes apart) and the tile stores spread over the LDS
+// banks.
+__device__ __forceinline__ int unit_kp(int u) { return (u & 7) | (((u >> 7) & 3) << 3); }
+__device__ __forceinline__ int unit_jb(int u) { return (u >> 3) & 3; }
+__device__ __forceinline__ int unit_qq(int u) { return (u >> 5) & 3; }
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
@@ -280,8 +289,8 @@ struct Producer {
   uint32_t xoff[kXInstr], roff[kRInstr];
   uint32_t wslot;                 // wave's first DMA slot byte offset (uniform)
   uint32_t x_step, r_step;        // bytes per K step in X and B (uniform)
-  uint32_t rd[4], rw[4], sh[4];
-  uint32_t st[4][4];
+  uint32_t rd[kUL], rw[kUL], sh[kUL];
+  uint32_t st[kUL][4];
   int nk;
 
   __device__ __forceinline__ void init(const Args& g, int m0, int j0, int t) {
@@ -306,19 +315,19 @@ struct Producer {
     }
 #pragma unroll
     for (int i = 0; i < kRInstr; ++i) {
-      const int q = i * kGemmThreads + t;  // raw row q / 9, piece q % 9
-      const int row = q / kRowChunks;
-      const int pc = q - row * kRowChunks;
-      roff[i] = q < kRChunks
-                    ? (uint32_t)row * row_bytes + (uint32_t)j0 * kBlockBytes + 16u * pc
+      const int q = i * kGemmThreads + t;  // raw row q / 18, dword q % 18
+      const int row = q / kRowWords;
+      const int pc = q - row * kRowWords;
+      roff[i] = q < kRWords
+                    ? (uint32_t)row * row_bytes + (uint32_t)j0 * kBlockBytes + 4u * pc
                     : kOut;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kUL; ++i) {
       const int u = t + i * kGemmThreads;
       const int kp = unit_kp(u), jb = unit_jb(u), qq = unit_qq(u);
-      rd[i] = (uint32_t)(2 * kp) * (kRowChunks * 16) + jb * kBlockBytes;
-      const uint32_t o = rd[i] + 2 + 4 * qq;  // 2-byte aligned; row 2kp+1 is 144 bytes on
+      rd[i] = (uint32_t)(2 * kp) * kRowBytes + jb * kBlockBytes;
+      const uint32_t o = rd[i] + 2 + 4 * qq;  // 2-byte aligned; row 2kp+1 is 72 bytes on
       sh[i] = o & 3u;
       rw[i] = o - sh[i];
       const int nb = jb * 32 + qq * 8;
@@ -345,10 +354,10 @@ struct Producer {
     constexpr uint32_t kOut = 0x80000000u;
     const bool valid = ks < nk;
     const uint32_t so = valid ? (uint32_t)ks * r_step : 0u;
-    uint8_t* dst = rstage(lds, ks % kRStages) + wslot;
+    uint8_t* dst = rstage(lds, ks % kRStages) + wslot / 4;
 #pragma unroll
     for (int i = 0; i < kRInstr; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + i * kGemmThreads * 16), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + i * kGemmThreads * 4), 4,
                                                valid ? roff[i] : kOut, so, 0, 0);
   }
 
@@ -356,22 +365,22 @@ struct Producer {
   __device__ __forceinline__ void dequant(const uint8_t* __restrict__ rsb,
                                           uint8_t* __restrict__ bsb) const {
     const half2v off = {(_Float16)1032.0f, (_Float16)1032.0f};
-    uint32_t d0[4], d1[4], q0[4], q1[4];
+    uint32_t d0[kUL], d1[kUL], q0[kUL], q1[kUL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kUL; ++i) {
       const uint8_t* pd = rsb + rd[i];
       const uint8_t* pw = rsb + rw[i];
       d0[i] = *reinterpret_cast<const uint16_t*>(pd);
-      d1[i] = *reinterpret_cast<const uint16_t*>(pd + kRowChunks * 16);
+      d1[i] = *reinterpret_cast<const uint16_t*>(pd + kRowBytes);
       const uint32_t a0 = *reinterpret_cast<const uint32_t*>(pw);
       const uint32_t a1 = *reinterpret_cast<const uint32_t*>(pw + 4);
-      const uint32_t b0 = *reinterpret_cast<const uint32_t*>(pw + kRowChunks * 16);
-      const uint32_t b1 = *reinterpret_cast<const uint32_t*>(pw + kRowChunks * 16 + 4);
+      const uint32_t b0 = *reinterpret_cast<const uint32_t*>(pw + kRowBytes);
+      const uint32_t b1 = *reinterpret_cast<const uint32_t*>(pw + kRowBytes + 4);
       q0[i] = __builtin_amdgcn_alignbyte(a1, a0, sh[i]);
       q1[i] = __builtin_amdgcn_alignbyte(b1, b0, sh[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kUL; ++i) {
       const half2v d2 = __builtin_bit_cast(half2v, d0[i] | (d1[i] << 16));
 #pragma unroll
       for (int by = 0; by < 4; ++by) {
@@ -439,7 +448,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 
   // -------------------------------------------------------------- consumer
   const int lane = threadIdx.x & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave;  // rows wm*64 .. +64, all 128 columns
   float16v acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -463,7 +472,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int n = wn * 128 + j * 32 + (lane & 31);
+        const int n = j * 32 + (lane & 31);
         bf[j] = *reinterpret_cast<const half8*>(bs + n * (BK * 2) + ((kc ^ swz_b(n)) << 4));
       }
 #pragma unroll
@@ -482,7 +491,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int col = j0 * kBlockWeights + wn * 128 + j * 32 + (lane & 31);
+      const int col = j0 * kBlockWeights + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -505,8 +514,10 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
   g.K = K;
   g.NB = N / kBlockWeights;
   g.tiles_n = (N + BN - 1) / BN;
-  const bool aligned16 = ((reinterpret_cast<uintptr_t>(X) | reinterpret_cast<uintptr_t>(B)) & 15) == 0;
-  if (K % fast::BK == 0 && N % fast::BN == 0 && aligned16) {
+  // X rows are copied in 16-byte chunks, raw B rows in dwords
+  const bool aligned = (reinterpret_cast<uintptr_t>(X) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(B) & 3) == 0;
+  if (K % fast::BK == 0 && N % fast::BN == 0 && aligned) {
     fast::Args f;
     f.X = X;
     f.B = B;
