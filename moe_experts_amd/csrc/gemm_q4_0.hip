@@ -217,7 +217,8 @@ constexpr int kXChunks = BM * BK / 8;                     // 16-byte chunks per 
 constexpr int kXBytes = kXChunks * 16;                    // 32 KiB
 constexpr int kRowBytes = (BN / kBlockWeights) * kBlockBytes;  // 72 bytes of raw row segment
 constexpr int kRowWords = kRowBytes / 4;                  // 18 dwords (copied 4 bytes at a time)
-constexpr int kRWords = BK * kRowWords;                   // 1152
+constexpr int kRowPitch = kRowBytes + 4;                  // LDS row pitch: one pad dword
+constexpr int kRWords = BK * (kRowWords + 1);             // 1216 dword slots, pads included
 constexpr int kRInstr = (kRWords + kGemmThreads - 1) / kGemmThreads;  // 5
 constexpr int kRBytes = kRInstr * kGemmThreads * 4;       // 5 KiB
 constexpr int kBBytes = BN * BK * 2;                      // 16 KiB fp16 tile
@@ -265,13 +266,14 @@ __device__ __forceinline__ uint32_t bpos(int n, int kp) {
 
 // Dequantization units: unit u = t + 256*i (2 per producer lane) covers row pair
 // kp (rows 2kp, 2kp+1), block jb and quarter qq (8 columns), with bits
-// u[0:2] = kp % 8, u[3:4] = jb, u[5:6] = qq, u[7:8] = kp / 8: the 64 lanes of
-// a wave span 8 row pairs x 4 blocks x 2 quarters, so the raw reads (rows 72
-// bytes apart, blocks 18 bytes apart) and the tile stores spread over the LDS
-// banks.
-__device__ __forceinline__ int unit_kp(int u) { return (u & 7) | (((u >> 7) & 3) << 3); }
-__device__ __forceinline__ int unit_jb(int u) { return (u >> 3) & 3; }
-__device__ __forceinline__ int unit_qq(int u) { return (u >> 5) & 3; }
+// u[0:3] = kp % 16, u[4] = qq % 2, u[5] = kp / 16, u[6:7] = jb, u[8] = qq / 2:
+// the 64 lanes of a wave span 32 row pairs x 2 quarters of one block. With
+// raw rows 76 bytes apart in LDS (a pad dword per row) this spreads the raw
+// reads and the tile stores over the LDS banks (chosen by a search over bit
+// assignments with a bank model of both operations).
+__device__ __forceinline__ int unit_kp(int u) { return (u & 15) | (((u >> 5) & 1) << 4); }
+__device__ __forceinline__ int unit_jb(int u) { return (u >> 6) & 3; }
+__device__ __forceinline__ int unit_qq(int u) { return ((u >> 4) & 1) | (((u >> 8) & 1) << 1); }
 
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
@@ -315,10 +317,10 @@ struct Producer {
     }
 #pragma unroll
     for (int i = 0; i < kRInstr; ++i) {
-      const int q = i * kGemmThreads + t;  // raw row q / 18, dword q % 18
-      const int row = q / kRowWords;
-      const int pc = q - row * kRowWords;
-      roff[i] = q < kRWords
+      const int q = i * kGemmThreads + t;  // LDS slot: raw row q / 19, dword q % 19
+      const int row = q / (kRowWords + 1);
+      const int pc = q - row * (kRowWords + 1);
+      roff[i] = (q < kRWords && pc < kRowWords)
                     ? (uint32_t)row * row_bytes + (uint32_t)j0 * kBlockBytes + 4u * pc
                     : kOut;
     }
@@ -326,8 +328,8 @@ struct Producer {
     for (int i = 0; i < kUL; ++i) {
       const int u = t + i * kGemmThreads;
       const int kp = unit_kp(u), jb = unit_jb(u), qq = unit_qq(u);
-      rd[i] = (uint32_t)(2 * kp) * kRowBytes + jb * kBlockBytes;
-      const uint32_t o = rd[i] + 2 + 4 * qq;  // 2-byte aligned; row 2kp+1 is 72 bytes on
+      rd[i] = (uint32_t)(2 * kp) * kRowPitch + jb * kBlockBytes;
+      const uint32_t o = rd[i] + 2 + 4 * qq;  // 2-byte aligned; row 2kp+1 is 76 bytes on
       sh[i] = o & 3u;
       rw[i] = o - sh[i];
       const int nb = jb * 32 + qq * 8;
@@ -371,11 +373,11 @@ struct Producer {
       const uint8_t* pd = rsb + rd[i];
       const uint8_t* pw = rsb + rw[i];
       d0[i] = *reinterpret_cast<const uint16_t*>(pd);
-      d1[i] = *reinterpret_cast<const uint16_t*>(pd + kRowBytes);
+      d1[i] = *reinterpret_cast<const uint16_t*>(pd + kRowPitch);
       const uint32_t a0 = *reinterpret_cast<const uint32_t*>(pw);
       const uint32_t a1 = *reinterpret_cast<const uint32_t*>(pw + 4);
-      const uint32_t b0 = *reinterpret_cast<const uint32_t*>(pw + kRowBytes);
-      const uint32_t b1 = *reinterpret_cast<const uint32_t*>(pw + kRowBytes + 4);
+      const uint32_t b0 = *reinterpret_cast<const uint32_t*>(pw + kRowPitch);
+      const uint32_t b1 = *reinterpret_cast<const uint32_t*>(pw + kRowPitch + 4);
       q0[i] = __builtin_amdgcn_alignbyte(a1, a0, sh[i]);
       q1[i] = __builtin_amdgcn_alignbyte(b1, b0, sh[i]);
     }
