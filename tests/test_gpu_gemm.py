@@ -24,11 +24,14 @@ def test_gemm_small_match_oracle(M, K, N):
     check_tol(gemm(X16, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
 
 
-# K % 64 == 0, N % 256 == 0 and 16-byte aligned operands take the pipelined
-# kernel (128 x 256 tiles, K steps of 64): a single step and row, ragged M
-# tails. The K values that are not multiples of 64 take the other kernel.
+# K % 64 == 0, N % 128 == 0, a 16-byte aligned X and a 4-byte aligned matrix
+# take the pipelined kernel (256 x 128 tiles, K steps of 64): a single step
+# and row, ragged M tails (one row past a tile, a tile and a bit), a single
+# column tile and odd tile counts. The K values that are not multiples of 64
+# take the other kernel.
 ALIGNED = [(1, 64, 256), (130, 128, 512), (129, 1024, 768), (300, 192, 256), (2, 4096, 1024),
-           (128, 64, 256), (130, 72, 512), (129, 1000, 768)]
+           (128, 64, 256), (130, 72, 512), (129, 1000, 768), (1, 64, 128), (257, 192, 384),
+           (70, 4096, 640), (513, 128, 128)]
 
 
 @pytest.mark.parametrize("M,K,N", ALIGNED)
