@@ -150,9 +150,12 @@ struct ExpertArgs {
   int x_row_div;                      // activation row = pair / x_row_div, times K
   const int32_t* __restrict__ ids;    // [npairs] expert ids (single-token items)
   int E;
+  ActSource act;                      // single-token down: activations from gate/up partials
+                                      // (part null: copy x)
 };
 
-template <int M, bool STAGED>
+// ACT: the tile may form its activations from gate/up partials (a.act).
+template <int M, bool STAGED, bool ACT>
 __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int c, int s,
                             float* smem) {
   constexpr int Lr = kJt * kLPB;
@@ -172,8 +175,9 @@ __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int
   float acc[M][32 / kLPB];
   float corr[M];
   if constexpr (STAGED)
-    tile_accumulate_staged<M, kLPB, kStagedRB, kJt, kStagedBufs>(g, a.x, a.x_bytes, xoff,
-                                                    reinterpret_cast<uint8_t*>(smem), acc, corr);
+    tile_accumulate_staged<M, kLPB, kStagedRB, kJt, kStagedBufs>(
+        g, a.x, a.x_bytes, xoff, reinterpret_cast<uint8_t*>(smem), acc, corr,
+        ACT ? a.act : ActSource{nullptr, 0, 0, 0});
   else
     tile_accumulate<M, kLPB, moe_rows_per_batch<M>()>(g, a.x, a.x_bytes, xoff, smem, acc, corr);
   const int n0 = g.j0 * kBlockWeights;
@@ -213,10 +217,10 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
   const int mat = rest % a.nmat;
   const int s = rest / a.nmat;
   if (it.cnt == 1) {
-    expert_tile<1, STAGED>(a, it, mat, c, s, smem);
+    expert_tile<1, STAGED, MC == 1>(a, it, mat, c, s, smem);
   } else if constexpr (MC > 1) {
     static_assert(MC == 2, "work items hold at most 2 pairs");
-    if (it.cnt == 2) expert_tile<2, STAGED>(a, it, mat, c, s, smem);
+    if (it.cnt == 2) expert_tile<2, STAGED, false>(a, it, mat, c, s, smem);
   }
 }
 
@@ -421,15 +425,24 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   g.x_row_div = p.topk;
   g.ids = ids;
   g.E = p.E;
+  g.act = ActSource{nullptr, 0, 0, 0};
   err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, staged_gu, st)
                     : launch_expert<kMaxChunk>(g, p.max_items, staged_gu, st);
   if (err != hipSuccess) return err;
 
   const size_t nh = (size_t)npairs * p.I;
-  hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st,
-                     gu_part, h, npairs, p.I, p.gu_S);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  // A single token's down tiles form h = SiLU(gate) * up themselves from the
+  // gate/up partial sums while staging their activation tile (same sums, same
+  // order, same expression as moe_act_kernel), which saves a kernel launch.
+  constexpr int kP = kThreads / (kJt * kLPB);
+  const bool fuse_act = p.MC == 1 && staged_dn && p.gu_S <= kActMaxSplits &&
+                        tile_rows_padded(p.dn_Kt, kP, kStagedRB) <= kActMaxVals * kThreads;
+  if (!fuse_act) {
+    hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st,
+                       gu_part, h, npairs, p.I, p.gu_S);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
 
   ExpertArgs d = g;
   d.x = h;
@@ -445,6 +458,9 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   d.S = p.dn_S;
   d.nmat = 1;
   d.x_row_div = 1;
+  if (fuse_act)
+    d.act = ActSource{gu_part, (uint32_t)(2 * (size_t)p.gu_S * nh * sizeof(float)), (uint32_t)nh,
+                      p.gu_S};
   err = (p.MC == 1) ? launch_expert<1>(d, p.max_items, staged_dn, st)
                     : launch_expert<kMaxChunk>(d, p.max_items, staged_dn, st);
   if (err != hipSuccess) return err;

@@ -416,13 +416,29 @@ __device__ __forceinline__ void read_block_part_lds(const uint8_t* __restrict__ 
   for (int k = 0; k < NW; ++k) bp.q[k] = __builtin_amdgcn_alignbyte(t[k + 1], t[k], sh);
 }
 
+// Activations computed from split-K partial sums of a gate and an up
+// projection instead of copied: x[i] = SiLU(g) * u with g = sum over s of
+// part[s][i] and u = sum over s of part[S + s][i], each in split order from
+// +0.0 (part: [2][S][slab] floats; x index i = xoff[m] + k0 + row as for a
+// copied tile). At most kActMaxSplits splits and kActMaxVals tile words per
+// lane (XW * rows_pad <= kActMaxVals * 256).
+struct ActSource {
+  const float* part;
+  uint32_t part_bytes;
+  uint32_t slab;
+  int S;
+};
+constexpr int kActMaxSplits = 16;
+constexpr int kActMaxVals = 2;
+
 template <int M, int LPB, int RB, int JT, int NBUF>
 __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
                                                        const float* __restrict__ x,
                                                        uint32_t x_bytes, const int (&xoff)[M],
                                                        uint8_t* __restrict__ lds,
                                                        float (&acc)[M][32 / LPB],
-                                                       float (&corr)[M]) {
+                                                       float (&corr)[M],
+                                                       ActSource act = ActSource{nullptr, 0, 0, 0}) {
   using SS = StageShape<LPB, RB, JT>;
   constexpr uint32_t kOutOfRange = 0x80000000u;
   static_assert(NBUF >= 2 && NBUF * SS::NI < 64, "vmcnt range");
@@ -473,13 +489,63 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
     }
   };
 
-  stage_x_tile<M>(x, x_bytes, xoff, g.k0, g.rows, rows_pad, xs);
-  __builtin_amdgcn_sched_barrier(0);
+  if (act.part != nullptr) {
+    // Every partial-sum load is issued before the weight copies (so the
+    // compiler's wait for them does not include the copies), then the
+    // activations are formed and stored.
+    constexpr int XW = xs_width<M>();
+    constexpr uint32_t kOut = 0x80000000u;
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(act.part, act.part_bytes);
+    float pv[kActMaxVals][2][kActMaxSplits];
 #pragma unroll
-  for (int b = 0; b < NBUF; ++b) stage_batch(b);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF * SS::NI));  // activations landed
-  zero_x_pad<M>(xs, g.rows, rows_pad);
+    for (int v = 0; v < kActMaxVals; ++v) {
+      const int q = v * kThreads + t;
+      const int row = q / XW;
+      const int m = q - row * XW;
+      int xo = 0;
+#pragma unroll
+      for (int mm = 0; mm < M; ++mm)
+        if (mm == m) xo = xoff[mm];
+      const bool valid = m < M && row < g.rows;
+      const uint32_t base = (uint32_t)(xo + g.k0 + row);
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int sp = 0; sp < kActMaxSplits; ++sp) {
+          const uint32_t o = (valid && sp < act.S)
+                                 ? ((uint32_t)(h * act.S + sp) * act.slab + base) * 4u
+                                 : kOut;
+          pv[v][h][sp] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, o, 0, 0));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) stage_batch(b);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < kActMaxVals; ++v) {
+      const int q = v * kThreads + t;
+      if (q < XW * rows_pad) {
+        float gs = 0.0f, us = 0.0f;  // out-of-range splits load +0.0: the sums are unchanged
+#pragma unroll
+        for (int sp = 0; sp < kActMaxSplits; ++sp) {
+          gs += pv[v][0][sp];
+          us += pv[v][1][sp];
+        }
+        const int row = q / XW;
+        const int m = q - row * XW;
+        xs[q] = (m < M && row < g.rows) ? gs / (1.0f + expf(-gs)) * us : 0.0f;
+      }
+    }
+  } else {
+    stage_x_tile<M>(x, x_bytes, xoff, g.k0, g.rows, rows_pad, xs);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) stage_batch(b);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(NBUF * SS::NI));  // activations landed
+    zero_x_pad<M>(xs, g.rows, rows_pad);
+  }
   // Share the activation tile. A plain __syncthreads() would also wait for
   // the weight copies in flight (its release fence waits on every memory
   // operation); the tile's own copies have landed (vmcnt above), so only the
