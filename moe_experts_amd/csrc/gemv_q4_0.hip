@@ -153,32 +153,34 @@ hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
 
 template <int M>
 hipError_t launch_m(const GemvArgs& a, int lpb, bool staged, hipStream_t st) {
-  if constexpr (M <= 4) {
-    if (lpb == 1) return launch_one<M, 1>(a, staged, st);
+  if constexpr (M == 1) {
+    if (lpb == 1) return launch_one<1, 1>(a, staged, st);
   }
   return launch_one<M, 2>(a, staged, st);
 }
 
 }  // namespace
 
-// Tile plan: 16-block column tiles; whole blocks per lane for M <= 4, half
-// blocks for M > 4 (register budget). The K split S sets the grid size C*S.
-// Measured on MI355X over the dense 7B shapes, the best grid is at most one
-// full round of resident workgroups: up to 512 (two per CU) for M >= 4, where
-// the VALU sets the pace and every SIMD needs two waves, and up to 352 for
-// M <= 3, where more splits only add partial-sum traffic; a grid just past a
-// round costs a whole second round. Tiles keep at least 128 rows (8 or 16 per
-// lane), or their fixed cost dominates. S is the largest split within both.
+// Tile plan: 16-block column tiles; whole blocks per lane for a single row,
+// half blocks for M >= 2 (half the accumulator registers, so more waves per
+// SIMD: measured 4-10 % faster than whole blocks at M = 2..4). The K split S
+// sets the grid size C*S. Measured on MI355X over the dense 7B shapes, the
+// best grid is at most one full round of resident workgroups: up to 512 (two
+// per CU) for M >= 2, where the VALU sets the pace and every SIMD needs two
+// waves, and up to 352 for M = 1, where more splits only add partial-sum
+// traffic; a grid just past a round costs a whole second round. Tiles keep at
+// least 128 rows (8 or 16 per lane), or their fixed cost dominates. S is the
+// largest split within both.
 GemvPlan plan_gemv(int M, int N, int K) {
   GemvPlan p{};
   constexpr int kMinTileRows = 128;
   const int NB = N / kBlockWeights;
-  p.LPB = (M <= 4) ? 1 : 2;
+  p.LPB = (M == 1) ? 1 : 2;
   p.Jt = NB < 16 ? NB : 16;
   p.Lr = p.Jt * p.LPB;
   p.P = kThreads / p.Lr;
   p.C = (NB + p.Jt - 1) / p.Jt;
-  const int target = M >= 4 ? 512 : 352;
+  const int target = M >= 2 ? 512 : 352;
   int best_kt = ((K + p.P - 1) / p.P) * p.P;  // S = 1
   int last_S = -1;
   for (int s = 2; s <= K; ++s) {
