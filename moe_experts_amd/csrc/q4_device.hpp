@@ -582,126 +582,11 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the tile
 }
 
-// Rows reduced per pass of the 16-block tile reduction, and its LDS floats:
-// per wave and row, 512 column sums and 16 block corrections.
-template <int M>
-constexpr int wave_reduce_rows() {
-  return M < 4 ? M : 4;
-}
-template <int M>
-constexpr int wave_reduce_lds_floats() {
-  return 4 * wave_reduce_rows<M>() * (512 + 16);
-}
-
-// LDS floats needed by reduce_phases (either of its two ways).
+// LDS floats needed by reduce_phases: one activation row's accumulators,
+// the raw corrections of all rows and their phase sums.
 template <int M, int LPB>
 constexpr int phase_lds_floats() {
-  constexpr int generic = (32 / LPB) * (256 + 1) + M * (256 + 1) + M * 256;
-  constexpr int wave = wave_reduce_lds_floats<M>();
-  return generic > wave ? generic : wave;
-}
-
-// Sum of the two halves of a wave (lanes l and l + 32) or of row pairs
-// (lanes l and l + 16 in each half), two registers at a time, with the
-// gfx950 lane-swap instructions. With x = [x0 | x1] and y = [y0 | y1] (halves,
-// or rows 0/2 and 1/3 for the 16-lane form), the result is [x0 + x1 | y0 + y1]:
-// the lanes of the first half (rows) end up holding x's sum and the others
-// y's. Passing x = y sums one register into both halves.
-// (The two results are copied to named words before the bit casts: casting
-// the subscripted builtin result directly made the front end read word 0
-// twice.)
-__device__ __forceinline__ float swap_add32(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, y), false, false);
-  const uint32_t a = r[0], b = r[1];
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-__device__ __forceinline__ float swap_add16(float x, float y) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, x),
-                                                  __builtin_bit_cast(uint32_t, y), false, false);
-  const uint32_t a = r[0], b = r[1];
-  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-
-// Phase reduction of a 16-block tile (Lr = 16 * LPB lanes per phase, LPB 1
-// or 2, so a wave holds 64 / Lr whole phases). First the phases inside each
-// wave are summed with lane swaps, pairing accumulator registers so that each
-// lane ends up with 8 consecutive columns of every row m: for LPB = 2 lane
-// (h, v) (h = lane / 32) holds columns 16v + 8h + 0..7, for LPB = 1 lane
-// (r, v) (r = lane / 16) holds columns 32v + 8r + 0..7. The corrections go
-// through the same additions. Then the 4 waves' sums meet in LDS, at most 4
-// rows at a time, and each thread adds them in wave order for columns 2t and
-// 2t + 1 and finishes them as reduce_phases does. Every output's sum runs the
-// same tree for acc and for 8 * corr, whatever M is, so all-8 nibbles still
-// give exactly zero and a row's results do not depend on the other rows.
-template <int M, int LPB, class Store>
-__device__ __forceinline__ void reduce_tile16(const float (&acc)[M][32 / LPB],
-                                              const float (&corr)[M], float* smem, int ncols,
-                                              Store store) {
-  static_assert(LPB == 1 || LPB == 2, "16-block tiles with whole or half blocks per lane");
-  constexpr int MR = wave_reduce_rows<M>();
-  const int t = threadIdx.x;
-  const int lane = t & (kWaveSize - 1);
-  const int wave = t / kWaveSize;
-  float red[M][8];
-  float cs[M];
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if constexpr (LPB == 2) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) red[m][c] = swap_add32(acc[m][c], acc[m][c + 8]);
-      cs[m] = swap_add32(corr[m], corr[m]);
-    } else {
-      float h[16];
-#pragma unroll
-      for (int c = 0; c < 16; ++c) h[c] = swap_add32(acc[m][c], acc[m][c + 16]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) red[m][c] = swap_add16(h[c], h[c + 8]);
-      cs[m] = swap_add16(swap_add32(corr[m], corr[m]), swap_add32(corr[m], corr[m]));
-    }
-  }
-  // this lane's first column and its block (the corrections are the same in
-  // every lane of a block, so one lane per block writes them)
-  const int o0 = (LPB == 2) ? 16 * (lane & 31) + 8 * (lane >> 5) : 32 * (lane & 15) + 8 * (lane >> 4);
-  const bool cwriter = (LPB == 2) ? (lane < 32 && (lane & 1) == 0) : (lane < 16);
-  const int cblock = (LPB == 2) ? ((lane & 31) >> 1) : (lane & 15);
-  float* S = smem;                    // [4 waves][MR][512]
-  float* C = smem + 4 * MR * 512;     // [4 waves][MR][16]
-  __syncthreads();
-#pragma unroll
-  for (int m0 = 0; m0 < M; m0 += MR) {
-#pragma unroll
-    for (int mi = 0; mi < MR; ++mi) {
-      if (m0 + mi < M) {
-        float* dst = S + (wave * MR + mi) * 512 + o0;
-        *reinterpret_cast<float4*>(dst) =
-            make_float4(red[m0 + mi][0], red[m0 + mi][1], red[m0 + mi][2], red[m0 + mi][3]);
-        *reinterpret_cast<float4*>(dst + 4) =
-            make_float4(red[m0 + mi][4], red[m0 + mi][5], red[m0 + mi][6], red[m0 + mi][7]);
-        if (cwriter) C[(wave * MR + mi) * 16 + cblock] = cs[m0 + mi];
-      }
-    }
-    __syncthreads();
-    const int o = 2 * t;
-#pragma unroll
-    for (int mi = 0; mi < MR; ++mi) {
-      if (m0 + mi < M) {
-        float2 sum = *reinterpret_cast<const float2*>(S + mi * 512 + o);
-        float csum = C[mi * 16 + (o >> 5)];
-#pragma unroll
-        for (int w = 1; w < 4; ++w) {
-          const float2 v = *reinterpret_cast<const float2*>(S + (w * MR + mi) * 512 + o);
-          sum.x += v.x;
-          sum.y += v.y;
-          csum += C[(w * MR + mi) * 16 + (o >> 5)];
-        }
-        const float c8 = 8.0f * csum;
-        if (o < ncols) store(m0 + mi, o, sum.x - c8);
-        if (o + 1 < ncols) store(m0 + mi, o + 1, sum.y * 0.0625f - c8);
-      }
-    }
-    __syncthreads();
-  }
+  return (32 / LPB) * (256 + 1) + M * (256 + 1) + M * 256;
 }
 
 // Sum a split-K tile over its P row phases through LDS, in phase order 0..P-1,
@@ -717,10 +602,6 @@ template <int M, int LPB, class Store>
 __device__ __forceinline__ void reduce_phases(const float (&acc)[M][32 / LPB],
                                               const float (&corr)[M], float* smem, int Lr, int P,
                                               int ncols, Store store) {
-  if (Lr == 16 * LPB) {  // uniform: a 16-block tile
-    reduce_tile16<M, LPB>(acc, corr, smem, ncols, store);
-    return;
-  }
   constexpr int CPL = 32 / LPB;
   constexpr int kStride = 256 + 1;
   float* A = smem;                  // [CPL][kStride] accumulators of one row m
