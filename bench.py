@@ -37,6 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 VALU_F32_PEAK_TFLOPS = 78.6    # 256 CU x 4 SIMD x 16 lanes x 2.4 GHz x 2 flop (no packed FP32)
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA, TFLOP/s
 GIB = 1 << 30
 
 
@@ -183,11 +184,14 @@ def bench_dense(torch, dev, steps, warmup):
 # The dominant unit of the headline step: q4_0_gemv at batch 8 on the
 # 4096 x 11008 gate matrix. Batch 8 takes the largest share of the step, and
 # its gate, up and down calls are the longest launches. One call is two
-# dispatches: gemv_q4_0_kernel<8,2,staged> and its split-K reduce kernel.
+# dispatches: the matrix-core kernel gemv_q4_0_mfma_kernel<2,8> and its
+# split-K reduce kernel.
 DOMINANT = {"M": 8, "shape": "ffn_gate"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_M8_4096x11008_traffic.md")
+MAIN_KERNEL = "gemv_q4_0_mfma_kernel"
 KERNEL_SOURCES = ["moe_experts_amd/csrc/q4_device.hpp", "moe_experts_amd/csrc/gemv_q4_0.hip",
-                  "moe_experts_amd/csrc/q4moe_api.cpp"]
+                  "moe_experts_amd/csrc/gemv_mfma_q4_0.hip", "moe_experts_amd/csrc/q4moe_api.cpp",
+                  "moe_experts_amd/build.py"]
 
 
 def kernel_source_hash():
@@ -217,7 +221,17 @@ def measured_traffic():
 
 
 def dense_roofline(d):
-    """Roofline of the dominant unit (see DOMINANT)."""
+    """Roofline of the dominant unit (see DOMINANT).
+
+    The batch-8 call runs on the fp32 matrix cores: every weight is one
+    multiply-add per activation row, 2MKN flops in all, done by
+    v_mfma_f32_4x4x1 (4 activation rows per instruction, no padding at batch 8).
+    The vector ALU unpacks the nibbles: per row of 16 MFMA blocks (512
+    weights) each lane issues about 17 instructions (2 masks, 8 converts, the
+    scale convert, products and corrections, 2 offsets). On one SIMD the matrix
+    and vector instructions issue one after the other (measured with a probe
+    kernel: adding the unpack work lowered the MFMA rate by its own issue
+    time), so the issue bound is their sum."""
     M = DOMINANT["M"]
     shapes = d["shapes"]
     i = [k for k, sh in enumerate(shapes) if sh[0] == DOMINANT["shape"]][0]
@@ -225,30 +239,25 @@ def dense_roofline(d):
     t = d["call_s"][(M, i)]
     flops = 2 * M * K * N
     algo_bytes = q4_bytes(K, N) + 4 * M * K + 4 * M * N
-    # fp32 VALU lane operations per weight of the unpack-and-FMA loop at this
-    # batch (half a block per lane): 16 nibble converts, 4 masks, 1 scale
-    # convert, 8 scale products and corrections ... per 16 weights, plus M FMAs
-    ops_per_weight = (21 + 18 * M) / 16.0
-    alu_s = K * N * ops_per_weight / (VALU_F32_PEAK_TFLOPS * 1e12 / 2)
+    mfma_flops = 2 * (4 * ((M + 3) // 4)) * K * N  # the instruction's 4-row granularity
+    mfma_s = mfma_flops / (MFMA_F32_PEAK_TFLOPS * 1e12)
+    valu_lane_ops = K * N * 17.0 * 64 / 512
+    valu_s = valu_lane_ops / (VALU_F32_PEAK_TFLOPS * 1e12 / 2)
     hbm_s = algo_bytes / (HBM_PEAK_GBS * 1e9)
     tflops = flops / t / 1e12
     gbs = algo_bytes / t / 1e9
-    common = {"traffic": measured_traffic(),
-              "kernel": f"q4_0_gemv M={M} on 4096x11008 (gemv_q4_0_kernel<{M},2,staged> + "
-                        "gemv_q4_0_reduce_kernel)",
-              "avg_launch_us": round(t * 1e6, 2),
-              "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
-              "alu_bound_us": round(alu_s * 1e6, 2), "hbm_bound_us": round(hbm_s * 1e6, 2)}
-    if alu_s > hbm_s:
-        roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": VALU_F32_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / VALU_F32_PEAK_TFLOPS, 4),
-                "note": "achieved counts the 2MKN useful flops; the VALU also unpacks nibbles "
-                        "(alu_ops_frac: all lane operations vs the VALU peak)",
-                "alu_ops_frac": round(alu_s / t, 4), "hbm_GBps": round(gbs, 1)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    roof.update(common)
+    roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_F32_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(),
+            "kernel": f"q4_0_gemv M={M} on 4096x11008 (gemv_q4_0_mfma_kernel<2,8> + "
+                      "gemv_q4_0_reduce_kernel)",
+            "avg_launch_us": round(t * 1e6, 2),
+            "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
+            "mfma_bound_us": round(mfma_s * 1e6, 2), "hbm_bound_us": round(hbm_s * 1e6, 2),
+            "issue_bound_us": round((mfma_s + valu_s) * 1e6, 2),
+            "issue_frac": round((mfma_s + valu_s) / t, 4), "hbm_GBps": round(gbs, 1),
+            "note": "achieved = 2MKN / call time against the fp32 MFMA peak; issue_bound adds "
+                    "the vector unpack work, which issues serially with the MFMAs on a SIMD"}
     return roof
 
 
@@ -307,8 +316,8 @@ def traffic_summary(fetch_csv, write_csv, command):
     cw = med(pick(write, "copyBuffer")[-4:])
     f_fetch = copy_bytes / cf
     f_write = copy_bytes / cw
-    main_f = med(pick(fetch, "gemv_q4_0_kernel")[4:])
-    main_w = med(pick(write, "gemv_q4_0_kernel")[4:])
+    main_f = med(pick(fetch, MAIN_KERNEL)[4:])
+    main_w = med(pick(write, MAIN_KERNEL)[4:])
     red_f = med(pick(fetch, "gemv_q4_0_reduce_kernel")[4:])
     red_w = med(pick(write, "gemv_q4_0_reduce_kernel")[4:])
     M = DOMINANT["M"]
@@ -334,7 +343,7 @@ scale the kernel's counter values to bytes.
 
 | dispatch | fetched (B) | written (B) |
 |---|---|---|
-| gemv_q4_0_kernel<8,2,staged> | {round(main_f * f_fetch)} | {round(main_w * f_write)} |
+| gemv_q4_0_mfma_kernel<2,8> | {round(main_f * f_fetch)} | {round(main_w * f_write)} |
 | gemv_q4_0_reduce_kernel | {round(red_f * f_fetch)} | {round(red_w * f_write)} |
 | **call** | {round((main_f + red_f) * f_fetch)} | {round((main_w + red_w) * f_write)} |
 

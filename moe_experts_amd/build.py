@@ -9,7 +9,13 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4moe.so")
-SOURCES = ["q4moe_api.cpp", "gemv_q4_0.hip", "moe_q4_0.hip", "gemm_q4_0.hip"]
+SOURCES = ["q4moe_api.cpp", "gemv_q4_0.hip", "gemv_mfma_q4_0.hip", "moe_q4_0.hip",
+           "gemm_q4_0.hip"]
+# Per-source extra flags. The matrix-core GEMV keeps its accumulators in
+# ordinary VGPRs (MFMA "VGPR form"): with accumulation registers the
+# allocator rotated the accumulators between loop iterations (register copies
+# on every batch).
+EXTRA = {"gemv_mfma_q4_0.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HEADERS = ["q4_device.hpp", "q4_internal.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -25,20 +31,38 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     """Compile every source into libq4moe.so (always recompiles)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in res.stderr.splitlines()
-                    if "packed-fp32-ops" not in l and l.strip())
-    if res.returncode != 0:
-        sys.stderr.write(err + "\n")
-        raise RuntimeError("hipcc failed building libq4moe.so")
-    if err and verbose:
-        sys.stderr.write(err + "\n")
-    os.replace(tmp, LIB)
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    cflags = [f for f in FLAGS if f != "-shared"]
+    with tempfile.TemporaryDirectory(prefix="q4moe_build_") as tmpdir:
+        def compile_one(src: str):
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+            cmd = [HIPCC, *cflags, *EXTRA.get(src, []), "-c", "-o", obj,
+                   os.path.join(CSRC, src)]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        objs = []
+        for obj, res in results:
+            err = "\n".join(l for l in res.stderr.splitlines()
+                            if "packed-fp32-ops" not in l and l.strip())
+            if res.returncode != 0:
+                sys.stderr.write(err + "\n")
+                raise RuntimeError("hipcc failed building libq4moe.so")
+            if err and verbose:
+                sys.stderr.write(err + "\n")
+            objs.append(obj)
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            sys.stderr.write(res.stderr + "\n")
+            raise RuntimeError("hipcc failed linking libq4moe.so")
+        os.replace(tmp, LIB)
     return LIB
 
 

@@ -1,0 +1,420 @@
+// Decode GEMV over Q4_0 weights on the fp32 matrix cores, for 3 <= M <= 8:
+// y[M x N] = x[M x K] . deq(B[K x N]).
+//
+// The operation is the fused dequantize-inside-the-inner-loop matmul of the
+// "2000-line C++ DeepSeek inference engine" article (§3.4 matmul_q4_0). With
+// several activation rows the work per weight grows with M while the bytes do
+// not, and the fp32 FMA rate of the vector ALU sets the pace. Here the M-fold
+// part runs on v_mfma_f32_4x4x1_16b_f32: sixteen independent 4x4 outer
+// products per instruction, 64 multiply-adds per SIMD cycle, twice the vector
+// FMA rate and with no rounding change (fp32 operands, fp32 accumulation).
+//
+// One MFMA "block" b (4 lanes, lane = 4b + q) is one Q4_0 block (row k, block
+// column j). Lane q holds
+//   A operand: s = x[q + 4h][k] * d[k][j]      (activation row q + 4h)
+//   B operand: nibble i of qs dword q          (column 32j + 8q + i)
+// so the 4x4 product adds s * nibble to output (m = q' + 4h, n = 32j + 8q + i)
+// of every lane pair (q', q): each instruction takes one weight per lane (the
+// dequantization stays one convert per weight) and all 4 (or 8, with the h
+// halves) activation rows. The -8 offset is folded out as in the vector
+// kernels: acc = sum s * nibble, corr = sum s, y = acc - 8 * corr; odd
+// nibbles are converted from the byte masked with 0xF0 (16x) and rescaled at
+// the end, which is exact.
+//
+// Tiles: a workgroup (4 waves) owns JW = 4 or 8 block columns and a K range of
+// Kt rows. The 16 MFMA blocks of a wave are JW columns x PW = 16/JW row phases;
+// the 4 waves are further phases, PT = 4*PW in all, so a lane walks rows
+// myph, myph + PT, ... . Each lane loads its qs dword and the block scale with
+// buffer loads (a buffer over the tile's rows: rows past the tile read zeros
+// without a memory access), RB rows per batch, two batches in flight. The
+// phases are summed inside the wave with lane swaps (v_permlane32/16_swap,
+// a fixed order) and across the waves through LDS, then the tile is written
+// as one split-K partial (or straight to y when K is not split); the split-K
+// sum is the same second kernel as the vector path.
+#include "q4_device.hpp"
+#include "q4_internal.hpp"
+
+namespace q4 {
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaRB = 4;      // rows per lane and batch
+constexpr int kMfmaMaxXs = 64 * 1024;  // LDS bytes for the activation tile
+
+struct MfmaArgs {
+  const float* __restrict__ x;
+  const uint8_t* __restrict__ B;
+  float* __restrict__ y;
+  float* __restrict__ part;  // [S][M][N]
+  int M, N, K, NB;
+  int C, Kt, S;
+};
+
+template <int MH, int JW>
+struct MfmaShape {
+  static constexpr int PW = 16 / JW;        // row phases inside a wave
+  static constexpr int PT = 4 * PW;         // row phases of the workgroup
+  static constexpr int XW = 4 * MH;         // staged activation floats per row
+  static constexpr int NE = 8 * MH / PW;    // accumulator quads per lane after the wave sum
+  static constexpr int TW = JW * 32;        // tile columns
+  static constexpr int OUT = TW * 4 * MH;   // tile outputs (rows 0 .. 4*MH-1)
+  static_assert(JW == 4 || JW == 8, "tile widths of 4 or 8 blocks");
+};
+
+template <int MH, int JW>
+__host__ __device__ constexpr int mfma_rows_pad(int rows) {
+  using SH = MfmaShape<MH, JW>;
+  const int nl = (rows + SH::PT - 1) / SH::PT;
+  return (nl + kMfmaRB - 1) / kMfmaRB * kMfmaRB * SH::PT;
+}
+
+template <int MH, int JW>
+__host__ __device__ constexpr int mfma_lds_bytes(int Kt) {
+  using SH = MfmaShape<MH, JW>;
+  const int xs = (mfma_rows_pad<MH, JW>(Kt) * SH::XW + 255) / 256 * 256 * 4;
+  const int red = 4 * SH::OUT * 4;
+  return xs > red ? xs : red;
+}
+
+// a + b where a comes from this lane and b from the lane 32 (or 16) away:
+// lanes below the distance return a_lo + a_hi, lanes above it b_lo + b_hi.
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// One row of the lane: s = x * d (and its correction sum), then the 8 nibbles
+// of its qs dword against the MH activation halves.
+template <int MH>
+__device__ __forceinline__ void mfma_row(const float (&xv)[MH], uint32_t dbits, uint32_t qs,
+                                         v4f (&acc)[MH][8], float (&corr)[MH]) {
+  const float d = half_bits_to_float(dbits);
+  float s[MH];
+  {
+    // corr sums exactly the rounded s the products use (all-8 nibbles cancel)
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      s[h] = xv[h] * d;
+      corr[h] += s[h];
+    }
+  }
+  uint32_t lo = qs & 0x0f0f0f0fu;
+  uint32_t hi = qs & 0xf0f0f0f0u;
+  asm volatile("" : "+v"(lo), "+v"(hi));  // keep one v_cvt_f32_ubyteN per nibble
+#pragma unroll
+  for (int by = 0; by < 4; ++by) {
+    const float fl = static_cast<float>((lo >> (8 * by)) & 0xffu);
+    const float fh = static_cast<float>((hi >> (8 * by)) & 0xffu);
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      acc[h][2 * by] = __builtin_amdgcn_mfma_f32_4x4x1f32(s[h], fl, acc[h][2 * by], 0, 0, 0);
+      acc[h][2 * by + 1] =
+          __builtin_amdgcn_mfma_f32_4x4x1f32(s[h], fh, acc[h][2 * by + 1], 0, 0, 0);
+    }
+  }
+}
+
+// Sum the tile over its row phases and store it. Inside the wave the PW
+// phases sit 16 lanes apart (PW = 4: lane bits 4 and 5; PW = 2: bit 5); a
+// reduce-scatter with lane swaps leaves each lane NE accumulator quads, summed
+// as (p0 + p2) + (p1 + p3), and the corrections are summed in the same order.
+// Each wave then finishes its values (odd columns / 16, minus 8 * corr) into
+// LDS, and the workgroup adds the 4 waves in wave order.
+template <int MH, int JW>
+__device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)[MH],
+                                                float* smem, const MfmaArgs& a, int s, int j0,
+                                                int lane, int wave, int q, int jj) {
+  using SH = MfmaShape<MH, JW>;
+  constexpr int PW = SH::PW;
+  // step 1 (distance 32): MH = 2 keeps h = lane bit 5, MH = 1 keeps i / 4
+  float S1[4 * MH][4];
+#pragma unroll
+  for (int u = 0; u < 4 * MH; ++u)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      S1[u][r] = MH == 2 ? swap_sum32(acc[0][u][r], acc[MH - 1][u][r])
+                         : swap_sum32(acc[0][u][r], acc[0][(u + 4) & 7][r]);
+  float R[SH::NE][4];
+  if constexpr (PW == 2) {
+#pragma unroll
+    for (int u = 0; u < SH::NE; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[u][r] = S1[u][r];
+  } else {
+    // step 2 (distance 16): lane bit 4 keeps the lower or upper half of the
+    // remaining i range (MH = 2: i vs i + 4; MH = 1: u vs u + 2)
+    constexpr int D2 = MH == 2 ? 4 : 2;
+#pragma unroll
+    for (int u = 0; u < SH::NE; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[u][r] = swap_sum16(S1[u][r], S1[u + D2][r]);
+  }
+#pragma unroll
+  for (int h = 0; h < MH; ++h) {
+    corr[h] += __shfl_xor(corr[h], 32);
+    if constexpr (PW == 4) corr[h] += __shfl_xor(corr[h], 16);
+  }
+  // this lane's activation half and first column: i = ibase + u
+  const int hsel = MH == 2 ? (lane >> 5) : 0;
+  int ibase;
+  if constexpr (PW == 2) ibase = MH == 2 ? 0 : 4 * (lane >> 5);
+  else ibase = MH == 2 ? 4 * ((lane >> 4) & 1) : 4 * (lane >> 5) + 2 * ((lane >> 4) & 1);
+  // corrections of rows m = r + 4 * hsel for this block: lane q = r of the quad
+  const float ch = hsel ? corr[MH - 1] : corr[0];
+  float cb[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cb[r] = __shfl(ch, (lane & ~3) | r);
+
+  __syncthreads();  // the activation tile is reused as the phase-sum scratch
+  float* red = smem + wave * SH::OUT;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = r + 4 * hsel;
+    float v[SH::NE];
+#pragma unroll
+    for (int u = 0; u < SH::NE; ++u)
+      v[u] = ((u & 1) ? R[u][r] * 0.0625f : R[u][r]) - 8.0f * cb[r];
+    float* dst = red + m * SH::TW + jj * 32 + 8 * q + ibase;
+    if constexpr (SH::NE == 2) {
+      *reinterpret_cast<float2*>(dst) = float2{v[0], v[1]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < SH::NE; u += 4)
+        *reinterpret_cast<float4*>(dst + u) = float4{v[u], v[u + 1], v[u + 2], v[u + 3]};
+    }
+  }
+  __syncthreads();
+  float* out = (a.S == 1) ? a.y : a.part + (size_t)s * a.M * a.N;
+  const int n0 = j0 * kBlockWeights;
+  for (int o = threadIdx.x; o < SH::OUT; o += kThreads) {
+    const int m = o / SH::TW;
+    const int n = o - m * SH::TW;
+    if (m < a.M && n0 + n < a.N) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) sum += smem[w * SH::OUT + o];
+      out[(size_t)m * a.N + n0 + n] = sum;
+    }
+  }
+}
+
+template <int MH, int JW>
+__global__ __launch_bounds__(kThreads) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
+  using SH = MfmaShape<MH, JW>;
+  constexpr int PW = SH::PW, PT = SH::PT, XW = SH::XW, RB = kMfmaRB;
+  constexpr uint32_t kOut = 0x80000000u;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int c = L % a.C;
+  const int s = L / a.C;
+  const int t = threadIdx.x;
+  const int lane = t % kWaveSize;
+  const int wave = t / kWaveSize;
+  const int q = lane & 3;
+  const int blk = lane >> 2;
+  const int jj = blk % JW;
+  const int ph = blk / JW;
+  const int j0 = c * JW;
+  const int k0 = s * a.Kt;
+  const int rows = min(a.Kt, a.K - k0);
+  const int nl = (rows + PT - 1) / PT;  // rows of the busiest lane (uniform)
+  const int nb = (nl + RB - 1) / RB;     // batches (uniform)
+  const int rows_pad = nb * RB * PT;
+  const int myph = wave * PW + ph;
+
+  // Activation tile xs[row * XW + e]: e = 2q + h holds row m = q + 4h (MH = 2),
+  // e = q holds m = q (MH = 1), so a lane reads its values with one LDS load.
+  // LDS-DMA copies, zeros for rows m >= M; padding rows zeroed below.
+  float* xs = smem;
+  {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(4 * a.M * a.K));
+    for (int q0 = 0; q0 < rows * XW; q0 += kThreads) {
+      const int idx = q0 + t;
+      const int row = idx / XW;
+      const int e = idx - row * XW;
+      const int m = MH == 2 ? (e >> 1) + 4 * (e & 1) : e;
+      const uint32_t off = (m < a.M && row < rows) ? (uint32_t)(m * a.K + k0 + row) * 4u : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
+                                               off, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Weights: a buffer over this tile's rows, so rows past the tile are out of
+  // range; blocks past the matrix's last column get bit 31 (out of range too).
+  const uint32_t pitch = (uint32_t)a.NB * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.B + (size_t)k0 * pitch, (uint32_t)rows * pitch);
+  const bool colok = j0 + jj < a.NB;
+  const uint32_t lane0 = (uint32_t)myph * pitch + (uint32_t)(j0 + jj) * kBlockBytes;
+  const uint32_t vs0 = colok ? lane0 : kOut;
+  const uint32_t vq0 = colok ? lane0 + 2u + 4u * (uint32_t)q : kOut;
+  const uint32_t step = (uint32_t)PT * pitch;  // bytes between a lane's rows
+
+  uint32_t QA[RB], DA[RB], QB[RB], DB[RB];
+  auto load = [&](int b, uint32_t(&Q)[RB], uint32_t(&D)[RB]) {
+    const uint32_t bo = (uint32_t)(b * RB) * step;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      Q[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, vq0 + bo + (uint32_t)i * step, 0, 0);
+      D[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs0 + bo + (uint32_t)i * step, 0, 0);
+    }
+  };
+  v4f acc[MH][8];
+  float corr[MH];
+#pragma unroll
+  for (int h = 0; h < MH; ++h) {
+    corr[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // Rows past the tile load zeros (zero scale) against a zero-padded
+  // activation, so every batch runs whole.
+  auto compute = [&](int b, const uint32_t(&Q)[RB], const uint32_t(&D)[RB]) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int tr = (b * RB + i) * PT + myph;
+      float xv[MH];
+      if constexpr (MH == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(xs + tr * XW + 2 * q);
+        xv[0] = v.x;
+        xv[1] = v.y;
+      } else {
+        xv[0] = xs[tr * XW + q];
+      }
+      mfma_row<MH>(xv, D[i], Q[i], acc, corr);
+    }
+  };
+
+  load(0, QA, DA);
+  load(1, QB, DB);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * RB));  // the activation copies have landed
+  for (int idx = rows * XW + t; idx < rows_pad * XW; idx += kThreads) xs[idx] = 0.0f;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): only LDS stores need a wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // Two register sets alternate; the scheduling barriers keep each batch's
+  // loads in issue order, so the waits before a batch count only its own.
+  int b = 0;
+  for (; b + 2 <= nb; b += 2) {
+    compute(b, QA, DA);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b + 2, QA, DA);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(b + 1, QB, DB);
+    __builtin_amdgcn_sched_barrier(0);
+    load(b + 3, QB, DB);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b < nb) compute(b, QA, DA);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+
+  mfma_tile_store<MH, JW>(acc, corr, smem, a, s, j0, lane, wave, q, jj);
+}
+
+template <int MH, int JW>
+hipError_t launch_mfma_t(const MfmaArgs& a, hipStream_t st) {
+  const int lds = mfma_lds_bytes<MH, JW>(a.Kt);
+  hipLaunchKernelGGL((gemv_q4_0_mfma_kernel<MH, JW>), dim3(a.C * a.S), dim3(kThreads), lds, st,
+                     a);
+  return hipGetLastError();
+}
+
+// Bytes between the tile start and the furthest row offset a lane forms
+// (rows of two batches past the tile's last batch): must stay below 2^31.
+uint64_t mfma_offset_span(int Kt, int JW, uint32_t pitch) {
+  const int PT = 4 * (16 / JW);
+  const int rows_pad = ((Kt + PT - 1) / PT + kMfmaRB - 1) / kMfmaRB * kMfmaRB * PT;
+  return (uint64_t)(rows_pad + 2 * kMfmaRB * PT) * pitch;
+}
+
+}  // namespace
+
+// Plan: block-column width JW (4 or 8) and K split S. Workgroups share the
+// CUs evenly only in whole rounds of 256, so the plan takes the largest
+// fraction of a whole round used, n / (256 * ceil(n / 256)), over the
+// candidates with at most 512 workgroups (measured: more only adds partial
+// sums) and at least 64 rows per tile; ties go to more workgroups, then to
+// fewer splits (less partial-sum traffic). Tiles are capped so that the
+// activation tile fits in kMfmaMaxXs bytes of LDS.
+bool plan_gemv_mfma(int M, int N, int K, GemvPlan& p) {
+  if (M < 3 || M > 8) return false;
+  const int NB = N / kBlockWeights;
+  const int XW = M > 4 ? 8 : 4;
+  const uint32_t pitch = (uint32_t)NB * kBlockBytes;
+  double best = -1.0;
+  for (int JW : {4, 8}) {
+    const int PT = 4 * (16 / JW);
+    const int C = (NB + JW - 1) / JW;
+    int last_S = -1;
+    for (int s = 1; s <= K; ++s) {
+      int kt = (K + s - 1) / s;
+      kt = (kt + PT - 1) / PT * PT;
+      const int S = (K + kt - 1) / kt;
+      if (S == last_S) continue;
+      last_S = S;
+      const long long n = (long long)C * S;
+      if (n > 512) break;
+      if (S > 1 && kt < 64) break;
+      const int rows_pad = ((kt + PT - 1) / PT + kMfmaRB - 1) / kMfmaRB * kMfmaRB * PT;
+      if (rows_pad * XW * 4 > kMfmaMaxXs) continue;
+      if (mfma_offset_span(kt, JW, pitch) >= (1ull << 31)) continue;
+      const double rounds = (double)((n + 255) / 256);
+      const double score = (double)n / (256.0 * rounds) + 1e-6 * (double)n - 1e-9 * S;
+      if (score > best) {
+        best = score;
+        p.JW = JW;
+        p.C = C;
+        p.Kt = kt;
+        p.S = S;
+      }
+    }
+  }
+  if (best < 0.0) return false;
+  p.mfma = true;
+  p.LPB = 0;
+  p.Jt = p.JW;
+  p.Lr = 0;
+  p.P = 4 * (16 / p.JW);
+  p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
+  return true;
+}
+
+hipError_t launch_gemv_mfma(const float* x, const uint8_t* B, float* y, int M, int N, int K,
+                            void* ws, const GemvPlan& p, hipStream_t st) {
+  MfmaArgs a;
+  a.x = x;
+  a.B = B;
+  a.y = y;
+  a.part = static_cast<float*>(ws);
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.NB = N / kBlockWeights;
+  a.C = p.C;
+  a.Kt = p.Kt;
+  a.S = p.S;
+  hipError_t err;
+  if (M > 4)
+    err = p.JW == 4 ? launch_mfma_t<2, 4>(a, st) : launch_mfma_t<2, 8>(a, st);
+  else
+    err = p.JW == 4 ? launch_mfma_t<1, 4>(a, st) : launch_mfma_t<1, 8>(a, st);
+  if (err != hipSuccess || p.S == 1) return err;
+  return launch_gemv_reduce(a.part, y, M * N, p.S, st);
+}
+
+}  // namespace q4

@@ -115,21 +115,6 @@ __global__ __launch_bounds__(256) void gemv_q4_0_reduce_kernel(const float* __re
   }
 }
 
-hipError_t launch_reduce(const float* part, float* y, int MN, int S, hipStream_t st) {
-  const dim3 grid((MN + 255) / 256), block(256);
-  if (S <= 8)
-    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<8>, grid, block, 0, st, part, y, MN, S);
-  else if (S <= 16)
-    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<16>, grid, block, 0, st, part, y, MN, S);
-  else if (S <= 32)
-    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<32>, grid, block, 0, st, part, y, MN, S);
-  else if (S <= 64)
-    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<64>, grid, block, 0, st, part, y, MN, S);
-  else
-    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<0>, grid, block, 0, st, part, y, MN, S);
-  return hipGetLastError();
-}
-
 template <int M, int LPB>
 hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
   const int rf = 4 * phase_lds_floats<M, LPB>();
@@ -148,7 +133,7 @@ hipError_t launch_one(const GemvArgs& a, bool staged, hipStream_t st) {
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.S == 1) return err;
-  return launch_reduce(a.part, a.y, M * a.N, a.S, st);
+  return launch_gemv_reduce(a.part, a.y, M * a.N, a.S, st);
 }
 
 template <int M>
@@ -160,6 +145,21 @@ hipError_t launch_m(const GemvArgs& a, int lpb, bool staged, hipStream_t st) {
 }
 
 }  // namespace
+
+hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStream_t st) {
+  const dim3 grid((MN + 255) / 256), block(256);
+  if (S <= 8)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<8>, grid, block, 0, st, part, y, MN, S);
+  else if (S <= 16)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<16>, grid, block, 0, st, part, y, MN, S);
+  else if (S <= 32)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<32>, grid, block, 0, st, part, y, MN, S);
+  else if (S <= 64)
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<64>, grid, block, 0, st, part, y, MN, S);
+  else
+    hipLaunchKernelGGL(gemv_q4_0_reduce_kernel<0>, grid, block, 0, st, part, y, MN, S);
+  return hipGetLastError();
+}
 
 // Tile plan: 16-block column tiles; whole blocks per lane for a single row,
 // half blocks for M >= 2 (half the accumulator registers, so more waves per
@@ -173,6 +173,7 @@ hipError_t launch_m(const GemvArgs& a, int lpb, bool staged, hipStream_t st) {
 // largest split within both.
 GemvPlan plan_gemv(int M, int N, int K) {
   GemvPlan p{};
+  if (plan_gemv_mfma(M, N, K, p)) return p;
   constexpr int kMinTileRows = 128;
   const int NB = N / kBlockWeights;
   p.LPB = (M == 1) ? 1 : 2;
@@ -215,6 +216,7 @@ hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N,
   a.C = p.C;
   a.Kt = p.Kt;
   a.S = p.S;
+  if (p.mfma) return launch_gemv_mfma(x, B, y, M, N, K, ws, p, st);
   // Wave-private staging needs 16-byte aligned 16-block row segments.
   const bool staged = p.Jt == kStagedJt && a.NB % 8 == 0 &&
                       (reinterpret_cast<uintptr_t>(B) & 15) == 0;

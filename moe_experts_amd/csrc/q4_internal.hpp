@@ -11,6 +11,8 @@ namespace q4 {
 
 // ---- decode GEMV ---------------------------------------------------------
 struct GemvPlan {
+  bool mfma;        // matrix-core kernel (3 <= M <= 8) instead of the vector tiles
+  int JW;           // matrix-core kernel: block columns per tile (4 or 8)
   int LPB;          // lanes per block (1: whole block per lane, 2: half)
   int Jt;           // block columns per workgroup tile
   int Lr;           // lanes per row phase (Jt * LPB)
@@ -24,6 +26,12 @@ struct GemvPlan {
 GemvPlan plan_gemv(int M, int N, int K);
 hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N, int K,
                        void* ws, const GemvPlan& p, hipStream_t st);
+// matrix-core variant (gemv_mfma_q4_0.hip): false when the shape does not suit it
+bool plan_gemv_mfma(int M, int N, int K, GemvPlan& p);
+hipError_t launch_gemv_mfma(const float* x, const uint8_t* B, float* y, int M, int N, int K,
+                            void* ws, const GemvPlan& p, hipStream_t st);
+// y[i] = sum over s < S of part[s * MN + i], in split order
+hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStream_t st);
 
 // ---- routed-expert MoE decode -------------------------------------------
 struct MoePlan {
