@@ -21,9 +21,9 @@
 // nibbles are converted from the byte masked with 0xF0 (16x) and rescaled at
 // the end, which is exact.
 //
-// Tiles: a workgroup (4 waves) owns JW = 4 or 8 block columns and a K range of
-// Kt rows. The 16 MFMA blocks of a wave are JW columns x PW = 16/JW row phases;
-// the 4 waves are further phases, PT = 4*PW in all, so a lane walks rows
+// Tiles: a workgroup (NW = 4 or 8 waves) owns JW = 4 or 8 block columns and a
+// K range of Kt rows. The 16 MFMA blocks of a wave are JW columns x PW = 16/JW
+// row phases; the waves are further phases, PT = NW*PW in all, so a lane walks rows
 // myph, myph + PT, ... . Each lane loads its qs dword and the block scale with
 // buffer loads (a buffer over the tile's rows: rows past the tile read zeros
 // without a memory access), RB rows per batch, two batches in flight. The
@@ -40,6 +40,7 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaRB = 4;      // rows per lane and batch
+constexpr int kMfmaSets = 2;    // batches in flight (measured: 3 or 4 are slower)
 constexpr int kMfmaMaxXs = 64 * 1024;  // LDS bytes for the activation tile
 
 struct MfmaArgs {
@@ -51,10 +52,11 @@ struct MfmaArgs {
   int C, Kt, S;
 };
 
-template <int MH, int JW>
+template <int MH, int JW, int NW>
 struct MfmaShape {
   static constexpr int PW = 16 / JW;        // row phases inside a wave
-  static constexpr int PT = 4 * PW;         // row phases of the workgroup
+  static constexpr int PT = NW * PW;        // row phases of the workgroup (NW waves)
+  static constexpr int NT = NW * kWaveSize; // lanes per workgroup
   static constexpr int XW = 4 * MH;         // staged activation floats per row
   static constexpr int NE = 8 * MH / PW;    // accumulator quads per lane after the wave sum
   static constexpr int TW = JW * 32;        // tile columns
@@ -62,18 +64,18 @@ struct MfmaShape {
   static_assert(JW == 4 || JW == 8, "tile widths of 4 or 8 blocks");
 };
 
-template <int MH, int JW>
+template <int MH, int JW, int NW>
 __host__ __device__ constexpr int mfma_rows_pad(int rows) {
-  using SH = MfmaShape<MH, JW>;
+  using SH = MfmaShape<MH, JW, NW>;
   const int nl = (rows + SH::PT - 1) / SH::PT;
   return (nl + kMfmaRB - 1) / kMfmaRB * kMfmaRB * SH::PT;
 }
 
-template <int MH, int JW>
+template <int MH, int JW, int NW>
 __host__ __device__ constexpr int mfma_lds_bytes(int Kt) {
-  using SH = MfmaShape<MH, JW>;
-  const int xs = (mfma_rows_pad<MH, JW>(Kt) * SH::XW + 255) / 256 * 256 * 4;
-  const int red = 4 * SH::OUT * 4;
+  using SH = MfmaShape<MH, JW, NW>;
+  const int xs = (mfma_rows_pad<MH, JW, NW>(Kt) * SH::XW + SH::NT - 1) / SH::NT * SH::NT * 4;
+  const int red = NW * SH::OUT * 4;
   return xs > red ? xs : red;
 }
 
@@ -131,12 +133,12 @@ __device__ __forceinline__ void mfma_row(const float (&xv)[MH], uint32_t dbits, 
 // reduce-scatter with lane swaps leaves each lane NE accumulator quads, summed
 // as (p0 + p2) + (p1 + p3), and the corrections are summed in the same order.
 // Each wave then finishes its values (odd columns / 16, minus 8 * corr) into
-// LDS, and the workgroup adds the 4 waves in wave order.
-template <int MH, int JW>
+// LDS, and the workgroup adds its NW waves in wave order.
+template <int MH, int JW, int NW>
 __device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)[MH],
                                                 float* smem, const MfmaArgs& a, int s, int j0,
                                                 int lane, int wave, int q, int jj) {
-  using SH = MfmaShape<MH, JW>;
+  using SH = MfmaShape<MH, JW, NW>;
   constexpr int PW = SH::PW;
   // step 1 (distance 32): MH = 2 keeps h = lane bit 5, MH = 1 keeps i / 4
   float S1[4 * MH][4];
@@ -198,21 +200,21 @@ __device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)
   __syncthreads();
   float* out = (a.S == 1) ? a.y : a.part + (size_t)s * a.M * a.N;
   const int n0 = j0 * kBlockWeights;
-  for (int o = threadIdx.x; o < SH::OUT; o += kThreads) {
+  for (int o = threadIdx.x; o < SH::OUT; o += SH::NT) {
     const int m = o / SH::TW;
     const int n = o - m * SH::TW;
     if (m < a.M && n0 + n < a.N) {
       float sum = 0.0f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) sum += smem[w * SH::OUT + o];
+      for (int w = 0; w < NW; ++w) sum += smem[w * SH::OUT + o];
       out[(size_t)m * a.N + n0 + n] = sum;
     }
   }
 }
 
-template <int MH, int JW>
-__global__ __launch_bounds__(kThreads) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
-  using SH = MfmaShape<MH, JW>;
+template <int MH, int JW, int NW>
+__global__ __launch_bounds__(NW * kWaveSize) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
+  using SH = MfmaShape<MH, JW, NW>;
   constexpr int PW = SH::PW, PT = SH::PT, XW = SH::XW, RB = kMfmaRB;
   constexpr uint32_t kOut = 0x80000000u;
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -240,7 +242,7 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
   float* xs = smem;
   {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(4 * a.M * a.K));
-    for (int q0 = 0; q0 < rows * XW; q0 += kThreads) {
+    for (int q0 = 0; q0 < rows * XW; q0 += SH::NT) {
       const int idx = q0 + t;
       const int row = idx / XW;
       const int e = idx - row * XW;
@@ -262,13 +264,15 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
   const uint32_t vq0 = colok ? lane0 + 2u + 4u * (uint32_t)q : kOut;
   const uint32_t step = (uint32_t)PT * pitch;  // bytes between a lane's rows
 
-  uint32_t QA[RB], DA[RB], QB[RB], DB[RB];
-  auto load = [&](int b, uint32_t(&Q)[RB], uint32_t(&D)[RB]) {
+  // Register sets of NSET batches in a ring: batch b lives in set b % NSET.
+  constexpr int NSET = kMfmaSets;
+  uint32_t Q[NSET][RB], D[NSET][RB];
+  auto load = [&](int b, int k) {
     const uint32_t bo = (uint32_t)(b * RB) * step;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      Q[i] = __builtin_amdgcn_raw_buffer_load_b32(rw, vq0 + bo + (uint32_t)i * step, 0, 0);
-      D[i] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs0 + bo + (uint32_t)i * step, 0, 0);
+      Q[k][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, vq0 + bo + (uint32_t)i * step, 0, 0);
+      D[k][i] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs0 + bo + (uint32_t)i * step, 0, 0);
     }
   };
   v4f acc[MH][8];
@@ -281,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
   }
   // Rows past the tile load zeros (zero scale) against a zero-padded
   // activation, so every batch runs whole.
-  auto compute = [&](int b, const uint32_t(&Q)[RB], const uint32_t(&D)[RB]) {
+  auto compute = [&](int b, int k) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int tr = (b * RB + i) * PT + myph;
@@ -293,103 +297,113 @@ __global__ __launch_bounds__(kThreads) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
       } else {
         xv[0] = xs[tr * XW + q];
       }
-      mfma_row<MH>(xv, D[i], Q[i], acc, corr);
+      mfma_row<MH>(xv, D[k][i], Q[k][i], acc, corr);
     }
   };
 
-  load(0, QA, DA);
-  load(1, QB, DB);
+#pragma unroll
+  for (int k = 0; k < NSET; ++k) load(k, k);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * RB));  // the activation copies have landed
-  for (int idx = rows * XW + t; idx < rows_pad * XW; idx += kThreads) xs[idx] = 0.0f;
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NSET * RB));  // the activation copies have landed
+  for (int idx = rows * XW + t; idx < rows_pad * XW; idx += SH::NT) xs[idx] = 0.0f;
   __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): only LDS stores need a wait
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 
-  // Two register sets alternate; the scheduling barriers keep each batch's
-  // loads in issue order, so the waits before a batch count only its own.
+  // The scheduling barriers keep each batch's loads in issue order, so the
+  // compiler's wait before a batch counts only that batch's loads.
   int b = 0;
-  for (; b + 2 <= nb; b += 2) {
-    compute(b, QA, DA);
-    __builtin_amdgcn_sched_barrier(0);
-    load(b + 2, QA, DA);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(b + 1, QB, DB);
-    __builtin_amdgcn_sched_barrier(0);
-    load(b + 3, QB, DB);
-    __builtin_amdgcn_sched_barrier(0);
+  for (; b + NSET <= nb; b += NSET) {
+#pragma unroll
+    for (int k = 0; k < NSET; ++k) {
+      compute(b + k, k);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b + k + NSET, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-  if (b < nb) compute(b, QA, DA);
+#pragma unroll
+  for (int k = 0; k < NSET - 1; ++k)
+    if (b + k < nb) compute(b + k, k);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
-  mfma_tile_store<MH, JW>(acc, corr, smem, a, s, j0, lane, wave, q, jj);
+  mfma_tile_store<MH, JW, NW>(acc, corr, smem, a, s, j0, lane, wave, q, jj);
 }
 
-template <int MH, int JW>
+template <int MH, int JW, int NW>
 hipError_t launch_mfma_t(const MfmaArgs& a, hipStream_t st) {
-  const int lds = mfma_lds_bytes<MH, JW>(a.Kt);
-  hipLaunchKernelGGL((gemv_q4_0_mfma_kernel<MH, JW>), dim3(a.C * a.S), dim3(kThreads), lds, st,
-                     a);
+  const int lds = mfma_lds_bytes<MH, JW, NW>(a.Kt);
+  hipLaunchKernelGGL((gemv_q4_0_mfma_kernel<MH, JW, NW>), dim3(a.C * a.S), dim3(NW * kWaveSize),
+                     lds, st, a);
   return hipGetLastError();
 }
 
+template <int MH>
+hipError_t launch_mfma_m(const MfmaArgs& a, int JW, int NW, hipStream_t st) {
+  if (NW == 8) return JW == 4 ? launch_mfma_t<MH, 4, 8>(a, st) : launch_mfma_t<MH, 8, 8>(a, st);
+  return JW == 4 ? launch_mfma_t<MH, 4, 4>(a, st) : launch_mfma_t<MH, 8, 4>(a, st);
+}
+
 // Bytes between the tile start and the furthest row offset a lane forms
-// (rows of two batches past the tile's last batch): must stay below 2^31.
-uint64_t mfma_offset_span(int Kt, int JW, uint32_t pitch) {
-  const int PT = 4 * (16 / JW);
+// (rows of kMfmaSets batches past the tile's last batch): must stay below 2^31.
+uint64_t mfma_offset_span(int Kt, int JW, int NW, uint32_t pitch) {
+  const int PT = NW * (16 / JW);
   const int rows_pad = ((Kt + PT - 1) / PT + kMfmaRB - 1) / kMfmaRB * kMfmaRB * PT;
-  return (uint64_t)(rows_pad + 2 * kMfmaRB * PT) * pitch;
+  return (uint64_t)(rows_pad + kMfmaSets * kMfmaRB * PT) * pitch;
 }
 
 }  // namespace
 
-// Plan: block-column width JW (4 or 8) and K split S. Workgroups share the
-// CUs evenly only in whole rounds of 256, so the plan takes the largest
-// fraction of a whole round used, n / (256 * ceil(n / 256)), over the
-// candidates with at most 512 workgroups (measured: more only adds partial
-// sums) and at least 64 rows per tile; ties go to more workgroups, then to
-// fewer splits (less partial-sum traffic). Tiles are capped so that the
-// activation tile fits in kMfmaMaxXs bytes of LDS.
+// Plan: block-column width JW (4 or 8), waves per workgroup NW (4 or 8) and
+// K split S, for n = C*S workgroups. Workgroups share the CUs evenly only in
+// whole rounds of 256, so the plan takes the largest fraction of a whole round
+// used, n / (256 * ceil(n / 256)), over the candidates with at most 2048
+// waves in all (two per SIMD; measured: more waves only add partial sums) and
+// at least 64 rows per tile; ties go to more waves, then to fewer splits (less
+// partial-sum traffic). Tiles are capped so that the activation tile fits in
+// kMfmaMaxXs bytes of LDS.
 bool plan_gemv_mfma(int M, int N, int K, GemvPlan& p) {
   if (M < 3 || M > 8) return false;
   const int NB = N / kBlockWeights;
   const int XW = M > 4 ? 8 : 4;
   const uint32_t pitch = (uint32_t)NB * kBlockBytes;
   double best = -1.0;
-  for (int JW : {4, 8}) {
-    const int PT = 4 * (16 / JW);
-    const int C = (NB + JW - 1) / JW;
-    int last_S = -1;
-    for (int s = 1; s <= K; ++s) {
-      int kt = (K + s - 1) / s;
-      kt = (kt + PT - 1) / PT * PT;
-      const int S = (K + kt - 1) / kt;
-      if (S == last_S) continue;
-      last_S = S;
-      const long long n = (long long)C * S;
-      if (n > 512) break;
-      if (S > 1 && kt < 64) break;
-      const int rows_pad = ((kt + PT - 1) / PT + kMfmaRB - 1) / kMfmaRB * kMfmaRB * PT;
-      if (rows_pad * XW * 4 > kMfmaMaxXs) continue;
-      if (mfma_offset_span(kt, JW, pitch) >= (1ull << 31)) continue;
-      const double rounds = (double)((n + 255) / 256);
-      const double score = (double)n / (256.0 * rounds) + 1e-6 * (double)n - 1e-9 * S;
-      if (score > best) {
-        best = score;
-        p.JW = JW;
-        p.C = C;
-        p.Kt = kt;
-        p.S = S;
+  for (int NW : {4, 8})
+    for (int JW : {4, 8}) {
+      const int PT = NW * (16 / JW);
+      const int C = (NB + JW - 1) / JW;
+      int last_S = -1;
+      for (int s = 1; s <= K; ++s) {
+        int kt = (K + s - 1) / s;
+        kt = (kt + PT - 1) / PT * PT;
+        const int S = (K + kt - 1) / kt;
+        if (S == last_S) continue;
+        last_S = S;
+        const long long n = (long long)C * S;
+        if (n * NW > 2048) break;
+        if (S > 1 && kt < 64) break;
+        const int rows_pad = ((kt + PT - 1) / PT + kMfmaRB - 1) / kMfmaRB * kMfmaRB * PT;
+        if (rows_pad * XW * 4 > kMfmaMaxXs) continue;
+        if (mfma_offset_span(kt, JW, NW, pitch) >= (1ull << 31)) continue;
+        const double rounds = (double)((n + 255) / 256);
+        const double score = (double)n / (256.0 * rounds) + 1e-7 * (double)(n * NW) - 1e-9 * S;
+        if (score > best) {
+          best = score;
+          p.JW = JW;
+          p.NW = NW;
+          p.C = C;
+          p.Kt = kt;
+          p.S = S;
+        }
       }
     }
-  }
   if (best < 0.0) return false;
   p.mfma = true;
   p.LPB = 0;
   p.Jt = p.JW;
   p.Lr = 0;
-  p.P = 4 * (16 / p.JW);
+  p.P = p.NW * (16 / p.JW);
   p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;
   return true;
 }
@@ -408,11 +422,8 @@ hipError_t launch_gemv_mfma(const float* x, const uint8_t* B, float* y, int M, i
   a.C = p.C;
   a.Kt = p.Kt;
   a.S = p.S;
-  hipError_t err;
-  if (M > 4)
-    err = p.JW == 4 ? launch_mfma_t<2, 4>(a, st) : launch_mfma_t<2, 8>(a, st);
-  else
-    err = p.JW == 4 ? launch_mfma_t<1, 4>(a, st) : launch_mfma_t<1, 8>(a, st);
+  const hipError_t err =
+      M > 4 ? launch_mfma_m<2>(a, p.JW, p.NW, st) : launch_mfma_m<1>(a, p.JW, p.NW, st);
   if (err != hipSuccess || p.S == 1) return err;
   return launch_gemv_reduce(a.part, y, M * N, p.S, st);
 }

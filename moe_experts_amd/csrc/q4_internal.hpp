@@ -13,6 +13,7 @@ namespace q4 {
 struct GemvPlan {
   bool mfma;        // matrix-core kernel (3 <= M <= 8) instead of the vector tiles
   int JW;           // matrix-core kernel: block columns per tile (4 or 8)
+  int NW;           // matrix-core kernel: waves per workgroup (4 or 8)
   int LPB;          // lanes per block (1: whole block per lane, 2: half)
   int Jt;           // block columns per workgroup tile
   int Lr;           // lanes per row phase (Jt * LPB)
