@@ -184,7 +184,7 @@ def bench_dense(torch, dev, steps, warmup):
 # The dominant unit of the headline step: q4_0_gemv at batch 8 on the
 # 4096 x 11008 gate matrix. Batch 8 takes the largest share of the step, and
 # its gate, up and down calls are the longest launches. One call is two
-# dispatches: the matrix-core kernel gemv_q4_0_mfma_kernel<2,8> and its
+# dispatches: the matrix-core kernel gemv_q4_0_mfma_kernel<2,8,4> and its
 # split-K reduce kernel.
 DOMINANT = {"M": 8, "shape": "ffn_gate"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_M8_4096x11008_traffic.md")
@@ -249,7 +249,7 @@ def dense_roofline(d):
     roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_F32_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(),
-            "kernel": f"q4_0_gemv M={M} on 4096x11008 (gemv_q4_0_mfma_kernel<2,8> + "
+            "kernel": f"q4_0_gemv M={M} on 4096x11008 (gemv_q4_0_mfma_kernel<2,8,4> + "
                       "gemv_q4_0_reduce_kernel)",
             "avg_launch_us": round(t * 1e6, 2),
             "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
@@ -343,7 +343,7 @@ scale the kernel's counter values to bytes.
 
 | dispatch | fetched (B) | written (B) |
 |---|---|---|
-| gemv_q4_0_mfma_kernel<2,8> | {round(main_f * f_fetch)} | {round(main_w * f_write)} |
+| gemv_q4_0_mfma_kernel<2,8,4> | {round(main_f * f_fetch)} | {round(main_w * f_write)} |
 | gemv_q4_0_reduce_kernel | {round(red_f * f_fetch)} | {round(red_w * f_write)} |
 | **call** | {round((main_f + red_f) * f_fetch)} | {round((main_w + red_w) * f_write)} |
 
