@@ -93,8 +93,9 @@ def test_gemv_integer_exact_bitwise(M, K, N):
     assert (gemv(x, B, N) == ref).all()
 
 
-def test_gemv_invariants_bitwise():
-    M, K, N = 4, 2048, 1536
+@pytest.mark.parametrize("M", [2, 4, 8])  # vector tiles; matrix cores with 1 and 2 row halves
+def test_gemv_invariants_bitwise(M):
+    K, N = 2048, 1536
     x = datagen.activations(5, M, K)
     B = datagen.q4_0_random(6, K, N)
     y = gemv(x, B, N)
@@ -110,12 +111,31 @@ def test_gemv_invariants_bitwise():
     assert (gemv(x, Bz, N) == 0).all()
     B8 = B.copy(); B8[..., 2:] = 0x88
     assert (gemv(x, B8, N) == 0).all()
-    # one-hot x selects the dequantized row bitwise
+    # one-hot x selects the dequantized row bitwise (M one-hot rows)
     W = oracle.dequant_rows(B, N, 0, K)
-    oh = np.zeros((3, K), dtype=np.float32)
-    oh[0, 0] = 1; oh[1, 777] = 1; oh[2, K - 1] = 1
+    rows = [0, 777, K - 1, 5, 1024, 1500, 2000, 3][:M]
+    oh = np.zeros((M, K), dtype=np.float32)
+    for m, k in enumerate(rows):
+        oh[m, k] = 1
     y1 = gemv(oh, B, N)
-    assert (y1[0] == W[0]).all() and (y1[1] == W[777]).all() and (y1[2] == W[K - 1]).all()
+    for m, k in enumerate(rows):
+        assert (y1[m] == W[k]).all(), (m, k)
+
+
+# Batches 3..8 run on the matrix-core kernel: tile widths of 4 or 8 block
+# columns with a partial last tile (N/32 = 13, 21, 43), fewer rows than the
+# tile's row phases (K = 1, 3, 15), one and two activation halves, odd batches,
+# and a matrix too wide for that kernel's plan (the vector tiles take it).
+MATRIX_CORE = [(3, 1, 416), (5, 3, 672), (7, 15, 416), (8, 17, 96), (4, 129, 4128),
+               (6, 300, 1376), (8, 700, 11008), (3, 5000, 672), (8, 64, 262144)]
+
+
+@pytest.mark.parametrize("M,K,N", MATRIX_CORE)
+def test_gemv_matrix_core_edges(M, K, N):
+    x = datagen.activations(M * 7 + K, M, K)
+    B = datagen.q4_0_random(N + 3 * K, K, N)
+    ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+    check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
 
 
 def test_gemv_rows_independent_of_batch():
