@@ -11,11 +11,12 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4moe.so")
 SOURCES = ["q4moe_api.cpp", "gemv_q4_0.hip", "gemv_mfma_q4_0.hip", "moe_q4_0.hip",
            "gemm_q4_0.hip"]
-# Per-source extra flags. The matrix-core GEMV keeps its accumulators in
+# Per-source extra flags. The matrix-core tiles keep their accumulators in
 # ordinary VGPRs (MFMA "VGPR form"): with accumulation registers the
 # allocator rotated the accumulators between loop iterations (register copies
 # on every batch).
-EXTRA = {"gemv_mfma_q4_0.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA = {"gemv_mfma_q4_0.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "moe_q4_0.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 HEADERS = ["q4_device.hpp", "q4_internal.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -9,39 +9,25 @@
 // products per instruction, 64 multiply-adds per SIMD cycle, twice the vector
 // FMA rate and with no rounding change (fp32 operands, fp32 accumulation).
 //
-// One MFMA "block" b (4 lanes, lane = 4b + q) is one Q4_0 block (row k, block
-// column j). Lane q holds
-//   A operand: s = x[q + 4h][k] * d[k][j]      (activation row q + 4h)
-//   B operand: nibble i of qs dword q          (column 32j + 8q + i)
-// so the 4x4 product adds s * nibble to output (m = q' + 4h, n = 32j + 8q + i)
-// of every lane pair (q', q): each instruction takes one weight per lane (the
-// dequantization stays one convert per weight) and all 4 (or 8, with the h
-// halves) activation rows. The -8 offset is folded out as in the vector
-// kernels: acc = sum s * nibble, corr = sum s, y = acc - 8 * corr; odd
-// nibbles are converted from the byte masked with 0xF0 (16x) and rescaled at
-// the end, which is exact.
-//
-// Tiles: a workgroup (NW = 4 or 8 waves) owns JW = 4 or 8 block columns and a
-// K range of Kt rows. The 16 MFMA blocks of a wave are JW columns x PW = 16/JW
-// row phases; the waves are further phases, PT = NW*PW in all, so a lane walks rows
-// myph, myph + PT, ... . Each lane loads its qs dword and the block scale with
-// buffer loads (a buffer over the tile's rows: rows past the tile read zeros
-// without a memory access), RB rows per batch, two batches in flight. The
-// phases are summed inside the wave with lane swaps (v_permlane32/16_swap,
-// a fixed order) and across the waves through LDS, then the tile is written
-// as one split-K partial (or straight to y when K is not split); the split-K
-// sum is the same second kernel as the vector path.
-#include "q4_device.hpp"
+// The tile (operands, phases, loads) is mfma_tile_accumulate in q4_mfma.hpp.
+// Here a workgroup of NW = 4 or 8 waves owns JW = 4 or 8 block columns and a
+// K range of Kt rows. The row phases are summed inside the wave with lane
+// swaps (v_permlane32/16_swap, a fixed order) and across the waves through
+// LDS, then the tile is written as one split-K partial (or straight to y when
+// K is not split); the split-K sum is the same second kernel as the vector path.
 #include "q4_internal.hpp"
+#include "q4_mfma.hpp"
 
 namespace q4 {
 namespace {
 
-typedef float v4f __attribute__((ext_vector_type(4)));
-
-constexpr int kMfmaRB = 4;      // rows per lane and batch
-constexpr int kMfmaSets = 2;    // batches in flight (measured: 3 or 4 are slower)
-constexpr int kMfmaMaxXs = 64 * 1024;  // LDS bytes for the activation tile
+// LDS of the GEMV tile: the activation tile, later reused by the phase sums.
+template <int MH, int JW, int NW>
+constexpr int mfma_lds_bytes(int Kt) {
+  const int xs = mfma_xs_bytes<MH, JW, NW>(Kt);
+  const int red = NW * MfmaShape<MH, JW, NW>::OUT * 4;
+  return xs > red ? xs : red;
+}
 
 struct MfmaArgs {
   const float* __restrict__ x;
@@ -51,82 +37,6 @@ struct MfmaArgs {
   int M, N, K, NB;
   int C, Kt, S;
 };
-
-template <int MH, int JW, int NW>
-struct MfmaShape {
-  static constexpr int PW = 16 / JW;        // row phases inside a wave
-  static constexpr int PT = NW * PW;        // row phases of the workgroup (NW waves)
-  static constexpr int NT = NW * kWaveSize; // lanes per workgroup
-  static constexpr int XW = 4 * MH;         // staged activation floats per row
-  static constexpr int NE = 8 * MH / PW;    // accumulator quads per lane after the wave sum
-  static constexpr int TW = JW * 32;        // tile columns
-  static constexpr int OUT = TW * 4 * MH;   // tile outputs (rows 0 .. 4*MH-1)
-  static_assert(JW == 4 || JW == 8, "tile widths of 4 or 8 blocks");
-};
-
-template <int MH, int JW, int NW>
-__host__ __device__ constexpr int mfma_rows_pad(int rows) {
-  using SH = MfmaShape<MH, JW, NW>;
-  const int nl = (rows + SH::PT - 1) / SH::PT;
-  return (nl + kMfmaRB - 1) / kMfmaRB * kMfmaRB * SH::PT;
-}
-
-template <int MH, int JW, int NW>
-__host__ __device__ constexpr int mfma_lds_bytes(int Kt) {
-  using SH = MfmaShape<MH, JW, NW>;
-  const int xs = (mfma_rows_pad<MH, JW, NW>(Kt) * SH::XW + SH::NT - 1) / SH::NT * SH::NT * 4;
-  const int red = NW * SH::OUT * 4;
-  return xs > red ? xs : red;
-}
-
-// a + b where a comes from this lane and b from the lane 32 (or 16) away:
-// lanes below the distance return a_lo + a_hi, lanes above it b_lo + b_hi.
-__device__ __forceinline__ float swap_sum32(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
-                                                  __builtin_bit_cast(uint32_t, b), false, false);
-  const uint32_t r0 = r[0];
-  const uint32_t r1 = r[1];
-  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
-}
-__device__ __forceinline__ float swap_sum16(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
-                                                  __builtin_bit_cast(uint32_t, b), false, false);
-  const uint32_t r0 = r[0];
-  const uint32_t r1 = r[1];
-  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
-}
-
-// One row of the lane: s = x * d (and its correction sum), then the 8 nibbles
-// of its qs dword against the MH activation halves.
-template <int MH>
-__device__ __forceinline__ void mfma_row(const float (&xv)[MH], uint32_t dbits, uint32_t qs,
-                                         v4f (&acc)[MH][8], float (&corr)[MH]) {
-  const float d = half_bits_to_float(dbits);
-  float s[MH];
-  {
-    // corr sums exactly the rounded s the products use (all-8 nibbles cancel)
-#pragma clang fp contract(off)
-#pragma unroll
-    for (int h = 0; h < MH; ++h) {
-      s[h] = xv[h] * d;
-      corr[h] += s[h];
-    }
-  }
-  uint32_t lo = qs & 0x0f0f0f0fu;
-  uint32_t hi = qs & 0xf0f0f0f0u;
-  asm volatile("" : "+v"(lo), "+v"(hi));  // keep one v_cvt_f32_ubyteN per nibble
-#pragma unroll
-  for (int by = 0; by < 4; ++by) {
-    const float fl = static_cast<float>((lo >> (8 * by)) & 0xffu);
-    const float fh = static_cast<float>((hi >> (8 * by)) & 0xffu);
-#pragma unroll
-    for (int h = 0; h < MH; ++h) {
-      acc[h][2 * by] = __builtin_amdgcn_mfma_f32_4x4x1f32(s[h], fl, acc[h][2 * by], 0, 0, 0);
-      acc[h][2 * by + 1] =
-          __builtin_amdgcn_mfma_f32_4x4x1f32(s[h], fh, acc[h][2 * by + 1], 0, 0, 0);
-    }
-  }
-}
 
 // Sum the tile over its row phases and store it. Inside the wave the PW
 // phases sit 16 lanes apart (PW = 4: lane bits 4 and 5; PW = 2: bit 5); a
@@ -214,119 +124,24 @@ __device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)
 
 template <int MH, int JW, int NW>
 __global__ __launch_bounds__(NW * kWaveSize) void gemv_q4_0_mfma_kernel(MfmaArgs a) {
-  using SH = MfmaShape<MH, JW, NW>;
-  constexpr int PW = SH::PW, PT = SH::PT, XW = SH::XW, RB = kMfmaRB;
-  constexpr uint32_t kOut = 0x80000000u;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
   const int c = L % a.C;
   const int s = L / a.C;
-  const int t = threadIdx.x;
-  const int lane = t % kWaveSize;
-  const int wave = t / kWaveSize;
+  const int lane = threadIdx.x % kWaveSize;
+  const int wave = threadIdx.x / kWaveSize;
   const int q = lane & 3;
-  const int blk = lane >> 2;
-  const int jj = blk % JW;
-  const int ph = blk / JW;
+  const int jj = (lane >> 2) % JW;
   const int j0 = c * JW;
   const int k0 = s * a.Kt;
   const int rows = min(a.Kt, a.K - k0);
-  const int nl = (rows + PT - 1) / PT;  // rows of the busiest lane (uniform)
-  const int nb = (nl + RB - 1) / RB;     // batches (uniform)
-  const int rows_pad = nb * RB * PT;
-  const int myph = wave * PW + ph;
-
-  // Activation tile xs[row * XW + e]: e = 2q + h holds row m = q + 4h (MH = 2),
-  // e = q holds m = q (MH = 1), so a lane reads its values with one LDS load.
-  // LDS-DMA copies, zeros for rows m >= M; padding rows zeroed below.
-  float* xs = smem;
-  {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint32_t)(4 * a.M * a.K));
-    for (int q0 = 0; q0 < rows * XW; q0 += SH::NT) {
-      const int idx = q0 + t;
-      const int row = idx / XW;
-      const int e = idx - row * XW;
-      const int m = MH == 2 ? (e >> 1) + 4 * (e & 1) : e;
-      const uint32_t off = (m < a.M && row < rows) ? (uint32_t)(m * a.K + k0 + row) * 4u : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
-                                               off, 0, 0, 0);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // Weights: a buffer over this tile's rows, so rows past the tile are out of
-  // range; blocks past the matrix's last column get bit 31 (out of range too).
-  const uint32_t pitch = (uint32_t)a.NB * kBlockBytes;
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.B + (size_t)k0 * pitch, (uint32_t)rows * pitch);
-  const bool colok = j0 + jj < a.NB;
-  const uint32_t lane0 = (uint32_t)myph * pitch + (uint32_t)(j0 + jj) * kBlockBytes;
-  const uint32_t vs0 = colok ? lane0 : kOut;
-  const uint32_t vq0 = colok ? lane0 + 2u + 4u * (uint32_t)q : kOut;
-  const uint32_t step = (uint32_t)PT * pitch;  // bytes between a lane's rows
-
-  // Register sets of NSET batches in a ring: batch b lives in set b % NSET.
-  constexpr int NSET = kMfmaSets;
-  uint32_t Q[NSET][RB], D[NSET][RB];
-  auto load = [&](int b, int k) {
-    const uint32_t bo = (uint32_t)(b * RB) * step;
+  int xoff[4 * MH];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      Q[k][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, vq0 + bo + (uint32_t)i * step, 0, 0);
-      D[k][i] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs0 + bo + (uint32_t)i * step, 0, 0);
-    }
-  };
+  for (int m = 0; m < 4 * MH; ++m) xoff[m] = m * a.K;
+  MfmaTileGeom g{a.B, a.NB, j0, k0, rows};
   v4f acc[MH][8];
   float corr[MH];
-#pragma unroll
-  for (int h = 0; h < MH; ++h) {
-    corr[h] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  }
-  // Rows past the tile load zeros (zero scale) against a zero-padded
-  // activation, so every batch runs whole.
-  auto compute = [&](int b, int k) {
-#pragma unroll
-    for (int i = 0; i < RB; ++i) {
-      const int tr = (b * RB + i) * PT + myph;
-      float xv[MH];
-      if constexpr (MH == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(xs + tr * XW + 2 * q);
-        xv[0] = v.x;
-        xv[1] = v.y;
-      } else {
-        xv[0] = xs[tr * XW + q];
-      }
-      mfma_row<MH>(xv, D[k][i], Q[k][i], acc, corr);
-    }
-  };
-
-#pragma unroll
-  for (int k = 0; k < NSET; ++k) load(k, k);
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NSET * RB));  // the activation copies have landed
-  for (int idx = rows * XW + t; idx < rows_pad * XW; idx += SH::NT) xs[idx] = 0.0f;
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): only LDS stores need a wait
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-
-  // The scheduling barriers keep each batch's loads in issue order, so the
-  // compiler's wait before a batch counts only that batch's loads.
-  int b = 0;
-  for (; b + NSET <= nb; b += NSET) {
-#pragma unroll
-    for (int k = 0; k < NSET; ++k) {
-      compute(b + k, k);
-      __builtin_amdgcn_sched_barrier(0);
-      load(b + k + NSET, k);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NSET - 1; ++k)
-    if (b + k < nb) compute(b + k, k);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  mfma_tile_accumulate<MH, JW, NW>(g, a.x, (uint32_t)(4 * a.M * a.K), xoff, a.M, smem, acc, corr);
 
   mfma_tile_store<MH, JW, NW>(acc, corr, smem, a, s, j0, lane, wave, q, jj);
 }

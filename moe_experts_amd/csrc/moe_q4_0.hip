@@ -9,35 +9,46 @@
 // five kernels on one stream (no host round trip, capturable in a graph):
 //
 //   1. route    : one workgroup groups the (token, slot) pairs by expert
-//                 (stable order) into work items of at most 2 pairs of one
-//                 expert. A single token skips it: its 6 pairs are the items.
-//   2. gate/up  : split-K GEMV tiles of the dense decode kernel over the
-//                 routed experts' gate and up matrices; a tile streams its
-//                 expert's 16-block row segments once for all pairs of its
-//                 item and writes per-pair partial sums.
-// At a few tokens per expert the FMA and unpack work (not HBM) bounds these
-// tiles, so what matters is how many waves each SIMD can interleave: work
-// items of at most 2 pairs keep the kernel at 76 VGPRs, whole-block lane
-// shares and 2-row staging batches keep its LDS small. Measured on MI355X,
-// this beats items of 4 or 8 pairs (which stream a hot expert's weights
-// fewer times) by 25 % on uniform and 2x on skewed routing at 32 tokens.
+//                 (stable order). An expert with 1 or 2 pairs becomes one
+//                 vector work item; one with 3 or more becomes ceil(n / 8)
+//                 matrix-core items of balanced sizes (3 .. 8 pairs). A single
+//                 token skips it: its 6 pairs are the (vector) items.
+//   2. gate/up  : split-K GEMV tiles over the routed experts' gate and up
+//                 matrices, two kernels over the two item lists: the dense
+//                 decode kernel's vector tiles (one or two pairs), and the
+//                 fp32 matrix-core tiles (3 .. 8 pairs, one weight per lane
+//                 against 4 pairs per v_mfma_f32_4x4x1). A tile streams its
+//                 expert's row segments once for all pairs of its item and
+//                 writes per-pair partial sums.
+// At a few tokens per expert the FMA and unpack work (not HBM) bounds the
+// vector tiles, so what matters there is how many waves each SIMD can
+// interleave: items of at most 2 pairs keep those tiles small in registers and
+// LDS. Experts chosen by more pairs (hot experts under skewed routing) go to
+// the matrix cores, which take their FMAs 4 pairs at a time and stream the
+// expert's weights once per 8 pairs instead of once per 2.
 //   3. act      : h = SiLU(sum of gate partials) * (sum of up partials).
 //   4. down     : split-K tiles of h . Wd_e, per-pair partial sums.
 //   5. combine  : out[t] = sum over slots in order 0..topk-1 of
 //                 w[t][s] * (sum of the slot's down partials).
 // No atomics and no cross-workgroup hand-off inside a kernel: deterministic.
-// For T >= 2 the tile shapes depend only on (H, I), never on T or on the item
-// sizes, so a token's result is bitwise the same whatever other tokens share
-// the call (batch invariance); a single token uses finer K splits, so it
-// matches its batched result to rounding, not bitwise.
+// For T >= 2 the K splits depend only on (H, I), never on T or on the item
+// sizes, and both tile kinds form the same FMA chains in the same 16 row
+// phases and sum them in the same order, so a token's result is bitwise the
+// same whatever other tokens share the call (batch invariance); a single token
+// uses finer K splits, so it matches its batched result to rounding, not
+// bitwise.
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
+#include "q4_mfma.hpp"
 
 namespace q4 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kMaxChunk = 2;  // pairs per work item (MC <= kMaxChunk)
+constexpr int kMaxChunk = 2;  // pairs per vector work item (MC <= kMaxChunk)
+constexpr int kMfmaPairs = 8;  // pairs per matrix-core work item (3 .. 8)
+constexpr int kMfmaJW = 4;     // matrix-core tiles: 4 block columns, 4 waves: 16 row
+constexpr int kMfmaNW = 4;     // phases, the same phases as the vector tiles
 constexpr int kSplitLoads = 16;    // act: splits summed with all loads in flight
 constexpr int kCombineSplits = 4;  // combine: same, per slot
 constexpr int kLPB = 1;       // whole-block lane shares, for every item size
@@ -45,7 +56,7 @@ constexpr int kJt = 16;       // block columns per tile: 288-byte row segments
 
 struct ItemRec {
   int e, cnt, pad0, pad1;
-  int pairs[kMaxChunk];  // pair index t * topk + slot, in stable expert order
+  int pairs[kMfmaPairs];  // pair index t * topk + slot, in stable expert order
 };
 
 constexpr int kMaxRB = 4;       // rows per lane in one pipelined batch (per-lane path)
@@ -62,9 +73,11 @@ constexpr int moe_rows_per_batch() {
 // ---------------------------------------------------------------------------
 struct RouteArgs {
   const int32_t* __restrict__ ids;  // [npairs]
-  int npairs, E, MC;
-  ItemRec* __restrict__ items;      // [max_items]
+  int npairs, E;
+  ItemRec* __restrict__ items;      // vector items: an expert's 1 or 2 pairs
   int* __restrict__ n_items;
+  ItemRec* __restrict__ mitems;     // matrix-core items: 3 .. 8 pairs of one expert
+  int* __restrict__ n_mitems;
 };
 
 // Inclusive prefix sum over one value per lane of the whole workgroup.
@@ -101,13 +114,20 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // Per-expert offsets into the sorted pair list and into the item list.
+  // Per-expert offsets into the sorted pair list and into the two item
+  // lists: an expert with 1 or 2 pairs makes one vector item; one with 3 or
+  // more makes ceil(cnt / 8) matrix-core items of balanced sizes (3 .. 8).
   const int cnt = (t < a.E) ? s_cnt[t] : 0;
-  const int nch = (cnt + a.MC - 1) / a.MC;
+  const int nv = (cnt >= 1 && cnt <= kMaxChunk) ? 1 : 0;
+  const int nm = cnt > kMaxChunk ? (cnt + kMfmaPairs - 1) / kMfmaPairs : 0;
   const int off = block_inclusive_scan(cnt, s_wsum) - cnt;
-  const int item_incl = block_inclusive_scan(nch, s_wsum);
+  const int v_incl = block_inclusive_scan(nv, s_wsum);
+  const int m_incl = block_inclusive_scan(nm, s_wsum);
   s_off[t] = off;
-  if (t == kRouteThreads - 1) *a.n_items = item_incl;
+  if (t == kRouteThreads - 1) {
+    *a.n_items = v_incl;
+    *a.n_mitems = m_incl;
+  }
   __syncthreads();
 
   // Stable placement: pair p goes after the earlier pairs of its expert.
@@ -120,16 +140,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  const int item0 = item_incl - nch;
-  for (int i = 0; i < nch; ++i) {
+  if (nv) {
     ItemRec r;
     r.e = t;
-    r.cnt = min(a.MC, cnt - i * a.MC);
+    r.cnt = cnt;
     r.pad0 = r.pad1 = 0;
 #pragma unroll
-    for (int m = 0; m < kMaxChunk; ++m)
-      r.pairs[m] = (m < r.cnt) ? s_sorted[off + i * a.MC + m] : 0;
-    a.items[item0 + i] = r;
+    for (int m = 0; m < kMfmaPairs; ++m) r.pairs[m] = (m < cnt) ? s_sorted[off + m] : 0;
+    a.items[v_incl - 1] = r;
+  }
+  int first = off;
+  for (int i = 0; i < nm; ++i) {
+    const int sz = cnt / nm + (i < cnt % nm ? 1 : 0);
+    ItemRec r;
+    r.e = t;
+    r.cnt = sz;
+    r.pad0 = r.pad1 = 0;
+#pragma unroll
+    for (int m = 0; m < kMfmaPairs; ++m) r.pairs[m] = (m < sz) ? s_sorted[first + m] : 0;
+    a.mitems[m_incl - nm + i] = r;
+    first += sz;
   }
 }
 
@@ -188,11 +218,17 @@ __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int
   });
 }
 
+// Tile order. A single token's grid is all live tiles, so consecutive tiles
+// (the same expert's row segments) are remapped onto one XCD to share its L2.
+// A batch's grid is sized for the most items the routing can make and the
+// tiles past the actual item count exit at once; there the plain dispatch
+// order is kept, which spreads the live tiles over all 8 XCDs (the remap
+// would crowd them onto the first few).
 template <int MC, bool STAGED>
 __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int per_item = a.nmat * a.C * a.S;
-  const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int L = MC == 1 ? xcd_logical_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
   const int item = L / per_item;
   ItemRec it;
   if constexpr (MC == 1) {
@@ -222,6 +258,109 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
     static_assert(MC == 2, "work items hold at most 2 pairs");
     if (it.cnt == 2) expert_tile<2, STAGED, false>(a, it, mat, c, s, smem);
   }
+}
+
+// ---------------------------------------------------------------------------
+// 2./4. matrix-core expert tiles (items of 3 .. 8 pairs of one expert)
+//
+// The same split-K tiles as above (the same K ranges, and 16 row phases that
+// take rows p, p + 16, ... in order), but the products run on the fp32 matrix
+// cores (mfma_tile_accumulate), one weight per lane against 4 pairs' rows per
+// instruction. That instruction rounds like v_fma_f32, so every accumulator is
+// the FMA chain a vector tile forms for that phase and column; the phases and
+// the corrections are then summed in phase order 0..15 and finished with the
+// vector tiles' expression. A pair's partial sums are therefore bitwise the same
+// whichever kind of item carries it: results stay independent of how many
+// other pairs chose the same expert.
+// LDS: the activation tile, then [16 phases][4 rows][128 columns] accumulator
+// scratch (one activation half at a time) and [16][8][4] corrections.
+// ---------------------------------------------------------------------------
+constexpr int kMfmaPhases = kMfmaNW * (16 / kMfmaJW);
+constexpr int kMfmaCols = kMfmaJW * kBlockWeights;
+constexpr int kMfmaScratchFloats = kMfmaPhases * 4 * kMfmaCols + kMfmaPhases * 8 * kMfmaJW;
+static_assert(kMfmaPhases == kThreads / (kJt * kLPB), "matrix-core and vector tiles share phases");
+
+template <int MH>
+__device__ void expert_mfma_tile(const ExpertArgs& a, const ItemRec& it, int mat, int c, int s,
+                                 float* smem) {
+  constexpr int JW = kMfmaJW, NW = kMfmaNW;
+  const int lane = threadIdx.x % kWaveSize;
+  const int wave = threadIdx.x / kWaveSize;
+  const int q = lane & 3;
+  const int jj = (lane >> 2) % JW;
+  const int p = wave * (16 / JW) + (lane >> 2) / JW;  // this lane's row phase
+  MfmaTileGeom g;
+  g.B = (mat == 0 ? a.W0 : a.W1) + (size_t)it.e * a.mat_bytes;
+  g.NB = a.NB;
+  g.j0 = c * JW;
+  g.k0 = s * a.Kt;
+  g.rows = min(a.Kt, a.K - g.k0);
+  int xoff[4 * MH];
+#pragma unroll
+  for (int m = 0; m < 4 * MH; ++m) xoff[m] = (it.pairs[m] / a.x_row_div) * a.K;
+  v4f acc[MH][8];
+  float corr[MH];
+  mfma_tile_accumulate<MH, JW, NW>(g, a.x, a.x_bytes, xoff, it.cnt, smem, acc, corr);
+
+  float* sa = smem;                                  // [phase][row r][column]
+  float* sc = smem + kMfmaPhases * 4 * kMfmaCols;    // [phase][m][block]
+  __syncthreads();  // the activation tile is done with
+#pragma unroll
+  for (int h = 0; h < MH; ++h) sc[(p * 8 + q + 4 * h) * JW + jj] = corr[h];
+  const int n0 = g.j0 * kBlockWeights;
+  float* dst = a.part + ((size_t)mat * a.S + s) * a.npairs * a.N;
+#pragma unroll
+  for (int h = 0; h < MH; ++h) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float* row = sa + (p * 4 + r) * kMfmaCols + jj * 32 + 8 * q;
+      *reinterpret_cast<float4*>(row) =
+          float4{acc[h][0][r], acc[h][1][r], acc[h][2][r], acc[h][3][r]};
+      *reinterpret_cast<float4*>(row + 4) =
+          float4{acc[h][4][r], acc[h][5][r], acc[h][6][r], acc[h][7][r]};
+    }
+    __syncthreads();
+    for (int o = threadIdx.x; o < 4 * kMfmaCols; o += kThreads) {
+      const int r = o / kMfmaCols;
+      const int n = o - r * kMfmaCols;
+      const int m = r + 4 * h;
+      if (m < it.cnt && n0 + n < a.N) {
+        float sum = 0.0f, cs = 0.0f;
+        for (int pp = 0; pp < kMfmaPhases; ++pp) {
+          sum += sa[(pp * 4 + r) * kMfmaCols + n];
+          cs += sc[(pp * 8 + m) * JW + n / kBlockWeights];
+        }
+        const float c8 = 8.0f * cs;
+        // the pair of row m, selected without indexing the record at run time
+        // (the record then stays in scalar registers)
+        int pr = 0;
+#pragma unroll
+        for (int mm = 0; mm < 4 * MH; ++mm)
+          if (mm == m) pr = it.pairs[mm];
+        dst[(size_t)pr * a.N + n0 + n] = ((n & 1) ? sum * 0.0625f : sum) - c8;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void moe_expert_mfma_kernel(ExpertArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int per_item = a.nmat * a.C * a.S;
+  const int L = blockIdx.x;  // plain order: see moe_expert_kernel
+  const int item = L / per_item;
+  const int n_items = *a.n_items;
+  const ItemRec it = a.items[item];  // max_items records: in bounds
+  if (item >= n_items) return;
+  int rest = L - item * per_item;
+  const int c = rest % a.C;
+  rest /= a.C;
+  const int mat = rest % a.nmat;
+  const int s = rest / a.nmat;
+  if (it.cnt > 4)
+    expert_mfma_tile<2>(a, it, mat, c, s, smem);
+  else
+    expert_mfma_tile<1>(a, it, mat, c, s, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -338,6 +477,15 @@ hipError_t launch_expert(const ExpertArgs& a, int max_items, bool staged, hipStr
   return hipGetLastError();
 }
 
+hipError_t launch_expert_mfma(const ExpertArgs& a, int max_items, hipStream_t st) {
+  if (max_items == 0) return hipSuccess;
+  const int xs = mfma_xs_bytes<2, kMfmaJW, kMfmaNW>(a.Kt);
+  const int sc = 4 * kMfmaScratchFloats;
+  const dim3 grid(max_items * a.nmat * a.C * a.S);
+  hipLaunchKernelGGL(moe_expert_mfma_kernel, grid, dim3(kThreads), xs > sc ? xs : sc, st, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 MoePlan plan_moe(int T, int H, int I, int E, int topk) {
@@ -350,20 +498,26 @@ MoePlan plan_moe(int T, int H, int I, int E, int topk) {
   const int npairs = T * topk;
   // One pair per item for a single token (only the M = 1 tiles are compiled
   // into that variant); up to 2 pairs of one expert per item otherwise.
+  // Batches: an expert with 1 or 2 pairs is one vector item (at most one per
+  // expert), one with more is matrix-core items of 3 .. 8 pairs.
   p.MC = (T == 1) ? 1 : kMaxChunk;
-  const int bound = E + npairs / p.MC;
-  p.max_items = npairs < bound ? npairs : bound;
+  p.max_items = (T == 1) ? npairs : (npairs < E ? npairs : E);
+  p.max_mitems = (T == 1) ? 0 : npairs / (kMaxChunk + 1);
   // K tiles: a single token has only 6 experts' worth of tiles, so it splits
   // K finer (more workgroups); batches use long tiles (less partial-sum
   // traffic, fewer tile epilogues). The choice depends only on whether T is 1.
   const bool single = (T == 1);
   plan_tiles(H, I / kBlockWeights, single ? 320 : 1280, p.gu_C, p.gu_Kt, p.gu_S);
   plan_tiles(I, H / kBlockWeights, single ? 384 : 768, p.dn_C, p.dn_Kt, p.dn_S);
+  p.gu_Cm = (I / kBlockWeights + kMfmaJW - 1) / kMfmaJW;
+  p.dn_Cm = (H / kBlockWeights + kMfmaJW - 1) / kMfmaJW;
   size_t off = 0;
   p.off_items = off;
   off += align256((size_t)p.max_items * sizeof(ItemRec));
-  p.off_n_items = off;
+  p.off_n_items = off;  // two counters: vector items, matrix-core items
   off += 256;
+  p.off_mitems = off;
+  off += align256((size_t)p.max_mitems * sizeof(ItemRec));
   p.off_gu_part = off;
   off += align256((size_t)2 * p.gu_S * npairs * I * sizeof(float));
   p.off_h = off;
@@ -385,13 +539,16 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   float* dn_part = reinterpret_cast<float*>(base + p.off_dn_part);
   const int npairs = p.T * p.topk;
 
+  ItemRec* mitems = reinterpret_cast<ItemRec*>(base + p.off_mitems);
+  int* n_mitems = n_items + 1;
   RouteArgs ra;
   ra.ids = ids;
   ra.npairs = npairs;
   ra.E = p.E;
-  ra.MC = p.MC;
   ra.items = items;
   ra.n_items = n_items;
+  ra.mitems = mitems;
+  ra.n_mitems = n_mitems;
   hipError_t err = hipSuccess;
   if (p.MC > 1) {  // single token: items are the pairs themselves
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
@@ -429,6 +586,12 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, staged_gu, st)
                     : launch_expert<kMaxChunk>(g, p.max_items, staged_gu, st);
   if (err != hipSuccess) return err;
+  ExpertArgs gm = g;
+  gm.items = mitems;
+  gm.n_items = n_mitems;
+  gm.C = p.gu_Cm;
+  err = launch_expert_mfma(gm, p.max_mitems, st);
+  if (err != hipSuccess) return err;
 
   const size_t nh = (size_t)npairs * p.I;
   // A single token's down tiles form h = SiLU(gate) * up themselves from the
@@ -463,6 +626,12 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
                       p.gu_S};
   err = (p.MC == 1) ? launch_expert<1>(d, p.max_items, staged_dn, st)
                     : launch_expert<kMaxChunk>(d, p.max_items, staged_dn, st);
+  if (err != hipSuccess) return err;
+  ExpertArgs dm = d;
+  dm.items = mitems;
+  dm.n_items = n_mitems;
+  dm.C = p.dn_Cm;
+  err = launch_expert_mfma(dm, p.max_mitems, st);
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;

@@ -37,12 +37,14 @@ hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStr
 // ---- routed-expert MoE decode -------------------------------------------
 struct MoePlan {
   int T, H, I, E, topk;
-  int MC;                // pairs per work item (1 for a single token, else 8)
-  int max_items;         // upper bound on (expert, pair-chunk) work items
+  int MC;                // pairs per vector work item (1 for a single token, else 2)
+  int max_items;         // upper bound on vector work items (1 or 2 pairs of one expert)
+  int max_mitems;        // upper bound on matrix-core work items (3 .. 8 pairs), 0 for T = 1
+  int gu_Cm, dn_Cm;      // matrix-core column tiles (4 block columns each)
   int gu_C, gu_Kt, gu_S; // gate/up tiles: column tiles, rows per tile, K splits
   int dn_C, dn_Kt, dn_S; // down tiles
   // workspace layout (byte offsets)
-  size_t off_items, off_n_items, off_gu_part, off_h, off_dn_part;
+  size_t off_items, off_n_items, off_mitems, off_gu_part, off_h, off_dn_part;
   size_t ws_bytes;
 };
 

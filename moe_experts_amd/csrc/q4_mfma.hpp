@@ -1,0 +1,250 @@
+// Matrix-core (fp32 v_mfma_f32_4x4x1_16b_f32) tile of a Q4_0 GEMV, shared by the
+// decode GEMV at batch 3..8 and the MoE expert tiles of 3..8 pairs.
+//
+// One MFMA "block" b (4 lanes, lane = 4b + q) is one Q4_0 block (row k, block
+// column j). Lane q holds
+//   A operand: s = x[q + 4h][k] * d[k][j]      (activation row q + 4h)
+//   B operand: nibble i of qs dword q          (column 32j + 8q + i)
+// so the 4x4 product adds s * nibble to output (m = q' + 4h, n = 32j + 8q + i)
+// of every lane pair (q', q): one weight per lane per instruction (one convert
+// per weight, as in the vector kernels) against 4 activation rows (8 with the
+// two h halves). The instruction rounds exactly like v_fma_f32 (one rounding;
+// checked bit for bit on MI355X), so each accumulator is the same fp32 FMA
+// chain a vector lane would form. The -8 offset is folded out: acc = sum of
+// s * nibble, corr = sum of s, y = acc - 8 * corr; odd nibbles come from the
+// byte masked with 0xF0 (16x) and are rescaled at the end, which is exact.
+//
+// Tile: a workgroup of NW waves owns JW block columns and the rows
+// [k0, k0 + rows) of one matrix. The 16 MFMA blocks of a wave are JW columns
+// x PW = 16/JW row phases; the waves are further phases, PT = NW*PW in all
+// (phase myph = wave*PW + ph), and phase p takes rows p, p + PT, ... in order.
+// Each lane loads its 4-byte qs dword and 2-byte scale per row with buffer
+// loads from a buffer over the tile's rows only (rows past the tile read zeros
+// with no memory access), kMfmaRB rows per batch, kMfmaSets batches in flight
+// in a register ring. Activations are staged once per tile in LDS.
+#pragma once
+
+#include "q4_device.hpp"
+
+namespace q4 {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaRB = 4;      // rows per lane and batch
+constexpr int kMfmaSets = 2;    // batches in flight (measured: 3 or 4 are slower)
+constexpr int kMfmaMaxXs = 64 * 1024;  // LDS bytes for the activation tile
+
+template <int MH, int JW, int NW>
+struct MfmaShape {
+  static constexpr int PW = 16 / JW;        // row phases inside a wave
+  static constexpr int PT = NW * PW;        // row phases of the workgroup (NW waves)
+  static constexpr int NT = NW * kWaveSize; // lanes per workgroup
+  static constexpr int XW = 4 * MH;         // staged activation floats per row
+  static constexpr int NE = 8 * MH / PW;    // accumulator quads per lane after the wave sum
+  static constexpr int TW = JW * 32;        // tile columns
+  static constexpr int OUT = TW * 4 * MH;   // tile outputs (rows 0 .. 4*MH-1)
+  static_assert(JW == 4 || JW == 8, "tile widths of 4 or 8 blocks");
+};
+
+template <int MH, int JW, int NW>
+__host__ __device__ constexpr int mfma_rows_pad(int rows) {
+  using SH = MfmaShape<MH, JW, NW>;
+  const int nl = (rows + SH::PT - 1) / SH::PT;
+  return (nl + kMfmaRB - 1) / kMfmaRB * kMfmaRB * SH::PT;
+}
+
+// LDS bytes of the activation tile of a tile of `rows` rows (whole staging
+// passes of NT words, so every DMA lane of the last pass writes inside it).
+template <int MH, int JW, int NW>
+__host__ __device__ constexpr int mfma_xs_bytes(int rows) {
+  using SH = MfmaShape<MH, JW, NW>;
+  return (mfma_rows_pad<MH, JW, NW>(rows) * SH::XW + SH::NT - 1) / SH::NT * SH::NT * 4;
+}
+
+// a + b where a comes from this lane and b from the lane 32 (or 16) away:
+// lanes below the distance return a_lo + a_hi, lanes above it b_lo + b_hi.
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// One row of the lane: s = x * d (and its correction sum), then the 8 nibbles
+// of its qs dword against the MH activation halves.
+template <int MH>
+__device__ __forceinline__ void mfma_row(const float (&xv)[MH], uint32_t dbits, uint32_t qs,
+                                         v4f (&acc)[MH][8], float (&corr)[MH]) {
+  const float d = half_bits_to_float(dbits);
+  float s[MH];
+  {
+    // corr sums exactly the rounded s the products use (all-8 nibbles cancel)
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      s[h] = xv[h] * d;
+      corr[h] += s[h];
+    }
+  }
+  uint32_t lo = qs & 0x0f0f0f0fu;
+  uint32_t hi = qs & 0xf0f0f0f0u;
+  asm volatile("" : "+v"(lo), "+v"(hi));  // keep one v_cvt_f32_ubyteN per nibble
+#pragma unroll
+  for (int by = 0; by < 4; ++by) {
+    const float fl = static_cast<float>((lo >> (8 * by)) & 0xffu);
+    const float fh = static_cast<float>((hi >> (8 * by)) & 0xffu);
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      acc[h][2 * by] = __builtin_amdgcn_mfma_f32_4x4x1f32(s[h], fl, acc[h][2 * by], 0, 0, 0);
+      acc[h][2 * by + 1] =
+          __builtin_amdgcn_mfma_f32_4x4x1f32(s[h], fh, acc[h][2 * by + 1], 0, 0, 0);
+    }
+  }
+}
+
+// Geometry of one tile.
+struct MfmaTileGeom {
+  const uint8_t* B;  // the matrix (K rows of NB blocks)
+  int NB;            // blocks per row
+  int j0;            // first block column of the tile
+  int k0, rows;      // row range of the tile
+};
+
+// Accumulate one tile (raw acc and corr per lane; see above). Activation row m
+// of the tile is x + xoff[m] floats, indexed by the matrix row, for m < M;
+// rows m >= M are zero. x_bytes bounds every activation read. smem must hold
+// mfma_xs_bytes<MH, JW, NW>(rows) bytes; the tile ends with the activation
+// tile still in LDS (callers that reuse it start with a barrier).
+template <int MH, int JW, int NW>
+__device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
+                                                     const float* __restrict__ x,
+                                                     uint32_t x_bytes, const int (&xoff)[4 * MH],
+                                                     int M, float* smem, v4f (&acc)[MH][8],
+                                                     float (&corr)[MH]) {
+  using SH = MfmaShape<MH, JW, NW>;
+  constexpr int PW = SH::PW, PT = SH::PT, XW = SH::XW, RB = kMfmaRB;
+  constexpr uint32_t kOut = 0x80000000u;
+  const int t = threadIdx.x;
+  const int lane = t % kWaveSize;
+  const int wave = t / kWaveSize;
+  const int q = lane & 3;
+  const int blk = lane >> 2;
+  const int jj = blk % JW;
+  const int ph = blk / JW;
+  const int k0 = g.k0;
+  const int rows = g.rows;
+  const int nl = (rows + PT - 1) / PT;  // rows of the busiest lane (uniform)
+  const int nb = (nl + RB - 1) / RB;     // batches (uniform)
+  const int rows_pad = nb * RB * PT;
+  const int myph = wave * PW + ph;
+  const int j0 = g.j0;
+  struct {
+    const float* x;
+    int M;
+    uint32_t x_bytes;
+  } a{x, M, x_bytes};
+
+  // Activation tile xs[row * XW + e]: e = 2q + h holds row m = q + 4h (MH = 2),
+  // e = q holds m = q (MH = 1), so a lane reads its values with one LDS load.
+  // LDS-DMA copies, zeros for rows m >= M; padding rows zeroed below.
+  float* xs = smem;
+  {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    for (int q0 = 0; q0 < rows * XW; q0 += SH::NT) {
+      const int idx = q0 + t;
+      const int row = idx / XW;
+      const int e = idx - row * XW;
+      const int m = MH == 2 ? (e >> 1) + 4 * (e & 1) : e;
+      int xo = 0;
+#pragma unroll
+      for (int mm = 0; mm < 4 * MH; ++mm)
+        if (mm == m) xo = xoff[mm];
+      const uint32_t off = (m < a.M && row < rows) ? (uint32_t)(xo + k0 + row) * 4u : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
+                                               off, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // Weights: a buffer over this tile's rows, so rows past the tile are out of
+  // range; blocks past the matrix's last column get bit 31 (out of range too).
+  const uint32_t pitch = (uint32_t)g.NB * kBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B + (size_t)k0 * pitch, (uint32_t)rows * pitch);
+  const bool colok = j0 + jj < g.NB;
+  const uint32_t lane0 = (uint32_t)myph * pitch + (uint32_t)(j0 + jj) * kBlockBytes;
+  const uint32_t vs0 = colok ? lane0 : kOut;
+  const uint32_t vq0 = colok ? lane0 + 2u + 4u * (uint32_t)q : kOut;
+  const uint32_t step = (uint32_t)PT * pitch;  // bytes between a lane's rows
+
+  // Register sets of NSET batches in a ring: batch b lives in set b % NSET.
+  constexpr int NSET = kMfmaSets;
+  uint32_t Q[NSET][RB], D[NSET][RB];
+  auto load = [&](int b, int k) {
+    const uint32_t bo = (uint32_t)(b * RB) * step;
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      Q[k][i] = __builtin_amdgcn_raw_buffer_load_b32(rw, vq0 + bo + (uint32_t)i * step, 0, 0);
+      D[k][i] = __builtin_amdgcn_raw_buffer_load_b16(rw, vs0 + bo + (uint32_t)i * step, 0, 0);
+    }
+  };
+#pragma unroll
+  for (int h = 0; h < MH; ++h) {
+    corr[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  // Rows past the tile load zeros (zero scale) against a zero-padded
+  // activation, so every batch runs whole.
+  auto compute = [&](int b, int k) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int tr = (b * RB + i) * PT + myph;
+      float xv[MH];
+      if constexpr (MH == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(xs + tr * XW + 2 * q);
+        xv[0] = v.x;
+        xv[1] = v.y;
+      } else {
+        xv[0] = xs[tr * XW + q];
+      }
+      mfma_row<MH>(xv, D[k][i], Q[k][i], acc, corr);
+    }
+  };
+
+#pragma unroll
+  for (int k = 0; k < NSET; ++k) load(k, k);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NSET * RB));  // the activation copies have landed
+  for (int idx = rows * XW + t; idx < rows_pad * XW; idx += SH::NT) xs[idx] = 0.0f;
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): only LDS stores need a wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+
+  // The scheduling barriers keep each batch's loads in issue order, so the
+  // compiler's wait before a batch counts only that batch's loads.
+  int b = 0;
+  for (; b + NSET <= nb; b += NSET) {
+#pragma unroll
+    for (int k = 0; k < NSET; ++k) {
+      compute(b + k, k);
+      __builtin_amdgcn_sched_barrier(0);
+      load(b + k + NSET, k);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NSET - 1; ++k)
+    if (b + k < nb) compute(b + k, k);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+}
+
+}  // namespace q4
