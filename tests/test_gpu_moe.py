@@ -43,7 +43,7 @@ def test_moe_duplicates_out_of_range_and_crowded_expert():
     Wg, Wu, Wd = small_experts(7, H, I, E)
     g = np.random.Generator(np.random.PCG64(3))
     ids = g.integers(0, E, size=(T, topk)).astype(np.int32)
-    ids[:, 0] = 2                    # every token uses expert 2: 20 pairs -> 10 work items
+    ids[:, 0] = 2                    # every token uses expert 2: 20 pairs -> 3 matrix-core items
     ids[0, 1] = ids[0, 2] = 5        # a duplicate within a token
     ids[1, 3] = E + 3                # out of range -> contributes nothing
     ids[2, 2] = -1
@@ -51,6 +51,25 @@ def test_moe_duplicates_out_of_range_and_crowded_expert():
     ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, H, I, E)
     got = moe_gpu(x, Wg, Wu, Wd, ids, w, I, E)
     check_tol(got, ref, bnd, TOL, "edge routing")
+
+
+@pytest.mark.parametrize("H,I", [(256, 128), (320, 96)])
+def test_moe_batch_invariance_across_item_kinds(H, I):
+    """Experts chosen by 3+ pairs run on the matrix-core tiles, by 1-2 pairs on
+    the vector tiles; a token's output must be bitwise the same either way."""
+    T, E, topk = 12, 4, 2
+    x = datagen.activations(H + I, T, H)
+    Wg, Wu, Wd = small_experts(5 * H + I, H, I, E)
+    ids, w, _ = datagen.routing(H, T, E, topk)
+    got = moe_gpu(x, Wg, Wu, Wd, ids, w, I, E)
+    ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, H, I, E)
+    check_tol(got, ref, bnd, TOL, "12 tokens on 4 experts")
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    assert counts.max() >= 3  # some expert takes the matrix-core path
+    for t in range(T):
+        sel = [t, (t + 5) % T]
+        pair = moe_gpu(x[sel], Wg, Wu, Wd, ids[sel], w[sel], I, E)
+        assert (pair[0] == got[t]).all(), f"token {t} differs in a batch of 2 vs 12"
 
 
 def test_moe_all_ids_invalid_gives_zero():
