@@ -189,9 +189,9 @@ def bench_dense(torch, dev, steps, warmup):
 DOMINANT = {"M": 8, "shape": "ffn_gate"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemv_q4_0_M8_4096x11008_traffic.md")
 MAIN_KERNEL = "gemv_q4_0_mfma_kernel"
-KERNEL_SOURCES = ["moe_experts_amd/csrc/q4_device.hpp", "moe_experts_amd/csrc/gemv_q4_0.hip",
-                  "moe_experts_amd/csrc/gemv_mfma_q4_0.hip", "moe_experts_amd/csrc/q4moe_api.cpp",
-                  "moe_experts_amd/build.py"]
+KERNEL_SOURCES = ["moe_experts_amd/csrc/q4_device.hpp", "moe_experts_amd/csrc/q4_mfma.hpp",
+                  "moe_experts_amd/csrc/gemv_q4_0.hip", "moe_experts_amd/csrc/gemv_mfma_q4_0.hip",
+                  "moe_experts_amd/csrc/q4moe_api.cpp", "moe_experts_amd/build.py"]
 
 
 def kernel_source_hash():
