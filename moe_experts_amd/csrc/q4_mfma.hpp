@@ -146,18 +146,13 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
   const int rows_pad = nb * RB * PT;
   const int myph = wave * PW + ph;
   const int j0 = g.j0;
-  struct {
-    const float* x;
-    int M;
-    uint32_t x_bytes;
-  } a{x, M, x_bytes};
 
   // Activation tile xs[row * XW + e]: e = 2q + h holds row m = q + 4h (MH = 2),
   // e = q holds m = q (MH = 1), so a lane reads its values with one LDS load.
   // LDS-DMA copies, zeros for rows m >= M; padding rows zeroed below.
   float* xs = smem;
   {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
     for (int q0 = 0; q0 < rows * XW; q0 += SH::NT) {
       const int idx = q0 + t;
       const int row = idx / XW;
@@ -167,7 +162,7 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
 #pragma unroll
       for (int mm = 0; mm < 4 * MH; ++mm)
         if (mm == m) xo = xoff[mm];
-      const uint32_t off = (m < a.M && row < rows) ? (uint32_t)(xo + k0 + row) * 4u : kOut;
+      const uint32_t off = (m < M && row < rows) ? (uint32_t)(xo + k0 + row) * 4u : kOut;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
                                                off, 0, 0, 0);
     }
