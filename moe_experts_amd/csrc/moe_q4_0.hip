@@ -97,20 +97,41 @@ __device__ int block_inclusive_scan(int v, int* wsum) {
   return v + add;
 }
 
+// Bits of an expert id (ids are below Q4_MOE_MAX_E).
+constexpr int kIdBits = 10;
+static_assert((1 << kIdBits) >= Q4_MOE_MAX_E, "expert ids fit the ballot match");
+static_assert(Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK <= kRouteThreads, "one lane per pair");
+constexpr int kRouteWaves = Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK / kWaveSize;
+
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
-  __shared__ int s_ids[Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK];
   __shared__ int s_cnt[Q4_MOE_MAX_E];
   __shared__ int s_off[Q4_MOE_MAX_E];
   __shared__ int s_sorted[Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK];
+  __shared__ int s_wcnt[kRouteWaves][Q4_MOE_MAX_E];  // pairs per expert in each wave
   __shared__ int s_wsum[kRouteThreads / kWaveSize];
   const int t = threadIdx.x;
+  const int lane = t & (kWaveSize - 1);
+  const int wave = t / kWaveSize;
 
+  // Lane p holds pair p. Lanes of one wave with the same (valid) expert id
+  // find each other with one ballot per id bit: the exact-match mask.
+  const int e = t < a.npairs ? a.ids[t] : -1;
+  const bool valid = e >= 0 && e < a.E;
+  uint64_t same = __ballot(valid);
+#pragma unroll
+  for (int b = 0; b < kIdBits; ++b) {
+    const bool bit = (e >> b) & 1;
+    const uint64_t set = __ballot(bit);
+    same &= bit ? set : ~set;
+  }
+  const uint64_t below = (1ull << lane) - 1;
   s_cnt[t] = 0;
-  for (int p = t; p < a.npairs; p += kRouteThreads) s_ids[p] = a.ids[p];
+  for (int i = t; i < kRouteWaves * Q4_MOE_MAX_E; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
   __syncthreads();
-  for (int p = t; p < a.npairs; p += kRouteThreads) {
-    const int e = s_ids[p];
-    if (e >= 0 && e < a.E) atomicAdd(&s_cnt[e], 1);
+  // the first lane of each match group records the group's size
+  if (valid && (same & below) == 0) {
+    s_wcnt[wave][e] = __popcll(same);
+    atomicAdd(&s_cnt[e], __popcll(same));
   }
   __syncthreads();
 
@@ -130,13 +151,12 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   }
   __syncthreads();
 
-  // Stable placement: pair p goes after the earlier pairs of its expert.
-  for (int p = t; p < a.npairs; p += kRouteThreads) {
-    const int e = s_ids[p];
-    if (e < 0 || e >= a.E) continue;
-    int rank = 0;
-    for (int q = 0; q < p; ++q) rank += (s_ids[q] == e) ? 1 : 0;
-    s_sorted[s_off[e] + rank] = p;
+  // Stable placement: pair p goes after the earlier pairs of its expert
+  // (those of earlier waves, then the lower lanes of its own wave).
+  if (valid) {
+    int rank = __popcll(same & below);
+    for (int w = 0; w < wave; ++w) rank += s_wcnt[w][e];
+    s_sorted[s_off[e] + rank] = t;
   }
   __syncthreads();
 
@@ -218,46 +238,38 @@ __device__ void expert_tile(const ExpertArgs& a, const ItemRec& it, int mat, int
   });
 }
 
-// Tile order. A single token's grid is all live tiles, so consecutive tiles
-// (the same expert's row segments) are remapped onto one XCD to share its L2.
-// A batch's grid is sized for the most items the routing can make and the
-// tiles past the actual item count exit at once; there the plain dispatch
-// order is kept, which spreads the live tiles over all 8 XCDs (the remap
-// would crowd them onto the first few).
+// Vector tile number r of item it: column tile, matrix and K split.
 template <int MC, bool STAGED>
-__global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int per_item = a.nmat * a.C * a.S;
-  const int L = MC == 1 ? xcd_logical_tile(blockIdx.x, gridDim.x) : (int)blockIdx.x;
-  const int item = L / per_item;
-  ItemRec it;
-  if constexpr (MC == 1) {
-    // One pair per item (a single token): item p is pair p, read straight
-    // from the routing ids; no routing table.
-    if (item >= a.npairs) return;
-    const int e = a.ids[item];
-    if (e < 0 || e >= a.E) return;  // an invalid slot contributes nothing
-    it.e = e;
-    it.cnt = 1;
-    it.pairs[0] = item;
-  } else {
-    // Both loads are issued before either is used (one round trip); the item
-    // array always has max_items records, so the read is in bounds.
-    const int n_items = *a.n_items;
-    it = a.items[item];
-    if (item >= n_items) return;
-  }
-  int rest = L - item * per_item;
-  const int c = rest % a.C;
-  rest /= a.C;
-  const int mat = rest % a.nmat;
-  const int s = rest / a.nmat;
+__device__ void vector_item_tile(const ExpertArgs& a, const ItemRec& it, int r, float* smem) {
+  const int c = r % a.C;
+  r /= a.C;
+  const int mat = r % a.nmat;
+  const int s = r / a.nmat;
   if (it.cnt == 1) {
     expert_tile<1, STAGED, MC == 1>(a, it, mat, c, s, smem);
   } else if constexpr (MC > 1) {
     static_assert(MC == 2, "work items hold at most 2 pairs");
     if (it.cnt == 2) expert_tile<2, STAGED, false>(a, it, mat, c, s, smem);
   }
+}
+
+// A single token: item p is pair p, read straight from the routing ids (no
+// routing table). The grid is all live tiles, so consecutive tiles (the same
+// expert's row segments) are remapped onto one XCD to share its L2.
+template <bool STAGED>
+__global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int per_item = a.nmat * a.C * a.S;
+  const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
+  const int item = L / per_item;
+  if (item >= a.npairs) return;
+  const int e = a.ids[item];
+  if (e < 0 || e >= a.E) return;  // an invalid slot contributes nothing
+  ItemRec it;
+  it.e = e;
+  it.cnt = 1;
+  it.pairs[0] = item;
+  vector_item_tile<1, STAGED>(a, it, L - item * per_item, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -344,23 +356,48 @@ __device__ void expert_mfma_tile(const ExpertArgs& a, const ItemRec& it, int mat
   }
 }
 
-__global__ __launch_bounds__(kThreads) void moe_expert_mfma_kernel(ExpertArgs a) {
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int per_item = a.nmat * a.C * a.S;
-  const int L = blockIdx.x;  // plain order: see moe_expert_kernel
-  const int item = L / per_item;
-  const int n_items = *a.n_items;
-  const ItemRec it = a.items[item];  // max_items records: in bounds
-  if (item >= n_items) return;
-  int rest = L - item * per_item;
-  const int c = rest % a.C;
-  rest /= a.C;
-  const int mat = rest % a.nmat;
-  const int s = rest / a.nmat;
+// Matrix-core tile number r of item it.
+__device__ void mfma_item_tile(const ExpertArgs& a, const ItemRec& it, int r, float* smem) {
+  const int c = r % a.C;
+  r /= a.C;
+  const int mat = r % a.nmat;
+  const int s = r / a.nmat;
   if (it.cnt > 4)
     expert_mfma_tile<2>(a, it, mat, c, s, smem);
   else
     expert_mfma_tile<1>(a, it, mat, c, s, smem);
+}
+
+// A batch: the vector items (a) and the matrix-core items (am) in one grid.
+// The grid is sized for the most items the routing can make; the live tiles
+// of both kinds come first, evenly interleaved (tile b is a matrix-core tile
+// when floor(b * Lm / (Lv + Lm)) steps up at b), so the vector tiles' unpack
+// and FMA work and the matrix-core tiles' MFMA work share every CU; tiles past
+// the live count exit at once. Two kernels would run one after the other on
+// the stream, each with its own ramp and tail. Plain dispatch order spreads
+// the live tiles over all 8 XCDs.
+template <bool STAGED>
+__global__ __launch_bounds__(kThreads) void moe_expert_mixed_kernel(ExpertArgs a, ExpertArgs am) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int pv = a.nmat * a.C * a.S;
+  const int pm = am.nmat * am.C * am.S;
+  const int Lv = *a.n_items * pv;
+  const int Lm = *am.n_items * pm;
+  const int total = Lv + Lm;
+  const int b = blockIdx.x;
+  if (b >= total) return;
+  const int m0 = (int)((long long)b * Lm / total);
+  const int m1 = (int)((long long)(b + 1) * Lm / total);
+  if (m1 > m0) {
+    const int item = m0 / pm;
+    const ItemRec it = am.items[item];
+    mfma_item_tile(am, it, m0 - item * pm, smem);
+  } else {
+    const int v = b - m0;
+    const int item = v / pv;
+    const ItemRec it = a.items[item];
+    vector_item_tile<kMaxChunk, STAGED>(a, it, v - item * pv, smem);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -460,29 +497,44 @@ void plan_tiles(int K, int NB, int kt_target, int& C, int& Kt, int& S) {
   S = (K + Kt - 1) / Kt;
 }
 
+// LDS of the vector tiles for items of up to MC pairs (activation tile or
+// weight staging, then the phase sums).
 template <int MC>
-hipError_t launch_expert(const ExpertArgs& a, int max_items, bool staged, hipStream_t st) {
+int vector_lds_bytes(int Kt, bool staged) {
   constexpr int P = kThreads / (kJt * kLPB);
   const int rf = 4 * phase_lds_floats<MC, kLPB>();
+  const int t = staged ? staged_lds_bytes<MC, kLPB, kStagedRB, kJt, kStagedBufs>(Kt)
+                       : 4 * tile_x_floats<MC>(Kt, P, kMaxRB);  // every item size M <= MC
+  return t > rf ? t : rf;
+}
+
+// LDS of the matrix-core tiles: the activation tile, then the phase sums.
+int mfma_item_lds_bytes(int Kt) {
+  const int xs = mfma_xs_bytes<2, kMfmaJW, kMfmaNW>(Kt);
+  const int sc = 4 * kMfmaScratchFloats;
+  return xs > sc ? xs : sc;
+}
+
+hipError_t launch_expert_single(const ExpertArgs& a, int max_items, bool staged, hipStream_t st) {
   const dim3 grid(max_items * a.nmat * a.C * a.S);
-  if (staged) {
-    const int sb = staged_lds_bytes<MC, kLPB, kStagedRB, kJt, kStagedBufs>(a.Kt);  // every M <= MC
-    hipLaunchKernelGGL((moe_expert_kernel<MC, true>), grid, dim3(kThreads), sb > rf ? sb : rf,
-                       st, a);
-  } else {
-    const int xf = 4 * tile_x_floats<MC>(a.Kt, P, kMaxRB);  // covers every item size M <= MC
-    hipLaunchKernelGGL((moe_expert_kernel<MC, false>), grid, dim3(kThreads), xf > rf ? xf : rf,
-                       st, a);
-  }
+  const int lds = vector_lds_bytes<1>(a.Kt, staged);
+  if (staged)
+    hipLaunchKernelGGL((moe_expert_kernel<true>), grid, dim3(kThreads), lds, st, a);
+  else
+    hipLaunchKernelGGL((moe_expert_kernel<false>), grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_expert_mfma(const ExpertArgs& a, int max_items, hipStream_t st) {
-  if (max_items == 0) return hipSuccess;
-  const int xs = mfma_xs_bytes<2, kMfmaJW, kMfmaNW>(a.Kt);
-  const int sc = 4 * kMfmaScratchFloats;
-  const dim3 grid(max_items * a.nmat * a.C * a.S);
-  hipLaunchKernelGGL(moe_expert_mfma_kernel, grid, dim3(kThreads), xs > sc ? xs : sc, st, a);
+hipError_t launch_expert_mixed(const ExpertArgs& a, const ExpertArgs& am, int max_items,
+                               int max_mitems, bool staged, hipStream_t st) {
+  const dim3 grid(max_items * a.nmat * a.C * a.S + max_mitems * am.nmat * am.C * am.S);
+  const int lv = vector_lds_bytes<kMaxChunk>(a.Kt, staged);
+  const int lm = max_mitems > 0 ? mfma_item_lds_bytes(am.Kt) : 0;
+  const int lds = lv > lm ? lv : lm;
+  if (staged)
+    hipLaunchKernelGGL((moe_expert_mixed_kernel<true>), grid, dim3(kThreads), lds, st, a, am);
+  else
+    hipLaunchKernelGGL((moe_expert_mixed_kernel<false>), grid, dim3(kThreads), lds, st, a, am);
   return hipGetLastError();
 }
 
@@ -583,14 +635,12 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   g.ids = ids;
   g.E = p.E;
   g.act = ActSource{nullptr, 0, 0, 0};
-  err = (p.MC == 1) ? launch_expert<1>(g, p.max_items, staged_gu, st)
-                    : launch_expert<kMaxChunk>(g, p.max_items, staged_gu, st);
-  if (err != hipSuccess) return err;
   ExpertArgs gm = g;
   gm.items = mitems;
   gm.n_items = n_mitems;
   gm.C = p.gu_Cm;
-  err = launch_expert_mfma(gm, p.max_mitems, st);
+  err = (p.MC == 1) ? launch_expert_single(g, p.max_items, staged_gu, st)
+                    : launch_expert_mixed(g, gm, p.max_items, p.max_mitems, staged_gu, st);
   if (err != hipSuccess) return err;
 
   const size_t nh = (size_t)npairs * p.I;
@@ -624,14 +674,12 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   if (fuse_act)
     d.act = ActSource{gu_part, (uint32_t)(2 * (size_t)p.gu_S * nh * sizeof(float)), (uint32_t)nh,
                       p.gu_S};
-  err = (p.MC == 1) ? launch_expert<1>(d, p.max_items, staged_dn, st)
-                    : launch_expert<kMaxChunk>(d, p.max_items, staged_dn, st);
-  if (err != hipSuccess) return err;
   ExpertArgs dm = d;
   dm.items = mitems;
   dm.n_items = n_mitems;
   dm.C = p.dn_Cm;
-  err = launch_expert_mfma(dm, p.max_mitems, st);
+  err = (p.MC == 1) ? launch_expert_single(d, p.max_items, staged_dn, st)
+                    : launch_expert_mixed(d, dm, p.max_items, p.max_mitems, staged_dn, st);
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;

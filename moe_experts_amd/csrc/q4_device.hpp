@@ -285,7 +285,6 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
   constexpr int kLoadsPerBatch = 2 * RB;  // scale + nibble load per row
   static_assert(2 * kLoadsPerBatch < 64, "vmcnt range");
   const int t = threadIdx.x;
-  const int wave = t / kWaveSize;
   const int r = t / g.Lr;
   const int v = t - r * g.Lr;
   const int jj = v / LPB;
