@@ -9,7 +9,8 @@ definition from the "2000-line C++ DeepSeek inference engine" article (§2.2
 block_q4_0 / dequantize, §3.2 loop order, §3.4 fused matmul_q4_0) evaluated in
 double precision, plus the routed-expert MoE composition of the KTransformers
 DeepSeek-V2 tutorial ("Optimization 3": top-6 of 160 routed experts as batched
-GEMVs). See ``q4_oracle.h`` for the exact contract of each function.
+GEMVs; the gate's top-k ids and weights, and the shared experts every token
+uses). See ``q4_oracle.h`` for the exact contract of each function.
 """
 from __future__ import annotations
 
@@ -59,6 +60,10 @@ def _load():
     lib.oracle_q4_0_matmul_f16.argtypes = [P, P, i32, i32, i32, P, P]
     lib.oracle_moe_decode.restype = i32
     lib.oracle_moe_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P]
+    lib.oracle_router_logits.restype = i32
+    lib.oracle_router_logits.argtypes = [P, P, i32, i32, i32, P, P]
+    lib.oracle_router_topk.restype = i32
+    lib.oracle_router_topk.argtypes = [P, i32, i32, i32, i32, P, P]
     _lib = lib
     return lib
 
@@ -142,3 +147,31 @@ def moe_decode(x, Wg, Wu, Wd, ids, w, H: int, I: int, E: int, with_bound: bool =
     if rc != 0:
         raise ValueError("oracle_moe_decode: bad arguments")
     return out, bnd, h
+
+
+def router_logits(x, Wr, with_bound: bool = True):
+    """Router logits [T, E] = x [T, H] . Wr[E, H]^T in double, rounded to float32."""
+    Wr = np.ascontiguousarray(Wr, dtype=np.float32)
+    E, H = Wr.shape
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, H)
+    T = x.shape[0]
+    lg = np.empty((T, E), dtype=np.float32)
+    bnd = np.empty((T, E), dtype=np.float64) if with_bound else None
+    rc = _load().oracle_router_logits(_ptr(x), _ptr(Wr), T, H, E, _ptr(lg), _ptr(bnd))
+    if rc != 0:
+        raise ValueError("oracle_router_logits: bad arguments")
+    return lg, bnd
+
+
+def router_topk(logits, topk: int, n_shared: int = 0):
+    """Top-k ids (largest first, ties to the lower index, NaN never chosen) and
+    softmax weights over them; n_shared shared-expert slots appended (id E + s,
+    weight 1). Returns (ids int32 [T, topk + n_shared], w float32 [T, topk + n_shared])."""
+    lg = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = lg.shape
+    ids = np.empty((T, topk + n_shared), dtype=np.int32)
+    w = np.empty((T, topk + n_shared), dtype=np.float32)
+    rc = _load().oracle_router_topk(_ptr(lg), T, E, topk, n_shared, _ptr(ids), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_router_topk: bad arguments")
+    return ids, w

@@ -182,4 +182,60 @@ int oracle_moe_decode(const float* x, const uint8_t* Wg, const uint8_t* Wu,
   return 0;
 }
 
+int oracle_router_logits(const float* x, const float* Wr, int T, int H, int E,
+                         float* logits, double* bound) {
+  if (x == nullptr || Wr == nullptr || logits == nullptr || T < 1 || H < 1 || E < 1)
+    return -1;
+  for (int t = 0; t < T; ++t)
+    for (int e = 0; e < E; ++e) {
+      double acc = 0.0, b = 0.0;
+      for (int h = 0; h < H; ++h) {
+        const double p = (double)x[(size_t)t * H + h] * (double)Wr[(size_t)e * H + h];
+        acc += p;
+        b += std::fabs(p);
+      }
+      logits[(size_t)t * E + e] = (float)acc;
+      if (bound) bound[(size_t)t * E + e] = b;
+    }
+  return 0;
+}
+
+int oracle_router_topk(const float* logits, int T, int E, int topk, int n_shared,
+                       int32_t* ids, float* w) {
+  if (logits == nullptr || ids == nullptr || w == nullptr || T < 1 || E < 1 || topk < 1 ||
+      topk > E || n_shared < 0)
+    return -1;
+  const int slots = topk + n_shared;
+  std::vector<char> taken(E);
+  std::vector<double> ex(topk);
+  for (int t = 0; t < T; ++t) {
+    const float* lg = logits + (size_t)t * E;
+    int32_t* id = ids + (size_t)t * slots;
+    float* wt = w + (size_t)t * slots;
+    for (int e = 0; e < E; ++e) taken[e] = 0;
+    // selection: repeatedly the largest remaining logit, lower index on ties
+    for (int j = 0; j < topk; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e] || std::isnan(lg[e])) continue;
+        if (best < 0 || lg[e] > lg[best]) best = e;
+      }
+      id[j] = best;
+      if (best >= 0) taken[best] = 1;
+    }
+    // softmax over the chosen logits; the first chosen one is their maximum
+    double sum = 0.0;
+    for (int j = 0; j < topk; ++j) {
+      ex[j] = id[j] >= 0 ? std::exp((double)lg[id[j]] - (double)lg[id[0]]) : 0.0;
+      sum += ex[j];
+    }
+    for (int j = 0; j < topk; ++j) wt[j] = id[j] >= 0 ? (float)(ex[j] / sum) : 0.0f;
+    for (int s = 0; s < n_shared; ++s) {
+      id[topk + s] = E + s;
+      wt[topk + s] = 1.0f;
+    }
+  }
+  return 0;
+}
+
 }  // extern "C"

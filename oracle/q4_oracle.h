@@ -24,7 +24,9 @@
  *    (www.mhpn.cn/news/2178346), section "Optimization 3" (arithmetic-intensity
  *    offload): routed experts of DeepSeek-V2, top-6 of 160, run as a set of
  *    batched GEMVs; the MoE module's gate yields top-k ids and weights that the
- *    experts consume.
+ *    experts consume; the shared experts are used by every token (kept in GPU
+ *    memory for that reason). Its YAML-injection section: the KDeepseekV2MoE
+ *    forward first runs the gate for each token's top-k ids and weights.
  *
  * Parity pins: every function here is pinned by tests that do not reuse its
  * code (hand-worked blocks, IEEE bit patterns checked against numpy's float16,
@@ -77,6 +79,24 @@ int oracle_moe_decode(const float* x, const uint8_t* Wg, const uint8_t* Wu,
                       const uint8_t* Wd, const int32_t* ids, const float* w,
                       int T, int H, int I, int E, int topk, float* out,
                       double* bound, double* h_out);
+
+/* MoE router (the gate in front of the routed experts):
+ *   logits[t][e] = sum_h x[t][h] * Wr[e][h]
+ * accumulated in double in h order and rounded once to float. Wr holds one row
+ * of H floats per routed expert (E rows). bound[t][e] (optional) receives
+ * sum_h |x[t][h] * Wr[e][h]| in double. */
+int oracle_router_logits(const float* x, const float* Wr, int T, int H, int E,
+                         float* logits, double* bound);
+
+/* Top-k routing of float logits [T][E]. Per token: the topk largest logits,
+ * largest first; equal logits go to the lower expert index; a NaN logit is
+ * never chosen, and a slot that finds no candidate gets id -1 and weight 0.
+ * The weights are the softmax over the chosen logits, computed in double with
+ * their maximum subtracted and rounded to float. n_shared shared experts
+ * follow the routed slots: slot topk + s holds id E + s with weight 1.
+ * ids and w are [T][topk + n_shared]. */
+int oracle_router_topk(const float* logits, int T, int E, int topk, int n_shared,
+                       int32_t* ids, float* w);
 
 #ifdef __cplusplus
 }

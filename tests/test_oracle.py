@@ -334,3 +334,61 @@ def test_generator_layout_and_ranges():
     assert counts.min() > 0.9 * nib.size / 16
     # deterministic from the seed
     assert (datagen.q4_0_random(1201, 64, 4096) == B).all()
+
+
+# --------------------------------------------------------------------------
+# Router: logits, top-k selection, softmax weights, shared-expert slots
+# --------------------------------------------------------------------------
+
+def test_router_logits_integer_exact_and_random():
+    g = np.random.Generator(np.random.PCG64(71))
+    # integer data: every partial sum is an integer below 2^24, so the double
+    # sum is exact and must equal numpy's integer matmul bitwise
+    x = g.integers(-4, 5, size=(3, 96)).astype(np.float32)
+    Wr = g.integers(-7, 8, size=(10, 96)).astype(np.float32)
+    lg, bnd = oracle.router_logits(x, Wr)
+    ref = x.astype(np.int64) @ Wr.astype(np.int64).T
+    assert (lg == ref.astype(np.float32)).all()
+    xa, wa = np.abs(x.astype(np.int64)), np.abs(Wr.astype(np.int64))
+    assert (bnd == (xa[:, None, :] * wa[None]).sum(-1)).all()
+    # random data: within a few float ulps of numpy's float64 product
+    x = g.standard_normal((5, 640)).astype(np.float32)
+    Wr = (g.standard_normal((33, 640)) / np.sqrt(640)).astype(np.float32)
+    lg, bnd = oracle.router_logits(x, Wr)
+    ref = x.astype(np.float64) @ Wr.astype(np.float64).T
+    assert np.all(np.abs(lg - ref) <= 1e-7 * bnd + 1e-30)
+
+
+def test_router_topk_handworked():
+    lg = np.array([[1.0, 3.0, 3.0, 2.0],            # tie: lower index first
+                   [0.0, math.log(3.0), -5.0, -5.0],  # weights 3/4 and 1/4
+                   [np.nan, 1.0, np.nan, np.nan],      # one candidate only
+                   [np.nan, np.nan, np.nan, np.nan]],  # none
+                  dtype=np.float32)
+    ids, w = oracle.router_topk(lg, 2, n_shared=1)
+    assert ids.tolist() == [[1, 2, 4], [1, 0, 4], [1, -1, 4], [-1, -1, 4]]
+    assert w[0, :2].tolist() == [0.5, 0.5]
+    assert abs(w[1, 0] - 0.75) <= 1e-7 and abs(w[1, 1] - 0.25) <= 1e-7
+    assert w[2, :2].tolist() == [1.0, 0.0] and w[3, :2].tolist() == [0.0, 0.0]
+    assert (w[:, 2] == 1.0).all()
+    # -inf logits are still candidates (lower index first among equals)
+    ids, w = oracle.router_topk(np.array([[-np.inf, 0.0, -np.inf]], np.float32), 2)
+    assert ids.tolist() == [[1, 0]] and w.tolist() == [[1.0, 0.0]]
+
+
+def test_router_topk_matches_stable_argsort_and_shift_invariance():
+    g = np.random.Generator(np.random.PCG64(72))
+    lg = g.standard_normal((40, 160)).astype(np.float32)
+    lg[:4, 10:20] = 0.25          # rows with many equal logits
+    ids, w = oracle.router_topk(lg, 6, n_shared=2)
+    ref_ids, ref_w = datagen.topk_softmax(lg, 6)   # numpy stable argsort, float64 softmax
+    assert (ids[:, :6] == ref_ids).all()
+    assert np.all(np.abs(w[:, :6] - ref_w) <= 1e-7 * ref_w)
+    assert (ids[:, 6:] == np.array([160, 161])).all() and (w[:, 6:] == 1.0).all()
+    assert np.all(np.abs(w[:, :6].astype(np.float64).sum(1) - 1.0) <= 1e-6)
+    assert (np.diff(np.take_along_axis(lg, ids[:, :6], 1), axis=1) <= 0).all()
+    # on a grid of 2^-10 adding 1 to every logit is exact and changes nothing
+    lq = (np.round(lg * 1024) / 1024).astype(np.float32)
+    ids1, w1 = oracle.router_topk(lq, 6, n_shared=2)
+    ids2, w2 = oracle.router_topk(lq + np.float32(1.0), 6, n_shared=2)
+    assert (ids2 == ids1).all() and (w2 == w1).all()
