@@ -58,7 +58,8 @@ typedef enum q4_status {
   Q4_OK = 0,
   Q4_EINVAL = -1,      /* null pointer or non-positive dimension */
   Q4_ESHAPE = -2,      /* N/H/I not a multiple of 32, or M/T/topk/E out of range */
-  Q4_EALIGN = -3,      /* pointer misaligned (blocks 2 B, fp32/fp16 arrays 4 B, ws 256 B) */
+  Q4_EALIGN = -3,      /* pointer misaligned (blocks 2 B, fp32/fp16 arrays 4 B, router x and
+                          Wr 16 B, ws 256 B) */
   Q4_EWORKSPACE = -4,  /* workspace missing or smaller than required */
   Q4_EHIP = -5,        /* the HIP runtime reported an error at launch */
   Q4_ETOOBIG = -6      /* a size exceeds the limits of the implementation */
@@ -127,6 +128,53 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
                     const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
                     float* out, int T, int H, int I, int E, int topk, void* ws,
                     size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * MoE router: the gate in front of moe_q4_0_decode, on the device. The
+ * KTransformers tutorial's YAML-injection section has the KDeepseekV2MoE
+ * forward run the gate first for each token's top-k ids and weights;
+ * "Optimization 3" keeps the shared experts, which every token uses, on the GPU.
+ *   logits[t][e] = sum_h x[t][h] * Wr[e][h]   (fp32 products and sums)
+ *   topk_ids[t][j], j < topk: the topk largest logits, largest first; equal
+ *     logits go to the lower expert index; a NaN logit is never chosen, and a
+ *     slot that finds no candidate gets id -1 (moe_q4_0_decode adds nothing
+ *     for it) and weight 0;
+ *   topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the chosen
+ *     logits l_0 >= l_1 >= ... (softmax over the chosen ones only);
+ *   slots topk .. topk + n_shared - 1: id E + s and weight 1, the shared
+ *     experts, stored after the E routed experts in the decode's weights.
+ *   x        fp32 [T][H], 16-byte aligned    Wr  fp32 [E][H] (one row per
+ *            routed expert), 16-byte aligned
+ *   logits   fp32 [T][E], overwritten        topk_ids int32, topk_w fp32
+ *            [T][topk + n_shared], overwritten; all 4-byte aligned
+ *   1 <= T <= Q4_MOE_MAX_T, 1 <= E <= Q4_MOE_MAX_E, 1 <= topk <= E,
+ *   0 <= n_shared, topk + n_shared <= Q4_MOE_MAX_TOPK, H >= 4, H % 4 == 0.
+ *   ws/ws_bytes: workspace of moe_router_workspace_bytes(T, H, E) bytes
+ *   (K-split partial logits).
+ * The outputs feed moe_q4_0_decode(..., E + n_shared experts, topk + n_shared
+ * slots) on the same stream with no host round trip.
+ * ------------------------------------------------------------------------- */
+size_t moe_router_workspace_bytes(int T, int H, int E);
+int moe_router_topk(const float* x, const float* Wr, float* logits, int32_t* topk_ids,
+                    float* topk_w, int T, int H, int E, int topk, int n_shared, void* ws,
+                    size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Whole MoE layer at decode: moe_router_topk, then moe_q4_0_decode over the
+ * routed and shared experts, on one stream:
+ *   out[t] = sum_{j < topk} w_j * FFN_{e_j}(x_t) + sum_{s < n_shared} FFN_{E+s}(x_t),
+ *   FFN_e(x) = Wd_e ( SiLU(x . Wg_e) * (x . Wu_e) ).
+ *   Wg, Wu, Wd  Q4_0 as in moe_q4_0_decode, E + n_shared consecutive matrices
+ *               (the E routed experts, then the shared ones)
+ *   Other arguments and limits as in moe_router_topk and moe_q4_0_decode
+ *   (H % 32 == 0, I % 32 == 0); E + n_shared <= Q4_MOE_MAX_E.
+ *   ws/ws_bytes: workspace of moe_q4_0_layer_workspace_bytes(...) bytes; the
+ *   router's logits, ids and weights are kept there.
+ * ------------------------------------------------------------------------- */
+size_t moe_q4_0_layer_workspace_bytes(int T, int H, int I, int E, int topk, int n_shared);
+int moe_q4_0_layer(const float* x, const float* Wr, const q4_0_block* Wg, const q4_0_block* Wu,
+                   const q4_0_block* Wd, float* out, int T, int H, int I, int E, int topk,
+                   int n_shared, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

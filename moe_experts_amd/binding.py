@@ -43,6 +43,14 @@ _lib.moe_q4_0_workspace_bytes.restype = _Z
 _lib.moe_q4_0_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.moe_q4_0_decode.restype = _I
 _lib.moe_q4_0_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
+_lib.moe_router_workspace_bytes.restype = _Z
+_lib.moe_router_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.moe_router_topk.restype = _I
+_lib.moe_router_topk.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
+_lib.moe_q4_0_layer_workspace_bytes.restype = _Z
+_lib.moe_q4_0_layer_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
+_lib.moe_q4_0_layer.restype = _I
+_lib.moe_q4_0_layer.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 
 BLOCK_BYTES = 18
 
@@ -170,4 +178,63 @@ def moe_q4_0_decode(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: tor
     pws, nws = (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8, ws.numel()), ws.numel())
     _check(_lib.moe_q4_0_decode(px, pg, pu, pd, pi, pw_, po, T, H, I, E, topk, pws, nws,
                                 _stream(x.device)))
+    return out
+
+
+def moe_router_workspace_bytes(T: int, H: int, E: int) -> int:
+    return int(_lib.moe_router_workspace_bytes(T, H, E))
+
+
+def moe_q4_0_layer_workspace_bytes(T: int, H: int, I: int, E: int, topk: int,
+                                   n_shared: int) -> int:
+    return int(_lib.moe_q4_0_layer_workspace_bytes(T, H, I, E, topk, n_shared))
+
+
+def _ws_arg(ws, need: int, device):
+    if ws is None:
+        ws = workspace(need, device)
+    return (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8, ws.numel()), ws.numel())
+
+
+def moe_router_topk(x: torch.Tensor, Wr: torch.Tensor, topk: int, n_shared: int = 0,
+                    ws: torch.Tensor | None = None):
+    """MoE router: x [T, H] fp32, Wr [E, H] fp32. Returns (logits [T, E],
+    topk_ids int32 [T, topk + n_shared], topk_w fp32 [T, topk + n_shared])."""
+    if x.dim() != 2 or Wr.dim() != 2:
+        raise ValueError("x must be [T, H] and Wr [E, H]")
+    T, H = x.shape
+    E = Wr.shape[0]
+    px = _dev(x, "x", torch.float32, T * H)
+    pr = _dev(Wr, "Wr", torch.float32, E * H)
+    slots = topk + n_shared
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, slots), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, slots), dtype=torch.float32, device=x.device)
+    pws, nws = _ws_arg(ws, moe_router_workspace_bytes(T, H, E), x.device)
+    _check(_lib.moe_router_topk(px, pr, logits.data_ptr(), ids.data_ptr(), w.data_ptr(), T, H, E,
+                                topk, n_shared, pws, nws, _stream(x.device)))
+    return logits, ids, w
+
+
+def moe_q4_0_layer(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor,
+                   Wd: torch.Tensor, I: int, topk: int, n_shared: int = 0,
+                   out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Router, then routed and shared experts: x [T, H] fp32, Wr [E, H] fp32, and
+    Wg/Wu/Wd holding E + n_shared Q4_0 expert matrices (routed, then shared)."""
+    if x.dim() != 2 or Wr.dim() != 2:
+        raise ValueError("x must be [T, H] and Wr [E, H]")
+    T, H = x.shape
+    E = Wr.shape[0]
+    mat = H * (I // 32) * BLOCK_BYTES
+    px = _dev(x, "x", torch.float32, T * H)
+    pr = _dev(Wr, "Wr", torch.float32, E * H)
+    pg = _dev(Wg, "Wg", torch.uint8, (E + n_shared) * mat)
+    pu = _dev(Wu, "Wu", torch.uint8, (E + n_shared) * mat)
+    pd = _dev(Wd, "Wd", torch.uint8, (E + n_shared) * mat)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    po = _dev(out, "out", torch.float32, T * H)
+    pws, nws = _ws_arg(ws, moe_q4_0_layer_workspace_bytes(T, H, I, E, topk, n_shared), x.device)
+    _check(_lib.moe_q4_0_layer(px, pr, pg, pu, pd, po, T, H, I, E, topk, n_shared, pws, nws,
+                               _stream(x.device)))
     return out

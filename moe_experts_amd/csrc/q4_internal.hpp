@@ -53,6 +53,12 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
                       const int32_t* ids, const float* w, float* out, void* ws,
                       const MoePlan& p, hipStream_t st);
 
+// ---- MoE router (router_moe.hip) ------------------------------------------
+// K-split partial logits: bytes of workspace for the router kernels
+size_t router_ws_bytes(int T, int H, int E);
+hipError_t launch_router(const float* x, const float* Wr, float* logits, int32_t* ids, float* w,
+                         int T, int H, int E, int topk, int n_shared, void* ws, hipStream_t st);
+
 // ---- prefill GEMM --------------------------------------------------------
 hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int N, int K,
                        hipStream_t st);

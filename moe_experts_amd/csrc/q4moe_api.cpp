@@ -43,6 +43,33 @@ int check_moe_shape(int T, int H, int I, int E, int topk) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
 
+int check_router_shape(int T, int H, int E, int topk, int n_shared) {
+  if (T <= 0 || H <= 0 || E <= 0 || topk <= 0 || n_shared < 0) return Q4_EINVAL;
+  if (H % 4 != 0 || T > Q4_MOE_MAX_T || E > Q4_MOE_MAX_E || topk > E ||
+      topk + n_shared > Q4_MOE_MAX_TOPK)
+    return Q4_ESHAPE;
+  if ((long long)E * H * 4 > kMaxBytes || (long long)T * H * 4 > kMaxBytes) return Q4_ETOOBIG;
+  return Q4_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// Layer workspace: router partials, logits, ids, weights, then the decode's.
+struct LayerWs {
+  size_t off_logits, off_ids, off_w, off_moe, bytes;
+};
+
+LayerWs layer_ws(int T, int H, int I, int E, int topk, int n_shared) {
+  const int slots = topk + n_shared;
+  LayerWs l;
+  l.off_logits = align256(q4::router_ws_bytes(T, H, E));
+  l.off_ids = l.off_logits + align256((size_t)T * E * sizeof(float));
+  l.off_w = l.off_ids + align256((size_t)T * slots * sizeof(int32_t));
+  l.off_moe = l.off_w + align256((size_t)T * slots * sizeof(float));
+  l.bytes = l.off_moe + q4::plan_moe(T, H, I, E + n_shared, slots).ws_bytes;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -52,7 +79,9 @@ const char* q4_strerror(int status) {
     case Q4_OK: return "success";
     case Q4_EINVAL: return "invalid argument: null pointer or non-positive dimension";
     case Q4_ESHAPE: return "unsupported shape: N/H/I must be multiples of 32, M/T/topk/E within limits";
-    case Q4_EALIGN: return "misaligned pointer (blocks 2 B, fp32/fp16 arrays 4 B, workspace 256 B)";
+    case Q4_EALIGN:
+      return "misaligned pointer (blocks 2 B, fp32/fp16 arrays 4 B, router x and Wr 16 B, "
+             "workspace 256 B)";
     case Q4_EWORKSPACE: return "workspace missing or too small";
     case Q4_EHIP: return "HIP runtime error at launch";
     case Q4_ETOOBIG: return "size exceeds implementation limits";
@@ -110,6 +139,63 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
                                  reinterpret_cast<const uint8_t*>(Wu),
                                  reinterpret_cast<const uint8_t*>(Wd), topk_ids, topk_w, out, ws,
                                  p, static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_router_workspace_bytes(int T, int H, int E) {
+  if (check_router_shape(T, H, E, 1, 0) != Q4_OK) return 0;
+  return q4::router_ws_bytes(T, H, E);
+}
+
+int moe_router_topk(const float* x, const float* Wr, float* logits, int32_t* topk_ids,
+                    float* topk_w, int T, int H, int E, int topk, int n_shared, void* ws,
+                    size_t ws_bytes, void* stream) {
+  if (!x || !Wr || !logits || !topk_ids || !topk_w) return Q4_EINVAL;
+  int rc = check_router_shape(T, H, E, topk, n_shared);
+  if (rc != Q4_OK) return rc;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(logits, 4) || !aligned(topk_ids, 4) ||
+      !aligned(topk_w, 4))
+    return Q4_EALIGN;
+  rc = check_ws(ws, ws_bytes, q4::router_ws_bytes(T, H, E));
+  if (rc != Q4_OK) return rc;
+  return from_hip(q4::launch_router(x, Wr, logits, topk_ids, topk_w, T, H, E, topk, n_shared, ws,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+size_t moe_q4_0_layer_workspace_bytes(int T, int H, int I, int E, int topk, int n_shared) {
+  if (check_router_shape(T, H, E, topk, n_shared) != Q4_OK ||
+      check_moe_shape(T, H, I, E + n_shared, topk + n_shared) != Q4_OK)
+    return 0;
+  return layer_ws(T, H, I, E, topk, n_shared).bytes;
+}
+
+int moe_q4_0_layer(const float* x, const float* Wr, const q4_0_block* Wg, const q4_0_block* Wu,
+                   const q4_0_block* Wd, float* out, int T, int H, int I, int E, int topk,
+                   int n_shared, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !Wr || !Wg || !Wu || !Wd || !out) return Q4_EINVAL;
+  int rc = check_router_shape(T, H, E, topk, n_shared);
+  if (rc != Q4_OK) return rc;
+  rc = check_moe_shape(T, H, I, E + n_shared, topk + n_shared);
+  if (rc != Q4_OK) return rc;
+  if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 4) || !aligned(Wg, 2) ||
+      !aligned(Wu, 2) || !aligned(Wd, 2))
+    return Q4_EALIGN;
+  const LayerWs l = layer_ws(T, H, I, E, topk, n_shared);
+  rc = check_ws(ws, ws_bytes, l.bytes);
+  if (rc != Q4_OK) return rc;
+  const int slots = topk + n_shared;
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  float* logits = reinterpret_cast<float*>(base + l.off_logits);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + l.off_ids);
+  float* w = reinterpret_cast<float*>(base + l.off_w);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t err =
+      q4::launch_router(x, Wr, logits, ids, w, T, H, E, topk, n_shared, ws, st);
+  if (err != hipSuccess) return Q4_EHIP;
+  const q4::MoePlan p = q4::plan_moe(T, H, I, E + n_shared, slots);
+  return from_hip(q4::launch_moe(x, reinterpret_cast<const uint8_t*>(Wg),
+                                 reinterpret_cast<const uint8_t*>(Wu),
+                                 reinterpret_cast<const uint8_t*>(Wd), ids, w, out,
+                                 base + l.off_moe, p, st));
 }
 
 }  // extern "C"

@@ -20,7 +20,10 @@ Workload recipe (mirrors the MoE decode and dense decode shapes of the pages:
   * router logits ~ N(0, 1) over E experts, optionally +bias on experts
     0..n_hot-1 (skewed routing); top-k by logit (ties to the lower index),
     softmax over the k selected logits in float64 after subtracting their max,
-    cast to float32.
+    cast to float32 (the decode-only configurations take this table as input);
+  * for the whole layer, router weights fp32 [E, H] ~ N(0, 1/H), so that the
+    router's logits of N(0, 1) activations are ~ N(0, 1) as above, and two
+    shared experts drawn like the routed ones.
 """
 from __future__ import annotations
 
@@ -127,6 +130,17 @@ def dense_x_seed(M: int) -> int:
 MOE_DSV2 = dict(H=5120, I=1536, E=160, topk=6)
 MOE_T1 = dict(T=1, x_seed=3101, logit_seed=3201)
 MOE_T32 = dict(T=32, x_seed=4101, logit_seed=4201, hot_bias=2.0, n_hot=8)
+
+
+#: whole layer: the same experts plus 2 shared experts of the routed experts'
+#: shape (stored as experts E, E + 1, seeds by expert_seed), and an fp32 router
+#: [E, H] ~ N(0, 1/H), so that the logits of x ~ N(0, 1) are ~ N(0, 1)
+MOE_LAYER = dict(n_shared=2, router_seed=3901)
+
+
+def router_weights(seed: int, E: int, H: int) -> np.ndarray:
+    """Router (gate) weights fp32 [E, H], N(0, 1/H)."""
+    return (rng(seed).standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)
 
 
 def expert_seed(e: int, m: int) -> int:

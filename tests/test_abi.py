@@ -27,6 +27,12 @@ def lib():
     L.moe_q4_0_decode.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, P, Z, P]
     L.moe_q4_0_workspace_bytes.restype = Z
     L.moe_q4_0_workspace_bytes.argtypes = [I, I, I, I, I]
+    L.moe_router_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, P, Z, P]
+    L.moe_router_workspace_bytes.restype = Z
+    L.moe_router_workspace_bytes.argtypes = [I, I, I]
+    L.moe_q4_0_layer.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    L.moe_q4_0_layer_workspace_bytes.restype = Z
+    L.moe_q4_0_layer_workspace_bytes.argtypes = [I, I, I, I, I, I]
     return L
 
 
@@ -40,7 +46,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("q4_0_gemv", "q4_0_gemm", "moe_q4_0_decode", "q4_0_gemv_workspace_bytes",
-              "moe_q4_0_workspace_bytes", "q4_strerror"):
+              "moe_q4_0_workspace_bytes", "moe_router_topk", "moe_router_workspace_bytes",
+              "moe_q4_0_layer", "moe_q4_0_layer_workspace_bytes", "q4_strerror"):
         assert n in names
 
 
@@ -113,3 +120,36 @@ def test_moe_rejects_bad_arguments(lib):
     assert f(*ok, 1, 5120, 1536, 160, 6, None, 0, None) == -4
     need = lib.moe_q4_0_workspace_bytes(1, 5120, 1536, 160, 6)
     assert f(*ok, 1, 5120, 1536, 160, 6, FAKE + 64, need, None) == -3
+
+
+def test_router_rejects_bad_arguments(lib):
+    f = lib.moe_router_topk
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert f(None, *ok[1:], 1, 5120, 160, 6, 2, None, 0, None) == -1
+    assert f(*ok, 0, 5120, 160, 6, 2, None, 0, None) == -1
+    assert f(*ok, 1, 5120, 160, 6, -1, None, 0, None) == -1
+    assert f(*ok, 65, 5120, 160, 6, 2, None, 0, None) == -2     # T > 64
+    assert f(*ok, 1, 5122, 160, 6, 2, None, 0, None) == -2     # H % 4
+    assert f(*ok, 1, 5120, 1025, 6, 2, None, 0, None) == -2    # E > 1024
+    assert f(*ok, 1, 5120, 5, 6, 0, None, 0, None) == -2       # topk > E
+    assert f(*ok, 1, 5120, 160, 6, 3, None, 0, None) == -2     # 9 slots
+    assert f(*ok, 1, 1 << 22, 160, 6, 2, None, 0, None) == -6  # router weights > 2 GiB
+    assert f(FAKE + 4, *ok[1:], 1, 5120, 160, 6, 2, None, 0, None) == -3  # x not 16-B aligned
+    assert f(*ok, 1, 5120, 160, 6, 2, None, 0, None) == -4
+    need = lib.moe_router_workspace_bytes(1, 5120, 160)
+    assert need > 0 and lib.moe_router_workspace_bytes(65, 5120, 160) == 0
+    assert f(*ok, 1, 5120, 160, 6, 2, FAKE + 64, need, None) == -3
+
+
+def test_layer_rejects_bad_arguments(lib):
+    f = lib.moe_q4_0_layer
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert f(None, *ok[1:], 1, 5120, 1536, 160, 6, 2, None, 0, None) == -1
+    assert f(*ok, 1, 5120, 1530, 160, 6, 2, None, 0, None) == -2     # I % 32
+    assert f(*ok, 1, 5120, 1536, 1023, 6, 2, None, 0, None) == -2    # E + n_shared > 1024
+    assert f(*ok, 1, 5120, 1536, 160, 7, 2, None, 0, None) == -2     # 9 slots
+    assert f(*ok, 1, 5120, 1536, 160, 6, 2, None, 0, None) == -4
+    need = lib.moe_q4_0_layer_workspace_bytes(32, 5120, 1536, 160, 6, 2)
+    assert need > lib.moe_q4_0_workspace_bytes(32, 5120, 1536, 162, 8)
+    assert lib.moe_q4_0_layer_workspace_bytes(32, 5120, 1536, 1023, 6, 2) == 0
+    assert f(*ok, 32, 5120, 1536, 160, 6, 2, FAKE + 64, need, None) == -3
