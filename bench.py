@@ -393,15 +393,17 @@ def datagen_x(M, K):
 # ---------------------------------------------------------------------------
 def bench_moe(torch, dev, steps, warmup):
     from moe_experts_amd import datagen, moe_q4_0_decode, moe_q4_0_workspace_bytes
-    c = datagen.MOE_DSV2
+    c, L = datagen.MOE_DSV2, datagen.MOE_LAYER
     H, I, E, topk = c["H"], c["I"], c["E"], c["topk"]
-    log("[moe] generating 160 experts (2.1 GB)")
-    Wg, Wu, Wd = datagen.moe_experts(H, I, E)
+    Es = E + L["n_shared"]
+    log(f"[moe] generating {Es} experts ({E} routed, {L['n_shared']} shared; 2.15 GB)")
+    Wg, Wu, Wd = datagen.moe_experts(H, I, Es)
     layers = 4  # distinct copies of the layer, visited round robin (>8 GB)
     dW = [(torch.from_numpy(Wg).to(dev), torch.from_numpy(Wu).to(dev), torch.from_numpy(Wd).to(dev))]
     for _ in range(layers - 1):
         dW.append(tuple(w.clone() for w in dW[0]))
     del Wg, Wu, Wd
+    routed = [tuple(w[:E] for w in ws) for ws in dW]  # the decode alone: routed experts only
     mat = H * (I // 32) * 18
     res = {}
     for label, T, bias, xseed, lseed in (("t1", 1, 0.0, datagen.MOE_T1["x_seed"], datagen.MOE_T1["logit_seed"]),
@@ -419,7 +421,7 @@ def bench_moe(torch, dev, steps, warmup):
         ws = torch.zeros(moe_q4_0_workspace_bytes(T, H, I, E, topk), dtype=torch.uint8, device=dev)
 
         def call(r):
-            g, u, dd = dW[r % layers]
+            g, u, dd = routed[r % layers]
             ids, w = routes[r % len(routes)]
             moe_q4_0_decode(x, g, u, dd, ids, w, I, E, out=out, ws=ws)
 
@@ -434,6 +436,49 @@ def bench_moe(torch, dev, steps, warmup):
         res[label] = {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 2),
                       "GBps": round(b / dt / 1e9, 1), "hbm_frac": round(b / dt / 1e9 / HBM_PEAK_GBS, 4),
                       "unique_experts": round(float(U), 2)}
+        log(f"[moe] {label}: {res[label]}")
+    res.update(bench_moe_layer(torch, dev, steps, warmup, dW))
+    return res
+
+
+def bench_moe_layer(torch, dev, steps, warmup, dW):
+    """Whole layer (moe_q4_0_layer): the on-device router, then the routed and
+    shared experts. The routing comes from the router, so each call's x differs
+    (16 seeds) and the unique experts are counted from the router's own ids."""
+    from moe_experts_amd import (datagen, moe_q4_0_layer, moe_q4_0_layer_workspace_bytes,
+                                 moe_router_topk)
+    c, L = datagen.MOE_DSV2, datagen.MOE_LAYER
+    H, I, E, topk, ns = c["H"], c["I"], c["E"], c["topk"], L["n_shared"]
+    layers = len(dW)
+    Wr0 = torch.from_numpy(datagen.router_weights(L["router_seed"], E, H)).to(dev)
+    Wr = [Wr0] + [Wr0.clone() for _ in range(layers - 1)]  # one router per layer copy
+    mat = H * (I // 32) * 18
+    res = {}
+    for label, T, xseed in (("layer_t1", 1, datagen.MOE_T1["x_seed"]),
+                            ("layer_t32", 32, datagen.MOE_T32["x_seed"])):
+        xs = [torch.from_numpy(datagen.activations(xseed + 1000 * r, T, H)).to(dev)
+              for r in range(16)]
+        uniq = []
+        for x in xs:
+            ids = moe_router_topk(x, Wr0, topk, ns)[1].cpu().numpy()
+            uniq.append(len(np.unique(ids[:, :topk][ids[:, :topk] >= 0])) + ns)
+        out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        ws = torch.zeros(moe_q4_0_layer_workspace_bytes(T, H, I, E, topk, ns), dtype=torch.uint8,
+                         device=dev)
+
+        def call(r):
+            g, u, dd = dW[r % layers]
+            moe_q4_0_layer(xs[r % 16], Wr[r % layers], g, u, dd, I, topk, ns, out=out, ws=ws)
+
+        for r in range(warmup):
+            call(r)
+        graphs = [capture(torch, lambda r=r: call(r)) for r in range(16)]
+        dt = time_graph(torch, graphs, max(steps, 16), 1)
+        U = float(np.mean(uniq))
+        b = U * 3 * mat + E * H * 4 + 2 * 4 * T * H
+        res[label] = {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 2),
+                      "GBps": round(b / dt / 1e9, 1), "hbm_frac": round(b / dt / 1e9 / HBM_PEAK_GBS, 4),
+                      "unique_experts_incl_shared": round(U, 2)}
         log(f"[moe] {label}: {res[label]}")
     return res
 

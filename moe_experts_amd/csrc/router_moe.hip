@@ -9,11 +9,12 @@
 // top-k choice and the softmax over the chosen logits.
 //
 //   1. router_logits_kernel: workgroup (g, s) owns experts 16g .. 16g+15 and
-//      the K chunk [256 s, 256 s + 256). It stages the chunk of every token's
-//      activations in LDS; a wave takes 4 experts, its lanes the tokens (one
-//      token per lane), and the 4 experts' weights are wave-uniform operands
-//      (scalar loads). Each lane forms its 4 dot products over the chunk in k
-//      order and writes them as K-split partials, part[t][e][s]; the split
+//      the K chunk [256 s, 256 s + 256). It stages that chunk of its 16 router
+//      rows and of every token's activations in LDS (all loads in flight at
+//      once); a wave takes 4 experts, its lanes the tokens (one token per
+//      lane), and reads the 4 rows as LDS broadcasts. Each lane forms its 4
+//      dot products over the chunk in k order and writes them as K-split
+//      partials, part[t][e][s]; the split
 //      count is padded to a multiple of 4 by chunks past H, which write zeros.
 //   2. router_topk_kernel: one workgroup per token. A thread per expert sums
 //      its partials in split order (contiguous, four per load) into the logit,
@@ -39,13 +40,25 @@ static_assert(Q4_MOE_MAX_T <= kWaveSize, "one lane per token");
 __global__ __launch_bounds__(kRouterWaves * kWaveSize) void router_logits_kernel(
     const float* __restrict__ x, const float* __restrict__ Wr, float* __restrict__ part, int T,
     int H, int E) {
-  extern __shared__ float4 xs[];  // [T][kRouterPitch]
+  extern __shared__ float4 lds[];
+  float4* ws = lds;                          // [kRouterEG][kRouterKc / 4] router rows
+  float4* xs = lds + kRouterEG * (kRouterKc / 4);  // [T][kRouterPitch] activations
   const int g = blockIdx.x;
   const int s = blockIdx.y;
   const int Sp = gridDim.y;
   const int k0 = s * kRouterKc;
   const int n4 = max(0, min(kRouterKc, H - k0) / 4);  // float4 of this chunk (H % 4 == 0)
-  for (int i = threadIdx.x; i < T * (kRouterKc / 4); i += kRouterWaves * kWaveSize) {
+  constexpr int kThr = kRouterWaves * kWaveSize;
+  // one round trip: the chunk of the workgroup's router rows and of every
+  // token's activations (zeros past the chunk or past E)
+  for (int i = threadIdx.x; i < kRouterEG * (kRouterKc / 4); i += kThr) {
+    const int r = i / (kRouterKc / 4);
+    const int c = i - r * (kRouterKc / 4);
+    const int e = g * kRouterEG + r;
+    ws[i] = (c < n4 && e < E) ? *reinterpret_cast<const float4*>(Wr + (size_t)e * H + k0 + 4 * c)
+                              : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  }
+  for (int i = threadIdx.x; i < T * (kRouterKc / 4); i += kThr) {
     const int t = i / (kRouterKc / 4);
     const int c = i - t * (kRouterKc / 4);
     xs[t * kRouterPitch + c] = c < n4
@@ -54,20 +67,18 @@ __global__ __launch_bounds__(kRouterWaves * kWaveSize) void router_logits_kernel
   }
   __syncthreads();
   const int lane = threadIdx.x % kWaveSize;
-  const int e0 = __builtin_amdgcn_readfirstlane(g * kRouterEG + (threadIdx.x / kWaveSize) * kRouterEW);
+  const int r0 = (threadIdx.x / kWaveSize) * kRouterEW;  // this wave's first row
+  const int e0 = g * kRouterEG + r0;
   if (e0 >= E) return;
-  // rows past E repeat the last one (loaded, never stored)
-  const float* w[kRouterEW];
-#pragma unroll
-  for (int j = 0; j < kRouterEW; ++j) w[j] = Wr + (size_t)min(e0 + j, E - 1) * H + k0;
   const float4* xr = xs + min(lane, T - 1) * kRouterPitch;
+  const float4* wr = ws + r0 * (kRouterKc / 4);
   float acc[kRouterEW] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 4
   for (int c = 0; c < n4; ++c) {
     const float4 v = xr[c];
 #pragma unroll
     for (int j = 0; j < kRouterEW; ++j) {
-      const float4 r = *reinterpret_cast<const float4*>(w[j] + 4 * c);
+      const float4 r = wr[j * (kRouterKc / 4) + c];  // same address in every lane
       acc[j] = __builtin_fmaf(v.x, r.x, acc[j]);
       acc[j] = __builtin_fmaf(v.y, r.y, acc[j]);
       acc[j] = __builtin_fmaf(v.z, r.z, acc[j]);
@@ -98,7 +109,7 @@ __global__ __launch_bounds__(kTopkThreads) void router_topk_kernel(
   for (int e = threadIdx.x; e < E; e += kTopkThreads) {
     const float4* p = reinterpret_cast<const float4*>(part + ((size_t)t * E + e) * Sp);
     float l = 0.0f;
-#pragma unroll 8
+#pragma unroll 16
     for (int c = 0; c < Sp / 4; ++c) {
       const float4 q = p[c];
       l += q.x;
@@ -188,7 +199,8 @@ hipError_t launch_router(const float* x, const float* Wr, float* logits, int32_t
   float* part = static_cast<float*>(ws);
   const int Sp = router_splits(H);
   const dim3 grid((E + kRouterEG - 1) / kRouterEG, Sp);
-  const size_t lds = (size_t)T * kRouterPitch * sizeof(float4);
+  const size_t lds = ((size_t)kRouterEG * (kRouterKc / 4) + (size_t)T * kRouterPitch) *
+                     sizeof(float4);
   hipLaunchKernelGGL(router_logits_kernel, grid, dim3(kRouterWaves * kWaveSize), lds, st, x, Wr,
                      part, T, H, E);
   hipError_t err = hipGetLastError();
