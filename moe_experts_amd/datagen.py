@@ -57,6 +57,30 @@ def q4_0_random(seed: int, K: int, N: int, d_lo: float = 0.001, d_hi: float = 0.
     return assemble(d.view(np.uint16), qs)
 
 
+Q8_BLOCK_BYTES = 34
+
+
+def q8_0_random(seed: int, K: int, N: int, d_lo: float = 0.001, d_hi: float = 0.02) -> np.ndarray:
+    """Q8_0 matrix [K, N/32, 34] (uint8 bytes): binary16 scale then 32 signed
+    bytes per block; the signed bytes uniform on -128..127, scales as for Q4_0."""
+    assert N % BLOCK_WEIGHTS == 0
+    g = rng(seed)
+    q = g.integers(0, 256, size=(K, N // BLOCK_WEIGHTS, BLOCK_WEIGHTS), dtype=np.uint8)
+    d = g.uniform(d_lo, d_hi, size=(K, N // BLOCK_WEIGHTS)).astype(np.float16).view(np.uint16)
+    return assemble_q8(d, q)
+
+
+def assemble_q8(d_bits: np.ndarray, q: np.ndarray) -> np.ndarray:
+    """Pack scale bits [..] and signed-byte weights [.., 32] (any 8-bit dtype)
+    into Q8_0 blocks [.., 34]."""
+    d_bits = np.asarray(d_bits, dtype=np.uint16)
+    out = np.empty(d_bits.shape + (Q8_BLOCK_BYTES,), dtype=np.uint8)
+    out[..., 0] = (d_bits & 0xFF).astype(np.uint8)
+    out[..., 1] = (d_bits >> 8).astype(np.uint8)
+    out[..., 2:] = np.asarray(q).view(np.uint8)
+    return out
+
+
 def assemble(d_bits: np.ndarray, qs: np.ndarray) -> np.ndarray:
     """Pack scale bit patterns [..., nb] and qs bytes [..., nb, 16] into [..., nb, 18]."""
     d_bits = np.asarray(d_bits, dtype=np.uint16)

@@ -60,6 +60,10 @@ def _load():
     lib.oracle_q4_0_matmul_f16.argtypes = [P, P, i32, i32, i32, P, P]
     lib.oracle_moe_decode.restype = i32
     lib.oracle_moe_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P, P, P]
+    lib.oracle_q8_0_dequant_block.restype = None
+    lib.oracle_q8_0_dequant_block.argtypes = [P, P]
+    lib.oracle_q8_0_matmul.restype = i32
+    lib.oracle_q8_0_matmul.argtypes = [P, P, i32, i32, i32, P, P]
     lib.oracle_router_logits.restype = i32
     lib.oracle_router_logits.argtypes = [P, P, i32, i32, i32, P, P]
     lib.oracle_router_topk.restype = i32
@@ -175,3 +179,25 @@ def router_topk(logits, topk: int, n_shared: int = 0):
     if rc != 0:
         raise ValueError("oracle_router_topk: bad arguments")
     return ids, w
+
+
+def q8_0_dequant_block(block34) -> np.ndarray:
+    b = np.ascontiguousarray(np.frombuffer(bytes(block34), dtype=np.uint8))
+    assert b.size == 34
+    out = np.empty(32, dtype=np.float64)
+    _load().oracle_q8_0_dequant_block(_ptr(b), _ptr(out))
+    return out
+
+
+def q8_0_matmul(x: np.ndarray, B: np.ndarray, N: int, K: int, with_bound: bool = True):
+    """y = x . deq(B) for Q8_0 B (34-byte blocks) in double, rounded to float32."""
+    x = np.ascontiguousarray(x, dtype=np.float32).reshape(-1, K)
+    M = x.shape[0]
+    b = _blocks_u8(B)
+    assert b.size == K * (N // 32) * 34, "B has the wrong number of bytes"
+    y = np.empty((M, N), dtype=np.float32)
+    bnd = np.empty((M, N), dtype=np.float64) if with_bound else None
+    rc = _load().oracle_q8_0_matmul(_ptr(x), _ptr(b), M, N, K, _ptr(y), _ptr(bnd))
+    if rc != 0:
+        raise ValueError("oracle_q8_0_matmul: bad arguments")
+    return y, bnd

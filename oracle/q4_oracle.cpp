@@ -24,13 +24,25 @@ namespace {
 
 constexpr int kBlockBytes = 18;   // 2-byte scale + 16 bytes of nibbles
 constexpr int kBlockWeights = 32;
+constexpr int kQ8BlockBytes = 34;  // 2-byte scale + 32 signed bytes
 
 // Row v (length K, double) times the dequantized K x N matrix B, accumulated
 // over k in ascending order: acc[n] = sum_k v[k] * w[k][n] and, when bnd is
 // given, bnd[n] = sum_k |v[k] * w[k][n]|. Each product v[k] * w[k][n] is exact
 // in double when v[k] came from a binary32 or binary16 value.
+// Dequantizes one block of either format into 32 doubles.
+typedef void (*DequantFn)(const uint8_t*, double*);
+
+void row_times_matrix_fmt(const double* v, const uint8_t* B, int N, int K, double* acc,
+                          double* bnd, DequantFn dequant, int block_bytes);
+
 void row_times_matrix(const double* v, const uint8_t* B, int N, int K,
                       double* acc, double* bnd) {
+  row_times_matrix_fmt(v, B, N, K, acc, bnd, oracle_dequant_block, kBlockBytes);
+}
+
+void row_times_matrix_fmt(const double* v, const uint8_t* B, int N, int K, double* acc,
+                          double* bnd, DequantFn dequant, int block_bytes) {
   const int nb = N / kBlockWeights;
   for (int n = 0; n < N; ++n) {
     acc[n] = 0.0;
@@ -39,9 +51,9 @@ void row_times_matrix(const double* v, const uint8_t* B, int N, int K,
   double w32[kBlockWeights];
   for (int k = 0; k < K; ++k) {
     const double a = v[k];
-    const uint8_t* row = B + (size_t)k * (size_t)nb * kBlockBytes;
+    const uint8_t* row = B + (size_t)k * (size_t)nb * block_bytes;
     for (int jb = 0; jb < nb; ++jb) {
-      oracle_dequant_block(row + (size_t)jb * kBlockBytes, w32);
+      dequant(row + (size_t)jb * block_bytes, w32);
       double* accb = acc + (size_t)jb * kBlockWeights;
       double* bndb = bnd ? bnd + (size_t)jb * kBlockWeights : nullptr;
       for (int l = 0; l < kBlockWeights; ++l) {
@@ -233,6 +245,31 @@ int oracle_router_topk(const float* logits, int T, int E, int topk, int n_shared
     for (int s = 0; s < n_shared; ++s) {
       id[topk + s] = E + s;
       wt[topk + s] = 1.0f;
+    }
+  }
+  return 0;
+}
+
+void oracle_q8_0_dequant_block(const uint8_t* block34, double* out32) {
+  const uint16_t bits = (uint16_t)(block34[0] | (block34[1] << 8));  // little-endian
+  const double d = oracle_fp16_to_double(bits);
+  for (int l = 0; l < kBlockWeights; ++l) {
+    const int q = (int)(int8_t)block34[2 + l];  // two's complement byte
+    out32[l] = (double)q * d;
+  }
+}
+
+int oracle_q8_0_matmul(const float* x, const uint8_t* B, int M, int N, int K, float* y,
+                       double* bound) {
+  if (bad_matmul_args(x, B, M, N, K, y)) return -1;
+  std::vector<double> v(K), acc(N), bnd(N);
+  for (int m = 0; m < M; ++m) {
+    for (int k = 0; k < K; ++k) v[k] = (double)x[(size_t)m * K + k];
+    row_times_matrix_fmt(v.data(), B, N, K, acc.data(), bound ? bnd.data() : nullptr,
+                         oracle_q8_0_dequant_block, kQ8BlockBytes);
+    for (int n = 0; n < N; ++n) {
+      y[(size_t)m * N + n] = (float)acc[n];
+      if (bound) bound[(size_t)m * N + n] = bnd[n];
     }
   }
   return 0;

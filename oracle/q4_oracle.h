@@ -80,6 +80,18 @@ int oracle_moe_decode(const float* x, const uint8_t* Wg, const uint8_t* Wu,
                       int T, int H, int I, int E, int topk, float* out,
                       double* bound, double* h_out);
 
+/* Q8_0 weights. The article's §2.2 compares Q8_0 with Q4_0 (twice the memory,
+ * about 60 % of Q4_0's token rate on the author's CPU) but does not define
+ * it; the plainest reading, used here: a block of 32 weights is 34
+ * little-endian bytes, a binary16 scale d then 32 signed (two's complement)
+ * bytes q, weight l = q[l] * d (exact in double and in float). Blocks run
+ * along N as for Q4_0. */
+void oracle_q8_0_dequant_block(const uint8_t* block34, double* out32);
+
+/* y[M x N] = x[M x K] . deq(B[K x N]) for Q8_0 B, as oracle_q4_0_matmul. */
+int oracle_q8_0_matmul(const float* x, const uint8_t* B, int M, int N, int K, float* y,
+                       double* bound);
+
 /* MoE router (the gate in front of the routed experts):
  *   logits[t][e] = sum_h x[t][h] * Wr[e][h]
  * accumulated in double in h order and rounded once to float. Wr holds one row

@@ -392,3 +392,53 @@ def test_router_topk_matches_stable_argsort_and_shift_invariance():
     ids1, w1 = oracle.router_topk(lq, 6, n_shared=2)
     ids2, w2 = oracle.router_topk(lq + np.float32(1.0), 6, n_shared=2)
     assert (ids2 == ids1).all() and (w2 == w1).all()
+
+
+# --------------------------------------------------------------------------
+# Q8_0 (34-byte blocks: binary16 scale, 32 signed bytes; w = q * d)
+# --------------------------------------------------------------------------
+
+def test_q8_0_block_handworked():
+    # weights -128, -120, ..., 120 (every eighth signed byte value, both signs)
+    q = np.array([8 * l - 128 for l in range(32)], dtype=np.int8)
+    blk = datagen.assemble_q8(np.uint16(0x3C00), q)      # d = 1.0
+    assert oracle.q8_0_dequant_block(blk).tolist() == [float(8 * l - 128) for l in range(32)]
+    blk = datagen.assemble_q8(np.uint16(0xB800), q)      # d = -0.5
+    assert oracle.q8_0_dequant_block(blk).tolist() == [-0.5 * (8 * l - 128) for l in range(32)]
+    # sign extension at the ends: bytes 0x7F, 0x80, 0xFF, 0x01 are 127, -128, -1, 1
+    q = np.zeros(32, dtype=np.uint8)
+    q[:4] = [0x7F, 0x80, 0xFF, 0x01]
+    blk = datagen.assemble_q8(np.uint16(0x4000), q)      # d = 2.0
+    assert oracle.q8_0_dequant_block(blk)[:5].tolist() == [254.0, -256.0, -2.0, 2.0, 0.0]
+    # subnormal and zero scales
+    assert oracle.q8_0_dequant_block(datagen.assemble_q8(np.uint16(0x0001), q))[0] == 127 * 2.0 ** -24
+    assert not oracle.q8_0_dequant_block(datagen.assemble_q8(np.uint16(0x8000), q)).any()
+
+
+def test_q8_0_matmul_integer_exact_and_invariants():
+    g = np.random.Generator(np.random.PCG64(81))
+    K, N, M = 96, 160, 3
+    q = g.integers(-128, 128, size=(K, N // 32, 32)).astype(np.int8)
+    d_bits = g.choice(np.array([0x3C00, 0x3800, 0x4000], dtype=np.uint16), size=(K, N // 32))
+    B = datagen.assemble_q8(d_bits, q)
+    x = g.integers(-4, 5, size=(M, K)).astype(np.float32)
+    y, bnd = oracle.q8_0_matmul(x, B, N, K)
+    d = d_bits.view(np.float16).astype(np.float64)
+    W = (q.astype(np.float64) * d[..., None]).reshape(K, N)   # dequantized by numpy
+    assert (y == (x.astype(np.float64) @ W).astype(np.float32)).all()
+    assert (bnd == np.abs(x.astype(np.float64)) @ np.abs(W)).all()
+    # one-hot rows select dequantized rows; doubling every scale doubles y
+    B = datagen.q8_0_random(82, K, N)
+    oh = np.zeros((2, K), dtype=np.float32)
+    oh[0, 5] = oh[1, K - 1] = 1.0
+    y, _ = oracle.q8_0_matmul(oh, B, N, K)
+    dq = np.stack([oracle.q8_0_dequant_block(B[k, j]) for k in (5, K - 1) for j in range(N // 32)])
+    assert (y == dq.reshape(2, N).astype(np.float32)).all()
+    x = datagen.activations(83, 2, K)
+    y, _ = oracle.q8_0_matmul(x, B, N, K)
+    B2 = B.copy()
+    B2[..., 0:2] = (B[..., 0:2].copy().view(np.uint16) + 0x0400).view(np.uint8)
+    assert (oracle.q8_0_matmul(x, B2, N, K)[0] == 2 * y).all()
+    Bz = B.copy()
+    Bz[..., 0:2] = 0
+    assert not oracle.q8_0_matmul(x, Bz, N, K)[0].any()
