@@ -181,6 +181,41 @@ def bench_dense(torch, dev, steps, warmup):
                 R=R, host=host, shapes=shapes, Ms=Ms)
 
 
+def bench_q8(torch, dev, steps, warmup, d):
+    """q8_0_gemv on the dense 7B shapes at batch 1 and 8 (Q8_0 weights: 34 bytes
+    per 32 weights), timed like the Q4_0 calls, and the batch-1 token-rate ratio
+    Q8_0 / Q4_0 over the four matrices (the article's CPU figure is about 60 %)."""
+    from moe_experts_amd import datagen, q8_0_gemv, q8_0_gemv_workspace_bytes
+    shapes = datagen.DENSE_7B_SHAPES
+    q8b = lambda K, N: K * (N // 32) * 34
+    wbytes = sum(q8b(K, N) for _, K, N, _ in shapes)
+    R = max(2, math.ceil(GIB / wbytes))
+    base = [torch.from_numpy(datagen.q8_0_random(seed + 4000, K, N)).to(dev)
+            for _, K, N, seed in shapes]
+    copies = [base] + [[b.clone() for b in base] for _ in range(R - 1)]
+    need = max(q8_0_gemv_workspace_bytes(M, N, K) for M in (1, 8) for _, K, N, _ in shapes)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    res, t8 = {}, {}
+    for M in (1, 8):
+        for i, (name, K, N, _) in enumerate(shapes):
+            x = torch.from_numpy(datagen.activations(datagen.dense_x_seed(M), M, K)).to(dev)
+            y = torch.empty((M, N), dtype=torch.float32, device=dev)
+            for u in range(warmup):
+                q8_0_gemv(x, copies[u % R][i], N, y=y, ws=ws)
+            gs = [capture(torch, lambda c=c: [q8_0_gemv(x, copies[(c * 8 + u) % R][i], N, y=y,
+                                                        ws=ws) for u in range(8)])
+                  for c in range(2)]
+            t = time_graph(torch, gs, max(steps, 10), 8)
+            t8[(M, i)] = t
+            b = q8b(K, N) + 4 * M * K + 4 * M * N
+            res[f"{name}_M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1)}
+    q4_t = sum(d["call_s"][(1, i)] for i in range(len(shapes)))
+    q8_t = sum(t8[(1, i)] for i in range(len(shapes)))
+    res["token_rate_vs_q4_0_M1"] = round(q4_t / q8_t, 3)
+    log(f"[q8_0] {res}")
+    return res
+
+
 # The dominant unit of the headline step: q4_0_gemv at batch 8 on the
 # 4096 x 11008 gate matrix. Batch 8 takes the largest share of the step, and
 # its gate, up and down calls are the longest launches. One call is two
@@ -539,6 +574,7 @@ def main():
     if not args.no_extras and args.only is None:
         extras["moe_decode"] = bench_moe(torch, dev, args.steps, args.warmup)
         extras["prefill_gemm"] = bench_prefill(torch, dev, args.steps, args.warmup)
+        extras["q8_0_gemv"] = bench_q8(torch, dev, args.steps, args.warmup, d)
     extras["dense_per_call"] = d["per_call"]
     extras["dense_per_batch_GBps"] = {str(M): round(b / (ms * 1e-3) / 1e9, 1)
                                       for M, (ms, b) in d["per_M"].items()}

@@ -54,6 +54,20 @@ static_assert(sizeof(q4_0_block) == 18, "q4_0_block must be 18 bytes");
 _Static_assert(sizeof(q4_0_block) == 18, "q4_0_block must be 18 bytes");
 #endif
 
+/* One Q8_0 block: 34 bytes, 2-byte aligned, little-endian. The article's
+ * §2.2 compares Q8_0 with Q4_0 (twice the memory) without defining it; read
+ * as 32 weights q[l] * d with a binary16 scale d and signed 8-bit q. */
+typedef struct __attribute__((packed, aligned(2))) q8_0_block {
+  uint16_t d;     /* binary16 scale bit pattern */
+  int8_t qs[32];  /* weights in two's complement */
+} q8_0_block;
+
+#ifdef __cplusplus
+static_assert(sizeof(q8_0_block) == 34, "q8_0_block must be 34 bytes");
+#else
+_Static_assert(sizeof(q8_0_block) == 34, "q8_0_block must be 34 bytes");
+#endif
+
 typedef enum q4_status {
   Q4_OK = 0,
   Q4_EINVAL = -1,      /* null pointer or non-positive dimension */
@@ -87,6 +101,18 @@ const char* q4_strerror(int status);
  * ------------------------------------------------------------------------- */
 size_t q4_0_gemv_workspace_bytes(int M, int N, int K);
 int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K, void* ws,
+              size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode GEMV over Q8_0 weights (batch 1..8): y[M x N] = x[M x K] . deq(B[K x N]),
+ * the Q8_0 counterpart of q4_0_gemv for the article's Q8_0-versus-Q4_0
+ * comparison (§2.2). Same layout rules (blocks along N), arguments, limits
+ * and errors as q4_0_gemv, with B of q8_0_block (2-byte aligned, < 2 GiB).
+ *   ws/ws_bytes: workspace of q8_0_gemv_workspace_bytes(M, N, K) bytes.
+ * Accumulation is fp32; each product x * q * d is formed as (x * d) * q.
+ * ------------------------------------------------------------------------- */
+size_t q8_0_gemv_workspace_bytes(int M, int N, int K);
+int q8_0_gemv(const float* x, const q8_0_block* B, float* y, int M, int N, int K, void* ws,
               size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------

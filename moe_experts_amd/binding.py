@@ -37,6 +37,10 @@ _lib.q4_0_gemv_workspace_bytes.restype = _Z
 _lib.q4_0_gemv_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.q4_0_gemv.restype = _I
 _lib.q4_0_gemv.argtypes = [_P, _P, _P, _I, _I, _I, _P, _Z, _P]
+_lib.q8_0_gemv_workspace_bytes.restype = _Z
+_lib.q8_0_gemv_workspace_bytes.argtypes = [_I, _I, _I]
+_lib.q8_0_gemv.restype = _I
+_lib.q8_0_gemv.argtypes = [_P, _P, _P, _I, _I, _I, _P, _Z, _P]
 _lib.q4_0_gemm.restype = _I
 _lib.q4_0_gemm.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 _lib.moe_q4_0_workspace_bytes.restype = _Z
@@ -53,6 +57,7 @@ _lib.moe_q4_0_layer.restype = _I
 _lib.moe_q4_0_layer.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 
 BLOCK_BYTES = 18
+Q8_BLOCK_BYTES = 34
 
 
 class Q4Error(RuntimeError):
@@ -135,6 +140,28 @@ def q4_0_gemv(x: torch.Tensor, B: torch.Tensor, N: int, y: torch.Tensor | None =
         ws = workspace(need, x.device)
     pw, nw = (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8, ws.numel()), ws.numel())
     _check(_lib.q4_0_gemv(px, pb, py, M, N, K, pw, nw, _stream(x.device)))
+    return y
+
+
+def q8_0_gemv_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.q8_0_gemv_workspace_bytes(M, N, K))
+
+
+def q8_0_gemv(x: torch.Tensor, B: torch.Tensor, N: int, y: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None) -> torch.Tensor:
+    """y[M, N] = x[M, K] . deq(B) for a Q8_0 matrix B (uint8, K*(N/32)*34 bytes)."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if N <= 0 or N % 32:
+        raise ValueError("N must be a positive multiple of 32")
+    px = _dev(x, "x", torch.float32, M * K)
+    pb = _dev(B, "B", torch.uint8, K * (N // 32) * Q8_BLOCK_BYTES)
+    if y is None:
+        y = torch.empty((M, N), dtype=torch.float32, device=x.device)
+    py = _dev(y, "y", torch.float32, M * N)
+    pw, nw = _ws_arg(ws, q8_0_gemv_workspace_bytes(M, N, K), x.device)
+    _check(_lib.q8_0_gemv(px, pb, py, M, N, K, pw, nw, _stream(x.device)))
     return y
 
 

@@ -31,6 +31,10 @@ hipError_t launch_gemv(const float* x, const uint8_t* B, float* y, int M, int N,
 bool plan_gemv_mfma(int M, int N, int K, GemvPlan& p);
 hipError_t launch_gemv_mfma(const float* x, const uint8_t* B, float* y, int M, int N, int K,
                             void* ws, const GemvPlan& p, hipStream_t st);
+// Q8_0 weights (gemv_q8_0.hip): the vector tiles' plan fields (LPB, Jt, Lr, P, C, Kt, S)
+GemvPlan plan_gemv_q8(int M, int N, int K);
+hipError_t launch_gemv_q8(const float* x, const uint8_t* B, float* y, int M, int N, int K,
+                          void* ws, const GemvPlan& p, hipStream_t st);
 // y[i] = sum over s < S of part[s * MN + i], in split order
 hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStream_t st);
 

@@ -25,6 +25,16 @@ int check_gemv(const float* x, const q4_0_block* B, const float* y, int M, int N
   return Q4_OK;
 }
 
+int check_gemv_q8(const float* x, const q8_0_block* B, const float* y, int M, int N, int K) {
+  if (!x || !B || !y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
+  if (N % 32 != 0 || M > Q4_GEMV_MAX_M) return Q4_ESHAPE;
+  if ((long long)K * (N / 32) * 34 > kMaxBytes || (long long)M * K * 4 > kMaxBytes ||
+      (long long)M * N * 4 > kMaxBytes)
+    return Q4_ETOOBIG;
+  if (!aligned(x, 4) || !aligned(y, 4) || !aligned(B, 2)) return Q4_EALIGN;
+  return Q4_OK;
+}
+
 int check_ws(const void* ws, size_t ws_bytes, size_t need) {
   if (need == 0) return Q4_OK;
   if (!ws || ws_bytes < need) return Q4_EWORKSPACE;
@@ -103,6 +113,22 @@ int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K
   if (rc != Q4_OK) return rc;
   return from_hip(q4::launch_gemv(x, reinterpret_cast<const uint8_t*>(B), y, M, N, K, ws, p,
                                   static_cast<hipStream_t>(stream)));
+}
+
+size_t q8_0_gemv_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || M > Q4_GEMV_MAX_M) return 0;
+  return q4::plan_gemv_q8(M, N, K).ws_bytes;
+}
+
+int q8_0_gemv(const float* x, const q8_0_block* B, float* y, int M, int N, int K, void* ws,
+              size_t ws_bytes, void* stream) {
+  int rc = check_gemv_q8(x, B, y, M, N, K);
+  if (rc != Q4_OK) return rc;
+  const q4::GemvPlan p = q4::plan_gemv_q8(M, N, K);
+  rc = check_ws(ws, ws_bytes, p.ws_bytes);
+  if (rc != Q4_OK) return rc;
+  return from_hip(q4::launch_gemv_q8(x, reinterpret_cast<const uint8_t*>(B), y, M, N, K, ws, p,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int q4_0_gemm(const uint16_t* X, const q4_0_block* B, float* Y, int M, int N, int K,

@@ -153,3 +153,20 @@ def test_layer_rejects_bad_arguments(lib):
     assert need > lib.moe_q4_0_workspace_bytes(32, 5120, 1536, 162, 8)
     assert lib.moe_q4_0_layer_workspace_bytes(32, 5120, 1536, 1023, 6, 2) == 0
     assert f(*ok, 32, 5120, 1536, 160, 6, 2, FAKE + 64, need, None) == -3
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, FAKE, FAKE, 1, 32, 1), -1),
+    ((FAKE, FAKE, FAKE, 9, 32, 4), -2),
+    ((FAKE, FAKE, FAKE, 1, 48, 4), -2),
+    ((FAKE, FAKE + 1, FAKE, 1, 32, 4), -3),
+    ((FAKE, FAKE, FAKE, 1, 1 << 29, 1 << 27), -6),   # Q8_0 matrix larger than 2 GiB
+])
+def test_q8_gemv_rejects_bad_arguments(lib, args, code):
+    f = lib.q8_0_gemv
+    f.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                ctypes.c_void_p]
+    assert f(*args, None, 0, None) == code
+    lib.q8_0_gemv_workspace_bytes.restype = ctypes.c_size_t
+    assert lib.q8_0_gemv_workspace_bytes(1, 4096, 4096) > 0
+    assert lib.q8_0_gemv_workspace_bytes(9, 4096, 4096) == 0
