@@ -84,6 +84,7 @@ typedef enum q4_status {
 #define Q4_MOE_MAX_T 64    /* tokens in one moe_q4_0_decode call */
 #define Q4_MOE_MAX_TOPK 8  /* routed experts per token */
 #define Q4_MOE_MAX_E 1024  /* experts per layer */
+#define Q4_MOE_PREFILL_MAX_T 65536  /* tokens in one moe_q4_0_prefill call */
 
 /* Static description of a status code (never NULL). */
 const char* q4_strerror(int status);
@@ -154,6 +155,33 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
                     const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
                     float* out, int T, int H, int I, int E, int topk, void* ws,
                     size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Routed-expert MoE at prefill (many tokens per expert): the same layer as
+ * moe_q4_0_decode, with every expert's gate, up and down products run as
+ * GEMMs on the fp16 matrix cores. The KTransformers tutorial gives the
+ * experts separate prefill and generate operators and runs prefill on the
+ * GPU ("KExpertsTorch"); the dense prefill GEMMs run on tensor cores
+ * ("Optimization 2").
+ *   out[t] = sum_{s < topk} topk_w[t][s] * Wd_e ( SiLU(x_t . Wg_e) * (x_t . Wu_e) )
+ *   x16      fp16 [T][H] (the caller rounds its activations), 16-byte aligned
+ *   Wg, Wu, Wd, topk_ids, topk_w, out   as in moe_q4_0_decode; weights 4-byte
+ *            aligned
+ *   1 <= T <= Q4_MOE_PREFILL_MAX_T, 1 <= topk <= Q4_MOE_MAX_TOPK,
+ *   1 <= E <= Q4_MOE_MAX_E, H % 128 == 0, I % 128 == 0.
+ * Pairs are sorted by expert on the device (stable); each expert's rows go
+ * through 256-row tiles. Each dequantized weight and h = SiLU(g) * u are
+ * rounded to fp16 before their products; sums are fp32. Ids outside [0, E)
+ * contribute zero; slots are summed in order 0..topk-1.
+ *   ws/ws_bytes: workspace of moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)
+ *   bytes (the per-pair gate, up, h and down rows: about 14 * T * topk * max(H, I)
+ *   bytes).
+ * ------------------------------------------------------------------------- */
+size_t moe_q4_0_prefill_workspace_bytes(int T, int H, int I, int E, int topk);
+int moe_q4_0_prefill(const uint16_t* x16, const q4_0_block* Wg, const q4_0_block* Wu,
+                     const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
+                     float* out, int T, int H, int I, int E, int topk, void* ws,
+                     size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * MoE router: the gate in front of moe_q4_0_decode, on the device. The

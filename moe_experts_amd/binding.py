@@ -47,6 +47,10 @@ _lib.moe_q4_0_workspace_bytes.restype = _Z
 _lib.moe_q4_0_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
 _lib.moe_q4_0_decode.restype = _I
 _lib.moe_q4_0_decode.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
+_lib.moe_q4_0_prefill_workspace_bytes.restype = _Z
+_lib.moe_q4_0_prefill_workspace_bytes.argtypes = [_I, _I, _I, _I, _I]
+_lib.moe_q4_0_prefill.restype = _I
+_lib.moe_q4_0_prefill.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
 _lib.moe_router_workspace_bytes.restype = _Z
 _lib.moe_router_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.moe_router_topk.restype = _I
@@ -264,4 +268,33 @@ def moe_q4_0_layer(x: torch.Tensor, Wr: torch.Tensor, Wg: torch.Tensor, Wu: torc
     pws, nws = _ws_arg(ws, moe_q4_0_layer_workspace_bytes(T, H, I, E, topk, n_shared), x.device)
     _check(_lib.moe_q4_0_layer(px, pr, pg, pu, pd, po, T, H, I, E, topk, n_shared, pws, nws,
                                _stream(x.device)))
+    return out
+
+
+def moe_q4_0_prefill_workspace_bytes(T: int, H: int, I: int, E: int, topk: int) -> int:
+    return int(_lib.moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk))
+
+
+def moe_q4_0_prefill(x16: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: torch.Tensor,
+                     topk_ids: torch.Tensor, topk_w: torch.Tensor, I: int, E: int,
+                     out: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed-expert MoE at prefill on the matrix cores; x16 [T, H] float16,
+    ids/weights [T, topk]."""
+    if x16.dim() != 2 or topk_ids.dim() != 2:
+        raise ValueError("x16 must be [T, H] and topk_ids [T, topk]")
+    T, H = x16.shape
+    topk = topk_ids.shape[1]
+    mat = H * (I // 32) * BLOCK_BYTES
+    px = _dev(x16, "x16", torch.float16, T * H)
+    pg = _dev(Wg, "Wg", torch.uint8, E * mat)
+    pu = _dev(Wu, "Wu", torch.uint8, E * mat)
+    pd = _dev(Wd, "Wd", torch.uint8, E * mat)
+    pi = _dev(topk_ids, "topk_ids", torch.int32, T * topk)
+    pw_ = _dev(topk_w, "topk_w", torch.float32, T * topk)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=x16.device)
+    po = _dev(out, "out", torch.float32, T * H)
+    pws, nws = _ws_arg(ws, moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk), x16.device)
+    _check(_lib.moe_q4_0_prefill(px, pg, pu, pd, pi, pw_, po, T, H, I, E, topk, pws, nws,
+                                 _stream(x16.device)))
     return out

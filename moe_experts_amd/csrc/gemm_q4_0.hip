@@ -212,6 +212,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_generic_kernel(GemmArg
 // ---------------------------------------------------------------------------
 namespace fast {
 constexpr int BM = 256, BN = 128, BK = 64;
+static_assert(BM == kGemmRows, "grouped m-tiles are one workgroup tile tall");
 constexpr int kXStages = 3, kRStages = 4;
 constexpr int kXChunks = BM * BK / 8;                     // 16-byte chunks per X stage: 2048
 constexpr int kXBytes = kXChunks * 16;                    // 32 KiB
@@ -232,10 +233,18 @@ static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct Args {
-  const uint16_t* X;
+  const uint16_t* X;  // M rows of K halves
   const uint8_t* B;
   float* Y;
   int M, N, K, NB, tiles_n, nk;
+  // Expert-grouped mode (tiles != null): m-tile i is tiles[i] = (expert e,
+  // first output row, rows <= BM); its weights are the e-th of consecutive
+  // K x N matrices of mat_bytes; output row q reads X row src[q] (src null:
+  // row q). Only the first *n_tiles m-tiles exist.
+  const int4* tiles;
+  const int* n_tiles;
+  const int32_t* src;
+  size_t mat_bytes;
 };
 
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
@@ -295,12 +304,13 @@ struct Producer {
   uint32_t st[kUL][4];
   int nk;
 
-  __device__ __forceinline__ void init(const Args& g, int m0, int j0, int t) {
+  __device__ __forceinline__ void init(const Args& g, const uint8_t* B, int m0, int rows, int j0,
+                                       int t) {
     constexpr uint32_t kOut = 0x80000000u;
     nk = g.nk;
     rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g.X), (short)0,
                                            (int)((uint32_t)g.M * (uint32_t)g.K * 2u), 0x00020000);
-    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(g.B), (short)0,
+    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B), (short)0,
                                            (int)((uint32_t)g.K * (uint32_t)g.NB * kBlockBytes),
                                            0x00020000);
     const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
@@ -312,8 +322,8 @@ struct Producer {
       const int slot = i * kGemmThreads + t;  // row r = slot / 8, stored position slot % 8
       const int r = slot >> 3;
       const int c = (slot & 7) ^ swz_x(r);   // source chunk landing in that position
-      const int m = m0 + r;
-      xoff[i] = m < g.M ? ((uint32_t)m * (uint32_t)g.K + 8u * c) * 2u : kOut;
+      const int xr = r < rows ? (g.src ? g.src[m0 + r] : m0 + r) : 0;
+      xoff[i] = r < rows ? ((uint32_t)xr * (uint32_t)g.K + 8u * c) * 2u : kOut;
     }
 #pragma unroll
     for (int i = 0; i < kRInstr; ++i) {
@@ -408,17 +418,32 @@ struct Producer {
 // dequant (VALU) runs on the same SIMDs while the matrix cores run the MFMAs.
 __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
-  const int tm = L / g.tiles_n;
-  const int tn = L - tm * g.tiles_n;
-  const int m0 = tm * BM;
+  int m0, rows, tn;
+  const uint8_t* B = g.B;
+  if (g.tiles) {
+    // grouped: plain dispatch order (the live tiles come first; the XCD remap
+    // would crowd them onto a few XCDs)
+    const int tile = blockIdx.x / g.tiles_n;
+    tn = blockIdx.x - tile * g.tiles_n;
+    if (tile >= *g.n_tiles) return;  // the whole workgroup, before any barrier
+    const int4 tl = g.tiles[tile];
+    B += (size_t)tl.x * g.mat_bytes;
+    m0 = tl.y;
+    rows = tl.z;
+  } else {
+    const int L = xcd_logical_tile(blockIdx.x, gridDim.x);
+    const int tm = L / g.tiles_n;
+    tn = L - tm * g.tiles_n;
+    m0 = tm * BM;
+    rows = g.M - m0;
+  }
   const int j0 = tn * (BN / kBlockWeights);
   const int wave = threadIdx.x >> 6;
 
   if (wave >= 4) {
     // ------------------------------------------------------------ producer
     Producer pr;
-    pr.init(g, m0, j0, (int)threadIdx.x - kGemmThreads);
+    pr.init(g, B, m0, rows, j0, (int)threadIdx.x - kGemmThreads);
     // Prologue: X(0), raw(0), raw(1) | X(1), raw(2); then raw(0) -> B(0).
     pr.issue_x(lds, 0);
     pr.issue_r(lds, 0);
@@ -496,8 +521,8 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
       const int col = j0 * kBlockWeights + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (row < g.M) g.Y[(size_t)row * g.N + col] = acc[i][j][r];
+        const int rr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (rr < rows) g.Y[(size_t)(m0 + rr) * g.N + col] = acc[i][j][r];
       }
     }
 }
@@ -530,6 +555,10 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
     f.NB = N / kBlockWeights;
     f.tiles_n = N / fast::BN;
     f.nk = (K + fast::BK - 1) / fast::BK;
+    f.tiles = nullptr;
+    f.n_tiles = nullptr;
+    f.src = nullptr;
+    f.mat_bytes = 0;
     const long long tiles = (long long)((M + fast::BM - 1) / fast::BM) * f.tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
     hipLaunchKernelGGL(fast::gemm_q4_0_kernel, dim3((unsigned)tiles), dim3(2 * kGemmThreads),
@@ -541,6 +570,33 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
   if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(gemm_q4_0_generic_kernel, dim3((unsigned)tiles), dim3(kGemmThreads), 0, st,
                      g);
+  return hipGetLastError();
+}
+
+bool gemm_grouped_supported(int N, int K) { return K % fast::BK == 0 && N % fast::BN == 0; }
+
+hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, size_t mat_bytes,
+                               float* Y, int N, int K, const int4* tiles, const int* n_tiles,
+                               int max_tiles, const int32_t* src, hipStream_t st) {
+  fast::Args f;
+  f.X = X;
+  f.B = B;
+  f.Y = Y;
+  f.M = x_rows;
+  f.N = N;
+  f.K = K;
+  f.NB = N / kBlockWeights;
+  f.tiles_n = N / fast::BN;
+  f.nk = K / fast::BK;
+  f.tiles = tiles;
+  f.n_tiles = n_tiles;
+  f.src = src;
+  f.mat_bytes = mat_bytes;
+  const long long grid = (long long)max_tiles * f.tiles_n;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL(fast::gemm_q4_0_kernel, dim3((unsigned)grid), dim3(2 * kGemmThreads),
+                     fast::kLdsBytes, st, f);
   return hipGetLastError();
 }
 

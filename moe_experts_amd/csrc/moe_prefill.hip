@@ -1,0 +1,225 @@
+// Routed-expert MoE at prefill: many tokens per expert, so each expert's
+// gate, up and down products are GEMMs on the fp16 matrix cores.
+//
+// The KTransformers DeepSeek-V2 tutorial runs the prefill-stage experts on the
+// GPU as batched matmuls (its injection rules give the experts separate
+// prefill and generate operators, "KExpertsTorch" for prefill) and the dense
+// prefill GEMMs on tensor cores ("Optimization 2", Marlin); this path combines
+// the two: the decode path's expert grouping with the prefill GEMM's tiles.
+//
+//   1. moe_prefill_route_kernel (one workgroup): a stable counting sort of
+//      the (token, slot) pairs by expert. Sorted row q holds pair perm[q]; the
+//      kernel writes, per sorted row, the token it reads (src[q]), per pair its
+//      sorted row (pos[p], -1 for an id outside [0, E)), and the list of
+//      256-row m-tiles (expert, first row, rows) of every expert's rows.
+//   2. gate and up: the prefill GEMM kernel in its grouped mode (X rows
+//      gathered by src, the expert's Q4_0 matrix, fp32 rows G and U in sorted
+//      order).
+//   3. moe_prefill_act_kernel: h = fp16(SiLU(G) * U), sorted order.
+//   4. down: the grouped GEMM on h (rows in sorted order, no gather) -> D.
+//   5. moe_prefill_combine_kernel: out[t] = sum over slots 0..topk-1 of
+//      w[t][s] * D[pos[t * topk + s]] (slot order; invalid slots skipped).
+// Precision: x is given in fp16 and h is rounded to fp16 for the down GEMM;
+// each dequantized weight is rounded to fp16 (the prefill GEMM's rule); all
+// sums are fp32.
+#include "q4_device.hpp"
+#include "q4_internal.hpp"
+
+namespace q4 {
+namespace {
+
+constexpr int kRouteThreads = 1024;
+constexpr int kChunk = 512;                      // pairs ranked per pass (8 waves)
+constexpr int kChunkWaves = kChunk / kWaveSize;
+constexpr int kIdBits = 10;
+static_assert((1 << kIdBits) >= Q4_MOE_MAX_E, "expert ids fit the ballot match");
+static_assert(Q4_MOE_MAX_E <= kRouteThreads, "one lane per expert");
+
+struct PrefillRoute {
+  const int32_t* ids;
+  int npairs, E, topk;
+  int32_t* src;   // [npairs] token of sorted row q
+  int32_t* pos;   // [npairs] sorted row of pair p (-1: invalid id)
+  int4* tiles;    // [max_tiles] (expert, first row, rows, 0)
+  int* counts;    // [2]: m-tiles, valid rows
+};
+
+__device__ int scan_inclusive(int v, int* wsum) {
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int wave = threadIdx.x / kWaveSize;
+#pragma unroll
+  for (int o = 1; o < kWaveSize; o <<= 1) {
+    const int n = __shfl_up(v, o);
+    if (lane >= o) v += n;
+  }
+  if (lane == kWaveSize - 1) wsum[wave] = v;
+  __syncthreads();
+  int add = 0;
+  for (int w = 0; w < wave; ++w) add += wsum[w];
+  __syncthreads();
+  return v + add;
+}
+
+__global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(PrefillRoute a) {
+  __shared__ int s_cnt[Q4_MOE_MAX_E];
+  __shared__ int s_base[Q4_MOE_MAX_E];
+  __shared__ int s_wcnt[kChunkWaves][Q4_MOE_MAX_E];
+  __shared__ int s_wsum[kRouteThreads / kWaveSize];
+  const int t = threadIdx.x;
+  const int lane = t & (kWaveSize - 1);
+  const int wave = t / kWaveSize;
+
+  s_cnt[t] = 0;
+  __syncthreads();
+  for (int p = t; p < a.npairs; p += kRouteThreads) {
+    const int e = a.ids[p];
+    if (e >= 0 && e < a.E) atomicAdd(&s_cnt[e], 1);
+  }
+  __syncthreads();
+  // expert t: its first sorted row and its m-tiles of 256 rows
+  const int cnt = t < a.E ? s_cnt[t] : 0;
+  const int nt = (cnt + kGemmRows - 1) / kGemmRows;
+  const int off = scan_inclusive(cnt, s_wsum) - cnt;
+  const int toff = scan_inclusive(nt, s_wsum) - nt;
+  for (int i = 0; i < nt; ++i)
+    a.tiles[toff + i] = make_int4(t, off + kGemmRows * i, min(kGemmRows, cnt - kGemmRows * i), 0);
+  if (t == kRouteThreads - 1) {
+    a.counts[0] = toff + nt;
+    a.counts[1] = off + cnt;
+  }
+  s_base[t] = off;
+  __syncthreads();
+
+  // Stable ranks, kChunk pairs at a time: within a wave by an exact-id ballot
+  // match, across the chunk's waves by per-wave counts, across chunks by a
+  // running base per expert.
+  const uint64_t below = (1ull << lane) - 1;
+  for (int c0 = 0; c0 < a.npairs; c0 += kChunk) {
+    for (int i = t; i < kChunkWaves * Q4_MOE_MAX_E; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int p = c0 + t;
+    const bool mine = t < kChunk && p < a.npairs;
+    const int e = mine ? a.ids[p] : -1;
+    const bool valid = e >= 0 && e < a.E;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < kIdBits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t set = __ballot(bit);
+      same &= bit ? set : ~set;
+    }
+    if (valid && (same & below) == 0) s_wcnt[wave][e] = __popcll(same);
+    __syncthreads();
+    if (mine) {
+      int q = -1;
+      if (valid) {
+        q = s_base[e] + __popcll(same & below);
+        for (int w = 0; w < wave; ++w) q += s_wcnt[w][e];
+        a.src[q] = p / a.topk;
+      }
+      a.pos[p] = q;
+    }
+    __syncthreads();
+    if (t < a.E) {
+      int add = 0;
+      for (int w = 0; w < kChunkWaves; ++w) add += s_wcnt[w][t];
+      s_base[t] += add;
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void moe_prefill_act_kernel(const float* __restrict__ G,
+                                                              const float* __restrict__ U,
+                                                              _Float16* __restrict__ h,
+                                                              const int* __restrict__ counts,
+                                                              int I) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)counts[1] * I) return;
+  const float g = G[idx];
+  h[idx] = (_Float16)(g / (1.0f + expf(-g)) * U[idx]);
+}
+
+__global__ __launch_bounds__(256) void moe_prefill_combine_kernel(
+    const float* __restrict__ D, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    float* __restrict__ out, int T, int H, int topk) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (size_t)T * H) return;
+  const int t = (int)(idx / H);
+  const int n = (int)(idx - (size_t)t * H);
+  float acc = 0.0f;
+  for (int s = 0; s < topk; ++s) {
+    const int q = pos[t * topk + s];
+    if (q >= 0) acc = __builtin_fmaf(w[t * topk + s], D[(size_t)q * H + n], acc);
+  }
+  out[idx] = acc;
+}
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+}  // namespace
+
+MoePrefillPlan plan_moe_prefill(int T, int H, int I, int E, int topk) {
+  MoePrefillPlan p{};
+  const size_t np = (size_t)T * topk;
+  p.max_tiles = (int)((np + kGemmRows - 1) / kGemmRows + (np < (size_t)E ? np : (size_t)E));
+  size_t off = 0;
+  p.off_src = off;
+  off += align256(np * 4);
+  p.off_pos = off;
+  off += align256(np * 4);
+  p.off_tiles = off;
+  off += align256((size_t)p.max_tiles * 16);
+  p.off_counts = off;
+  off += 256;
+  p.off_g = off;
+  off += align256(np * I * 4);
+  p.off_u = off;
+  off += align256(np * I * 4);
+  p.off_h = off;
+  off += align256(np * I * 2);
+  p.off_d = off;
+  off += align256(np * H * 4);
+  p.ws_bytes = off;
+  return p;
+}
+
+hipError_t launch_moe_prefill(const uint16_t* x16, const uint8_t* Wg, const uint8_t* Wu,
+                              const uint8_t* Wd, const int32_t* ids, const float* w, float* out,
+                              int T, int H, int I, int E, int topk, void* ws,
+                              const MoePrefillPlan& p, hipStream_t st) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* src = reinterpret_cast<int32_t*>(base + p.off_src);
+  int32_t* pos = reinterpret_cast<int32_t*>(base + p.off_pos);
+  int4* tiles = reinterpret_cast<int4*>(base + p.off_tiles);
+  int* counts = reinterpret_cast<int*>(base + p.off_counts);
+  float* G = reinterpret_cast<float*>(base + p.off_g);
+  float* U = reinterpret_cast<float*>(base + p.off_u);
+  _Float16* h = reinterpret_cast<_Float16*>(base + p.off_h);
+  float* D = reinterpret_cast<float*>(base + p.off_d);
+  const int npairs = T * topk;
+  const size_t mat = (size_t)H * (I / kBlockWeights) * kBlockBytes;
+
+  PrefillRoute r{ids, npairs, E, topk, src, pos, tiles, counts};
+  hipLaunchKernelGGL(moe_prefill_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, r);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_gemm_grouped(x16, T, Wg, mat, G, I, H, tiles, counts, p.max_tiles, src, st);
+  if (err != hipSuccess) return err;
+  err = launch_gemm_grouped(x16, T, Wu, mat, U, I, H, tiles, counts, p.max_tiles, src, st);
+  if (err != hipSuccess) return err;
+  const size_t nh = (size_t)npairs * I;
+  hipLaunchKernelGGL(moe_prefill_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0,
+                     st, G, U, h, counts, I);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  err = launch_gemm_grouped(reinterpret_cast<const uint16_t*>(h), npairs, Wd, mat, D, H, I, tiles,
+                            counts, p.max_tiles, nullptr, st);
+  if (err != hipSuccess) return err;
+  const size_t total = (size_t)T * H;
+  hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+                     0, st, D, pos, w, out, T, H, topk);
+  return hipGetLastError();
+}
+
+}  // namespace q4

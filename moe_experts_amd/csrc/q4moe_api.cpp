@@ -64,6 +64,18 @@ int check_router_shape(int T, int H, int E, int topk, int n_shared) {
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
+int check_prefill_shape(int T, int H, int I, int E, int topk) {
+  if (T <= 0 || H <= 0 || I <= 0 || E <= 0 || topk <= 0) return Q4_EINVAL;
+  if (H % 128 != 0 || I % 128 != 0 || T > Q4_MOE_PREFILL_MAX_T || topk > Q4_MOE_MAX_TOPK ||
+      E > Q4_MOE_MAX_E)
+    return Q4_ESHAPE;
+  const long long np = (long long)T * topk;
+  if ((long long)H * (I / 32) * 18 > kMaxBytes || (long long)T * H * 2 > kMaxBytes ||
+      np * I * 4 > kMaxBytes || np * H * 4 > kMaxBytes)
+    return Q4_ETOOBIG;
+  return Q4_OK;
+}
+
 // Layer workspace: router partials, logits, ids, weights, then the decode's.
 struct LayerWs {
   size_t off_logits, off_ids, off_w, off_moe, bytes;
@@ -222,6 +234,31 @@ int moe_q4_0_layer(const float* x, const float* Wr, const q4_0_block* Wg, const 
                                  reinterpret_cast<const uint8_t*>(Wu),
                                  reinterpret_cast<const uint8_t*>(Wd), ids, w, out,
                                  base + l.off_moe, p, st));
+}
+
+size_t moe_q4_0_prefill_workspace_bytes(int T, int H, int I, int E, int topk) {
+  if (check_prefill_shape(T, H, I, E, topk) != Q4_OK) return 0;
+  return q4::plan_moe_prefill(T, H, I, E, topk).ws_bytes;
+}
+
+int moe_q4_0_prefill(const uint16_t* x16, const q4_0_block* Wg, const q4_0_block* Wu,
+                     const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
+                     float* out, int T, int H, int I, int E, int topk, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!x16 || !Wg || !Wu || !Wd || !topk_ids || !topk_w || !out) return Q4_EINVAL;
+  int rc = check_prefill_shape(T, H, I, E, topk);
+  if (rc != Q4_OK) return rc;
+  if (!aligned(x16, 16) || !aligned(Wg, 4) || !aligned(Wu, 4) || !aligned(Wd, 4) ||
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(out, 4))
+    return Q4_EALIGN;
+  const q4::MoePrefillPlan p = q4::plan_moe_prefill(T, H, I, E, topk);
+  rc = check_ws(ws, ws_bytes, p.ws_bytes);
+  if (rc != Q4_OK) return rc;
+  return from_hip(q4::launch_moe_prefill(x16, reinterpret_cast<const uint8_t*>(Wg),
+                                         reinterpret_cast<const uint8_t*>(Wu),
+                                         reinterpret_cast<const uint8_t*>(Wd), topk_ids, topk_w,
+                                         out, T, H, I, E, topk, ws, p,
+                                         static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -170,3 +170,23 @@ def test_q8_gemv_rejects_bad_arguments(lib, args, code):
     lib.q8_0_gemv_workspace_bytes.restype = ctypes.c_size_t
     assert lib.q8_0_gemv_workspace_bytes(1, 4096, 4096) > 0
     assert lib.q8_0_gemv_workspace_bytes(9, 4096, 4096) == 0
+
+
+def test_moe_prefill_rejects_bad_arguments(lib):
+    f = lib.moe_q4_0_prefill
+    f.argtypes = [ctypes.c_void_p] * 7 + [ctypes.c_int] * 5 + [ctypes.c_void_p, ctypes.c_size_t,
+                                                                ctypes.c_void_p]
+    ws = lib.moe_q4_0_prefill_workspace_bytes
+    ws.restype = ctypes.c_size_t
+    ws.argtypes = [ctypes.c_int] * 5
+    ok = (FAKE,) * 7
+    assert f(None, *ok[1:], 64, 5120, 1536, 160, 6, None, 0, None) == -1
+    assert f(*ok, 64, 5120, 1504, 160, 6, None, 0, None) == -2     # I % 128
+    assert f(*ok, 64, 5184, 1536, 160, 6, None, 0, None) == -2     # H % 128
+    assert f(*ok, 65537, 5120, 1536, 160, 6, None, 0, None) == -2  # T > 65536
+    assert f(*ok, 64, 5120, 1536, 160, 9, None, 0, None) == -2     # topk > 8
+    assert f(FAKE + 8, *ok[1:], 64, 5120, 1536, 160, 6, None, 0, None) == -3
+    assert f(*ok, 64, 5120, 1536, 160, 6, None, 0, None) == -4
+    assert f(*ok, 60000, 5120, 1536, 160, 8, None, 0, None) == -6  # down rows > 2 GiB
+    assert ws(2048, 5120, 1536, 160, 6) > 2048 * 6 * (5120 + 1536) * 4
+    assert ws(64, 5120, 1504, 160, 6) == 0

@@ -1,0 +1,79 @@
+"""GPU parity of moe_q4_0_prefill (experts as grouped GEMMs on the fp16 matrix
+cores) against the CPU oracle, which takes the same fp16 activations and keeps
+every product and sum in double. Tolerance: the prefill GEMM's relative bound,
+1e-2 * sum_slot |w| * sum_k |h_k * Wd[k][n]| + 1e-6 (each dequantized weight
+and h are rounded to fp16 on the GPU)."""
+import numpy as np
+import pytest
+
+import oracle
+from moe_experts_amd import datagen
+from tests.gpu_util import check_tol, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+
+
+def prefill_gpu(x16, dw, ids, w, I, E):
+    from moe_experts_amd import moe_q4_0_prefill
+    return to_host(moe_q4_0_prefill(to_dev(x16), *dw, to_dev(ids.astype(np.int32)),
+                                    to_dev(w.astype(np.float32)), I, E))
+
+
+def experts(seed, H, I, E):
+    Wg = np.stack([datagen.q4_0_random(seed + 3 * e, H, I) for e in range(E)])
+    Wu = np.stack([datagen.q4_0_random(seed + 3 * e + 1, H, I) for e in range(E)])
+    Wd = np.stack([datagen.q4_0_random(seed + 3 * e + 2, I, H) for e in range(E)])
+    return (Wg, Wu, Wd), (to_dev(Wg), to_dev(Wu), to_dev(Wd))
+
+
+# one token; several tokens per expert; more than one 512-pair ranking pass
+# and several 256-row tiles per expert; every slot on one expert (duplicates,
+# 3 tiles of one expert); wide I
+@pytest.mark.parametrize("T,H,I,E,topk", [(1, 128, 128, 3, 1), (300, 256, 128, 6, 2),
+                                          (513, 384, 256, 9, 6), (70, 128, 384, 1, 8),
+                                          (40, 256, 640, 20, 4)])
+def test_prefill_small_match_oracle(T, H, I, E, topk):
+    x16 = datagen.to_f16(datagen.activations(T + H + I, T, H))
+    (Wg, Wu, Wd), dw = experts(50 * E + I, H, I, E)
+    if E > 1:
+        ids, w, _ = datagen.routing(T + E + topk, T, E, topk)
+    else:
+        ids = np.zeros((T, topk), dtype=np.int32)
+        w = np.random.Generator(np.random.PCG64(T)).random((T, topk)).astype(np.float32)
+    got = prefill_gpu(x16, dw, ids, w, I, E)
+    ref, bnd, _ = oracle.moe_decode(x16.astype(np.float32), Wg, Wu, Wd, ids, w, H, I, E)
+    check_tol(got, ref, bnd, TOL, f"T={T} E={E} topk={topk}")
+    assert (prefill_gpu(x16, dw, ids, w, I, E) == got).all()   # deterministic
+
+
+def test_prefill_invalid_and_duplicate_ids():
+    T, H, I, E, topk = 33, 128, 128, 4, 3
+    x16 = datagen.to_f16(datagen.activations(5, T, H))
+    (Wg, Wu, Wd), dw = experts(9, H, I, E)
+    g = np.random.Generator(np.random.PCG64(6))
+    ids = g.integers(0, E, size=(T, topk)).astype(np.int32)
+    ids[0, :] = 2          # a token that picks one expert three times
+    ids[1, 1] = -1         # invalid ids contribute zero
+    ids[2, 2] = E + 5
+    ids[3, :] = -3         # a token with no valid slot: zeros
+    w = g.random((T, topk)).astype(np.float32)
+    got = prefill_gpu(x16, dw, ids, w, I, E)
+    ref, bnd, _ = oracle.moe_decode(x16.astype(np.float32), Wg, Wu, Wd, ids, w, H, I, E)
+    check_tol(got, ref, bnd, TOL, "invalid/duplicate ids")
+    assert (got[3] == 0).all()
+
+
+def test_prefill_dsv2_shape():
+    c = datagen.MOE_DSV2
+    H, I, E, topk = c["H"], c["I"], c["E"], c["topk"]
+    T = 256
+    ids, w, _ = datagen.routing(5301, T, E, topk)
+    used = sorted(set(ids.ravel().tolist()))
+    Wg, Wu, Wd = datagen.moe_experts(H, I, E, experts=used)
+    x16 = datagen.to_f16(datagen.activations(5101, T, H))
+    got = prefill_gpu(x16, (to_dev(Wg), to_dev(Wu), to_dev(Wd)), ids, w, I, E)
+    for t in (0, 77, T - 1):
+        ref, bnd, _ = oracle.moe_decode(x16[t:t + 1].astype(np.float32), Wg, Wu, Wd,
+                                        ids[t:t + 1], w[t:t + 1], H, I, E)
+        check_tol(got[t:t + 1], ref, bnd, TOL, f"dsv2 prefill token {t}")
