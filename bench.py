@@ -473,6 +473,42 @@ def bench_moe(torch, dev, steps, warmup):
                       "unique_experts": round(float(U), 2)}
         log(f"[moe] {label}: {res[label]}")
     res.update(bench_moe_layer(torch, dev, steps, warmup, dW))
+    res.update(bench_moe_prefill(torch, dev, steps, warmup, routed))
+    return res
+
+
+def bench_moe_prefill(torch, dev, steps, warmup, routed):
+    """moe_q4_0_prefill: 2048 prompt tokens, top-6 of the 160 routed experts
+    (uniform routing), experts as grouped GEMMs on the fp16 matrix cores.
+    Useful flops: 3 products of 2*H*I per valid (token, slot) pair."""
+    from moe_experts_amd import datagen, moe_q4_0_prefill, moe_q4_0_prefill_workspace_bytes
+    c = datagen.MOE_DSV2
+    H, I, E, topk = c["H"], c["I"], c["E"], c["topk"]
+    T = 2048
+    x16 = torch.from_numpy(datagen.to_f16(datagen.activations(5101, T, H))).to(dev)
+    routes = []
+    for r in range(4):
+        ids, w, _ = datagen.routing(5301 + 1000 * r, T, E, topk)
+        routes.append((torch.from_numpy(ids).to(dev), torch.from_numpy(w).to(dev)))
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.zeros(moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk), dtype=torch.uint8,
+                     device=dev)
+    layers = len(routed)
+
+    def call(r):
+        g, u, dd = routed[r % layers]
+        ids, w = routes[r % len(routes)]
+        moe_q4_0_prefill(x16, g, u, dd, ids, w, I, E, out=out, ws=ws)
+
+    for r in range(warmup):
+        call(r)
+    graphs = [capture(torch, lambda r=r: call(r)) for r in range(4)]
+    dt = time_graph(torch, graphs, max(steps // 2, 8), 1)
+    flops = T * topk * 3 * 2.0 * H * I
+    tf = flops / dt / 1e12
+    res = {"prefill_t2048": {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 1),
+                             "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}}
+    log(f"[moe] prefill_t2048: {res['prefill_t2048']}")
     return res
 
 

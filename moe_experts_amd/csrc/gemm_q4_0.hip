@@ -211,11 +211,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_generic_kernel(GemmArg
 // Aligned-shape kernel
 // ---------------------------------------------------------------------------
 namespace fast {
-constexpr int BM = 256, BN = 128, BK = 64;
-static_assert(BM == kGemmRows, "grouped m-tiles are one workgroup tile tall");
+// Tile heights: 256 rows for a plain GEMM, 128 for expert-grouped m-tiles
+// (a prefill expert has tens to hundreds of rows).
+constexpr int kDenseBM = 256, kGroupedBM = kGemmRows;
+constexpr int BN = 128, BK = 64;
 constexpr int kXStages = 3, kRStages = 4;
-constexpr int kXChunks = BM * BK / 8;                     // 16-byte chunks per X stage: 2048
-constexpr int kXBytes = kXChunks * 16;                    // 32 KiB
 constexpr int kRowBytes = (BN / kBlockWeights) * kBlockBytes;  // 72 bytes of raw row segment
 constexpr int kRowWords = kRowBytes / 4;                  // 18 dwords (copied 4 bytes at a time)
 constexpr int kRowPitch = kRowBytes + 4;                  // LDS row pitch: one pad dword
@@ -223,12 +223,20 @@ constexpr int kRWords = BK * (kRowWords + 1);             // 1216 dword slots, p
 constexpr int kRInstr = (kRWords + kGemmThreads - 1) / kGemmThreads;  // 5
 constexpr int kRBytes = kRInstr * kGemmThreads * 4;       // 5 KiB
 constexpr int kBBytes = BN * BK * 2;                      // 16 KiB fp16 tile
-constexpr int kXInstr = kXChunks / kGemmThreads;          // 8
-constexpr int kGroup = kXInstr + kRInstr;                 // copies issued per step
 constexpr int kUnits = BN * BK / 16;                      // dequant units (2 rows x 8 columns)
 constexpr int kUL = kUnits / kGemmThreads;                // 2 per producer lane
-constexpr int kLdsBytes = kXStages * kXBytes + kRStages * kRBytes + 2 * kBBytes;
-static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+
+// The X stage and what depends on the tile height BM.
+template <int BM>
+struct XCfg {
+  static constexpr int kXChunks = BM * BK / 8;            // 16-byte chunks per stage: 2048 at 256
+  static constexpr int kXBytes = kXChunks * 16;           // 32 KiB at 256 rows
+  static constexpr int kXInstr = kXChunks / kGemmThreads; // 8 at 256 rows
+  static constexpr int kGroup = kXInstr + kRInstr;        // copies issued per step
+  static constexpr int kLdsBytes = kXStages * kXBytes + kRStages * kRBytes + 2 * kBBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+  static_assert(BM % 128 == 0, "4 consumer waves of 32-row multiples");
+};
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -249,12 +257,17 @@ struct Args {
 
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-__device__ __forceinline__ uint8_t* xstage(uint8_t* lds, int s) { return lds + s * kXBytes; }
-__device__ __forceinline__ uint8_t* rstage(uint8_t* lds, int s) {
-  return lds + kXStages * kXBytes + s * kRBytes;
+template <int BM>
+__device__ __forceinline__ uint8_t* xstage(uint8_t* lds, int s) {
+  return lds + s * XCfg<BM>::kXBytes;
 }
+template <int BM>
+__device__ __forceinline__ uint8_t* rstage(uint8_t* lds, int s) {
+  return lds + kXStages * XCfg<BM>::kXBytes + s * kRBytes;
+}
+template <int BM>
 __device__ __forceinline__ uint8_t* bstage(uint8_t* lds, int s) {
-  return lds + kXStages * kXBytes + kRStages * kRBytes + s * kBBytes;
+  return lds + kXStages * XCfg<BM>::kXBytes + kRStages * kRBytes + s * kBBytes;
 }
 
 // LDS tiles hold rows of 64 halves (128 bytes = 8 chunks of 16 bytes); chunk
@@ -295,7 +308,9 @@ __device__ __forceinline__ void lds_barrier() {
 // Dequant: per unit, the offsets of the scale and of the aligned nibble
 // dwords inside a raw stage, the alignbyte shift, and the store offsets of
 // its four column pairs inside a B tile (column n+1 is 128 bytes after n).
+template <int BM>
 struct Producer {
+  static constexpr int kXInstr = XCfg<BM>::kXInstr;
   __amdgpu_buffer_rsrc_t rx, rb;
   uint32_t xoff[kXInstr], roff[kRInstr];
   uint32_t wslot;                 // wave's first DMA slot byte offset (uniform)
@@ -356,7 +371,7 @@ struct Producer {
     constexpr uint32_t kOut = 0x80000000u;
     const bool valid = ks < nk;
     const uint32_t so = valid ? (uint32_t)ks * x_step : 0u;
-    uint8_t* dst = xstage(lds, ks % kXStages) + wslot;
+    uint8_t* dst = xstage<BM>(lds, ks % kXStages) + wslot;
 #pragma unroll
     for (int i = 0; i < kXInstr; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + i * kGemmThreads * 16), 16,
@@ -366,7 +381,7 @@ struct Producer {
     constexpr uint32_t kOut = 0x80000000u;
     const bool valid = ks < nk;
     const uint32_t so = valid ? (uint32_t)ks * r_step : 0u;
-    uint8_t* dst = rstage(lds, ks % kRStages) + wslot / 4;
+    uint8_t* dst = rstage<BM>(lds, ks % kRStages) + wslot / 4;
 #pragma unroll
     for (int i = 0; i < kRInstr; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + i * kGemmThreads * 4), 4,
@@ -416,7 +431,9 @@ struct Producer {
 // 512 lanes: waves 0-3 contract (MFMA only), waves 4-7 produce (copies and
 // dequantization). Both roles pass one barrier per K step, so a step's
 // dequant (VALU) runs on the same SIMDs while the matrix cores run the MFMAs.
+template <int BM>
 __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
+  constexpr int kGroup = XCfg<BM>::kGroup;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int m0, rows, tn;
   const uint8_t* B = g.B;
@@ -442,7 +459,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 
   if (wave >= 4) {
     // ------------------------------------------------------------ producer
-    Producer pr;
+    Producer<BM> pr;
     pr.init(g, B, m0, rows, j0, (int)threadIdx.x - kGemmThreads);
     // Prologue: X(0), raw(0), raw(1) | X(1), raw(2); then raw(0) -> B(0).
     pr.issue_x(lds, 0);
@@ -453,7 +470,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup + kRInstr));  // X(0), raw(0) landed
     lds_barrier();                                           // barrier A
-    pr.dequant(rstage(lds, 0), bstage(lds, 0));
+    pr.dequant(rstage<BM>(lds, 0), bstage<BM>(lds, 0));
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);  // raw(1); B(0) stores done
     lds_barrier();                                           // barrier B: X(0), B(0) ready
     for (int ks = 0; ks < g.nk; ++ks) {
@@ -464,7 +481,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
       __builtin_amdgcn_sched_barrier(0);
       // B(ks+1) from raw(ks+1); on the last step the raw stage holds
       // out-of-range zeros and the tile is never read
-      pr.dequant(rstage(lds, (ks + 1) % kRStages), bstage(lds, (ks + 1) & 1));
+      pr.dequant(rstage<BM>(lds, (ks + 1) % kRStages), bstage<BM>(lds, (ks + 1) & 1));
       // X(ks+1), raw(ks+2) (issued one step ago) landed; B(ks+1) stores done
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);
       lds_barrier();
@@ -475,10 +492,11 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 
   // -------------------------------------------------------------- consumer
   const int lane = threadIdx.x & 63;
-  const int wm = wave;  // rows wm*64 .. +64, all 128 columns
-  float16v acc[2][4];
+  constexpr int MI = BM / 128;  // 32-row accumulator blocks per consumer wave
+  const int wm = wave;           // rows wm*(BM/4) .. +BM/4, all 128 columns
+  float16v acc[MI][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -486,15 +504,15 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   lds_barrier();  // barrier A
   lds_barrier();  // barrier B
   for (int ks = 0; ks < g.nk; ++ks) {
-    const uint8_t* xs = xstage(lds, ks % kXStages);
-    const uint8_t* bs = bstage(lds, ks & 1);
+    const uint8_t* xs = xstage<BM>(lds, ks % kXStages);
+    const uint8_t* bs = bstage<BM>(lds, ks & 1);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int kc = 2 * kk + (lane >> 5);  // 16-byte k chunk of this lane
-      half8 af[2], bf[4];
+      half8 af[MI], bf[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int r = wm * 64 + i * 32 + (lane & 31);
+      for (int i = 0; i < MI; ++i) {
+        const int r = wm * (BM / 4) + i * 32 + (lane & 31);
         af[i] = *reinterpret_cast<const half8*>(xs + (r * 8 + (kc ^ swz_x(r))) * 16);
       }
 #pragma unroll
@@ -503,7 +521,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
         bf[j] = *reinterpret_cast<const half8*>(bs + n * (BK * 2) + ((kc ^ swz_b(n)) << 4));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
@@ -515,13 +533,13 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   // Accumulator layout of a 32 x 32 fp32 MFMA result: lane l holds column
   // l % 32; register r holds row 8*(r/4) + 4*(l/32) + r%4.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int col = j0 * kBlockWeights + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int rr = wm * (BM / 4) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (rr < rows) g.Y[(size_t)(m0 + rr) * g.N + col] = acc[i][j][r];
       }
     }
@@ -559,10 +577,11 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
     f.n_tiles = nullptr;
     f.src = nullptr;
     f.mat_bytes = 0;
-    const long long tiles = (long long)((M + fast::BM - 1) / fast::BM) * f.tiles_n;
+    constexpr int BM = fast::kDenseBM;
+    const long long tiles = (long long)((M + BM - 1) / BM) * f.tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fast::gemm_q4_0_kernel, dim3((unsigned)tiles), dim3(2 * kGemmThreads),
-                       fast::kLdsBytes, st, f);
+    hipLaunchKernelGGL(fast::gemm_q4_0_kernel<BM>, dim3((unsigned)tiles), dim3(2 * kGemmThreads),
+                       fast::XCfg<BM>::kLdsBytes, st, f);
     return hipGetLastError();
   }
   const int tiles_m = (M + BM - 1) / BM;
@@ -595,8 +614,9 @@ hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, 
   const long long grid = (long long)max_tiles * f.tiles_n;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(fast::gemm_q4_0_kernel, dim3((unsigned)grid), dim3(2 * kGemmThreads),
-                     fast::kLdsBytes, st, f);
+  constexpr int BM = fast::kGroupedBM;
+  hipLaunchKernelGGL(fast::gemm_q4_0_kernel<BM>, dim3((unsigned)grid), dim3(2 * kGemmThreads),
+                     fast::XCfg<BM>::kLdsBytes, st, f);
   return hipGetLastError();
 }
 

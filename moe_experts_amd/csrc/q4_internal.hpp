@@ -69,7 +69,7 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
 // Expert-grouped mode of the aligned prefill kernel (gemm_q4_0.hip): m-tiles
 // (expert, first output row, rows <= kGemmRows) from a device list, X rows
 // gathered through src (null: identity), B = consecutive K x N matrices.
-constexpr int kGemmRows = 256;  // rows of one m-tile
+constexpr int kGemmRows = 128;  // rows of one grouped m-tile
 bool gemm_grouped_supported(int N, int K);
 hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, size_t mat_bytes,
                                float* Y, int N, int K, const int4* tiles, const int* n_tiles,
