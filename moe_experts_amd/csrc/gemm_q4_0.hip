@@ -363,29 +363,26 @@ struct Producer {
     }
   }
 
-  // Copies of K step ks: X into stage ks % 3, raw B into stage ks % 4. A
-  // step past the end reads out of range in every lane (zeros, no memory
-  // access; its scalar offset is zero, so no lane offset plus scalar offset
-  // can point past the buffer).
+  // Copies of K step ks: X into stage ks % 3, raw B into stage ks % 4. The
+  // copies issued past the last step (ks >= nk) repeat step nk - 1: they land
+  // in an X stage of a step that is never computed, or in a raw stage whose
+  // B tile is never read, so no lane needs a select to keep its offset in
+  // range.
   __device__ __forceinline__ void issue_x(uint8_t* lds, int ks) const {
-    constexpr uint32_t kOut = 0x80000000u;
-    const bool valid = ks < nk;
-    const uint32_t so = valid ? (uint32_t)ks * x_step : 0u;
+    const uint32_t so = (uint32_t)min(ks, nk - 1) * x_step;
     uint8_t* dst = xstage<BM>(lds, ks % kXStages) + wslot;
 #pragma unroll
     for (int i = 0; i < kXInstr; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + i * kGemmThreads * 16), 16,
-                                               valid ? xoff[i] : kOut, so, 0, 0);
+                                               xoff[i], so, 0, 0);
   }
   __device__ __forceinline__ void issue_r(uint8_t* lds, int ks) const {
-    constexpr uint32_t kOut = 0x80000000u;
-    const bool valid = ks < nk;
-    const uint32_t so = valid ? (uint32_t)ks * r_step : 0u;
+    const uint32_t so = (uint32_t)min(ks, nk - 1) * r_step;
     uint8_t* dst = rstage<BM>(lds, ks % kRStages) + wslot / 4;
 #pragma unroll
     for (int i = 0; i < kRInstr; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + i * kGemmThreads * 4), 4,
-                                               valid ? roff[i] : kOut, so, 0, 0);
+                                               roff[i], so, 0, 0);
   }
 
   // Raw stage -> fp16 B tile, w = fp16((q - 8) * d).
@@ -479,8 +476,8 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
       pr.issue_x(lds, ks + 2);
       pr.issue_r(lds, ks + 3);
       __builtin_amdgcn_sched_barrier(0);
-      // B(ks+1) from raw(ks+1); on the last step the raw stage holds
-      // out-of-range zeros and the tile is never read
+      // B(ks+1) from raw(ks+1); on the last step the raw stage holds a
+      // repeat of the last step and the tile is never read
       pr.dequant(rstage<BM>(lds, (ks + 1) % kRStages), bstage<BM>(lds, (ks + 1) & 1));
       // X(ks+1), raw(ks+2) (issued one step ago) landed; B(ks+1) stores done
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);
