@@ -489,13 +489,20 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 
   // -------------------------------------------------------------- consumer
   const int lane = threadIdx.x & 63;
-  constexpr int MI = BM / 128;  // 32-row accumulator blocks per consumer wave
-  const int wm = wave;           // rows wm*(BM/4) .. +BM/4, all 128 columns
-  float16v acc[MI][4];
+  // Consumer wave tiles: 256-row tiles give each wave 64 rows x all 128
+  // columns; 128-row tiles a 2 x 2 grid of 64 x 64 (each wave then reads half
+  // the B tile instead of all of it: 64 instead of 80 KB of LDS reads per step).
+  constexpr int WGR = BM == 256 ? 4 : 2;  // waves along the rows
+  constexpr int WR = BM / WGR;            // rows per wave (64)
+  constexpr int WC = BN / (4 / WGR);      // columns per wave (128 or 64)
+  constexpr int MI = WR / 32, NJ = WC / 32;
+  const int wm = wave % WGR;
+  const int wn = wave / WGR;
+  float16v acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   lds_barrier();  // barrier A
@@ -506,21 +513,21 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int kc = 2 * kk + (lane >> 5);  // 16-byte k chunk of this lane
-      half8 af[MI], bf[4];
+      half8 af[MI], bf[NJ];
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const int r = wm * (BM / 4) + i * 32 + (lane & 31);
+        const int r = wm * WR + i * 32 + (lane & 31);
         af[i] = *reinterpret_cast<const half8*>(xs + (r * 8 + (kc ^ swz_x(r))) * 16);
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = j * 32 + (lane & 31);
+      for (int j = 0; j < NJ; ++j) {
+        const int n = wn * WC + j * 32 + (lane & 31);
         bf[j] = *reinterpret_cast<const half8*>(bs + n * (BK * 2) + ((kc ^ swz_b(n)) << 4));
       }
 #pragma unroll
       for (int i = 0; i < MI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < NJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS reads done before the stage is reused
@@ -532,11 +539,11 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int col = j0 * kBlockWeights + j * 32 + (lane & 31);
+    for (int j = 0; j < NJ; ++j) {
+      const int col = j0 * kBlockWeights + wn * WC + j * 32 + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rr = wm * (BM / 4) + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int rr = wm * WR + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (rr < rows) g.Y[(size_t)(m0 + rr) * g.N + col] = acc[i][j][r];
       }
     }
