@@ -166,7 +166,7 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
  *   out[t] = sum_{s < topk} topk_w[t][s] * Wd_e ( SiLU(x_t . Wg_e) * (x_t . Wu_e) )
  *   x16      fp16 [T][H] (the caller rounds its activations), 16-byte aligned
  *   Wg, Wu, Wd, topk_ids, topk_w, out   as in moe_q4_0_decode; weights 4-byte
- *            aligned
+ *            aligned, out 16-byte aligned
  *   1 <= T <= Q4_MOE_PREFILL_MAX_T, 1 <= topk <= Q4_MOE_MAX_TOPK,
  *   1 <= E <= Q4_MOE_MAX_E, H % 128 == 0, I % 128 == 0.
  * Pairs are sorted by expert on the device (stable); each expert's rows go

@@ -129,30 +129,60 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
   }
 }
 
+// Four consecutive values per thread (I % 4 == 0; 16-byte loads, 8-byte stores).
 __global__ __launch_bounds__(256) void moe_prefill_act_kernel(const float* __restrict__ G,
                                                               const float* __restrict__ U,
                                                               _Float16* __restrict__ h,
                                                               const int* __restrict__ counts,
                                                               int I) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)counts[1] * I) return;
-  const float g = G[idx];
-  h[idx] = (_Float16)(g / (1.0f + expf(-g)) * U[idx]);
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i4 >= (size_t)counts[1] * (I / 4)) return;
+  const float4 g = reinterpret_cast<const float4*>(G)[i4];
+  const float4 u = reinterpret_cast<const float4*>(U)[i4];
+  half4 r;
+  r[0] = (_Float16)(g.x / (1.0f + expf(-g.x)) * u.x);
+  r[1] = (_Float16)(g.y / (1.0f + expf(-g.y)) * u.y);
+  r[2] = (_Float16)(g.z / (1.0f + expf(-g.z)) * u.z);
+  r[3] = (_Float16)(g.w / (1.0f + expf(-g.w)) * u.w);
+  reinterpret_cast<half4*>(h)[i4] = r;
 }
 
+// Four consecutive outputs per thread (16-byte loads and stores; H % 4 == 0,
+// rows and out 16-byte aligned); every slot's sorted row and weight, then
+// every slot's four values, are loaded before the sum.
 __global__ __launch_bounds__(256) void moe_prefill_combine_kernel(
     const float* __restrict__ D, const int32_t* __restrict__ pos, const float* __restrict__ w,
     float* __restrict__ out, int T, int H, int topk) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (size_t)T * H) return;
-  const int t = (int)(idx / H);
-  const int n = (int)(idx - (size_t)t * H);
-  float acc = 0.0f;
-  for (int s = 0; s < topk; ++s) {
-    const int q = pos[t * topk + s];
-    if (q >= 0) acc = __builtin_fmaf(w[t * topk + s], D[(size_t)q * H + n], acc);
+  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+  const int H4 = H / 4;
+  if (i4 >= (size_t)T * H4) return;
+  const int t = (int)(i4 / H4);
+  const int n4 = (int)(i4 - (size_t)t * H4);
+  int q[Q4_MOE_MAX_TOPK];
+  float wv[Q4_MOE_MAX_TOPK];
+#pragma unroll
+  for (int s = 0; s < Q4_MOE_MAX_TOPK; ++s) {
+    const int p = t * topk + min(s, topk - 1);
+    q[s] = pos[p];
+    wv[s] = w[p];
   }
-  out[idx] = acc;
+  float4 d[Q4_MOE_MAX_TOPK];
+#pragma unroll
+  for (int s = 0; s < Q4_MOE_MAX_TOPK; ++s)
+    d[s] = (s < topk && q[s] >= 0)
+               ? reinterpret_cast<const float4*>(D + (size_t)q[s] * H)[n4]
+               : float4{0.0f, 0.0f, 0.0f, 0.0f};
+  float4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int s = 0; s < Q4_MOE_MAX_TOPK; ++s)
+    if (s < topk && q[s] >= 0) {
+      acc.x = __builtin_fmaf(wv[s], d[s].x, acc.x);
+      acc.y = __builtin_fmaf(wv[s], d[s].y, acc.y);
+      acc.z = __builtin_fmaf(wv[s], d[s].z, acc.z);
+      acc.w = __builtin_fmaf(wv[s], d[s].w, acc.w);
+    }
+  reinterpret_cast<float4*>(out)[i4] = acc;
 }
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
@@ -208,16 +238,16 @@ hipError_t launch_moe_prefill(const uint16_t* x16, const uint8_t* Wg, const uint
   if (err != hipSuccess) return err;
   err = launch_gemm_grouped(x16, T, Wu, mat, U, I, H, tiles, counts, p.max_tiles, src, st);
   if (err != hipSuccess) return err;
-  const size_t nh = (size_t)npairs * I;
-  hipLaunchKernelGGL(moe_prefill_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0,
+  const size_t nh4 = (size_t)npairs * I / 4;
+  hipLaunchKernelGGL(moe_prefill_act_kernel, dim3((unsigned)((nh4 + 255) / 256)), dim3(256), 0,
                      st, G, U, h, counts, I);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_gemm_grouped(reinterpret_cast<const uint16_t*>(h), npairs, Wd, mat, D, H, I, tiles,
                             counts, p.max_tiles, nullptr, st);
   if (err != hipSuccess) return err;
-  const size_t total = (size_t)T * H;
-  hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256),
+  const size_t total4 = (size_t)T * H / 4;
+  hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256),
                      0, st, D, pos, w, out, T, H, topk);
   return hipGetLastError();
 }

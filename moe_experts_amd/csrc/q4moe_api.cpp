@@ -249,7 +249,7 @@ int moe_q4_0_prefill(const uint16_t* x16, const q4_0_block* Wg, const q4_0_block
   int rc = check_prefill_shape(T, H, I, E, topk);
   if (rc != Q4_OK) return rc;
   if (!aligned(x16, 16) || !aligned(Wg, 4) || !aligned(Wu, 4) || !aligned(Wd, 4) ||
-      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(out, 4))
+      !aligned(topk_ids, 4) || !aligned(topk_w, 4) || !aligned(out, 16))
     return Q4_EALIGN;
   const q4::MoePrefillPlan p = q4::plan_moe_prefill(T, H, I, E, topk);
   rc = check_ws(ws, ws_bytes, p.ws_bytes);

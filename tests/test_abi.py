@@ -186,6 +186,7 @@ def test_moe_prefill_rejects_bad_arguments(lib):
     assert f(*ok, 65537, 5120, 1536, 160, 6, None, 0, None) == -2  # T > 65536
     assert f(*ok, 64, 5120, 1536, 160, 9, None, 0, None) == -2     # topk > 8
     assert f(FAKE + 8, *ok[1:], 64, 5120, 1536, 160, 6, None, 0, None) == -3
+    assert f(*ok[:6], FAKE + 4, 64, 5120, 1536, 160, 6, None, 0, None) == -3  # out not 16-B aligned
     assert f(*ok, 64, 5120, 1536, 160, 6, None, 0, None) == -4
     assert f(*ok, 60000, 5120, 1536, 160, 8, None, 0, None) == -6  # down rows > 2 GiB
     assert ws(2048, 5120, 1536, 160, 6) > 2048 * 6 * (5120 + 1536) * 4
