@@ -174,8 +174,7 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
  * rounded to fp16 before their products; sums are fp32. Ids outside [0, E)
  * contribute zero; slots are summed in order 0..topk-1.
  *   ws/ws_bytes: workspace of moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)
- *   bytes (the per-pair gate, up, h and down rows: about 14 * T * topk * max(H, I)
- *   bytes).
+ *   bytes (the per-pair h and down rows: about T * topk * (2 * I + 4 * H) bytes).
  * ------------------------------------------------------------------------- */
 size_t moe_q4_0_prefill_workspace_bytes(int T, int H, int I, int E, int topk);
 int moe_q4_0_prefill(const uint16_t* x16, const q4_0_block* Wg, const q4_0_block* Wu,

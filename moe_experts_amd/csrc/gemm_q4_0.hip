@@ -226,14 +226,18 @@ constexpr int kBBytes = BN * BK * 2;                      // 16 KiB fp16 tile
 constexpr int kUnits = BN * BK / 16;                      // dequant units (2 rows x 8 columns)
 constexpr int kUL = kUnits / kGemmThreads;                // 2 per producer lane
 
-// The X stage and what depends on the tile height BM.
-template <int BM>
+// The X stage and what depends on the tile height BM and on the number NM
+// of weight matrices a workgroup contracts with the same X tile (2: an
+// expert's gate and up matrices). LDS: [X stages][matrix 0: raw stages, B
+// tiles][matrix 1: ...].
+template <int BM, int NM>
 struct XCfg {
   static constexpr int kXChunks = BM * BK / 8;            // 16-byte chunks per stage: 2048 at 256
   static constexpr int kXBytes = kXChunks * 16;           // 32 KiB at 256 rows
   static constexpr int kXInstr = kXChunks / kGemmThreads; // 8 at 256 rows
-  static constexpr int kGroup = kXInstr + kRInstr;        // copies issued per step
-  static constexpr int kLdsBytes = kXStages * kXBytes + kRStages * kRBytes + 2 * kBBytes;
+  static constexpr int kGroup = kXInstr + NM * kRInstr;   // copies issued per step
+  static constexpr int kMatBytes = kRStages * kRBytes + 2 * kBBytes;
+  static constexpr int kLdsBytes = kXStages * kXBytes + NM * kMatBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
   static_assert(BM % 128 == 0, "4 consumer waves of 32-row multiples");
 };
@@ -253,21 +257,26 @@ struct Args {
   const int* n_tiles;
   const int32_t* src;
   size_t mat_bytes;
+  // Two matrices (gate B and up B1, same shape): the output is
+  // H = fp16(SiLU(X . B) * (X . B1)) instead of Y.
+  const uint8_t* B1;
+  _Float16* H;
 };
 
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
 
-template <int BM>
+template <int BM, int NM>
 __device__ __forceinline__ uint8_t* xstage(uint8_t* lds, int s) {
-  return lds + s * XCfg<BM>::kXBytes;
+  return lds + s * XCfg<BM, NM>::kXBytes;
 }
-template <int BM>
-__device__ __forceinline__ uint8_t* rstage(uint8_t* lds, int s) {
-  return lds + kXStages * XCfg<BM>::kXBytes + s * kRBytes;
+template <int BM, int NM>
+__device__ __forceinline__ uint8_t* rstage(uint8_t* lds, int m, int s) {
+  return lds + kXStages * XCfg<BM, NM>::kXBytes + m * XCfg<BM, NM>::kMatBytes + s * kRBytes;
 }
-template <int BM>
-__device__ __forceinline__ uint8_t* bstage(uint8_t* lds, int s) {
-  return lds + kXStages * XCfg<BM>::kXBytes + kRStages * kRBytes + s * kBBytes;
+template <int BM, int NM>
+__device__ __forceinline__ uint8_t* bstage(uint8_t* lds, int m, int s) {
+  return lds + kXStages * XCfg<BM, NM>::kXBytes + m * XCfg<BM, NM>::kMatBytes +
+         kRStages * kRBytes + s * kBBytes;
 }
 
 // LDS tiles hold rows of 64 halves (128 bytes = 8 chunks of 16 bytes); chunk
@@ -308,10 +317,10 @@ __device__ __forceinline__ void lds_barrier() {
 // Dequant: per unit, the offsets of the scale and of the aligned nibble
 // dwords inside a raw stage, the alignbyte shift, and the store offsets of
 // its four column pairs inside a B tile (column n+1 is 128 bytes after n).
-template <int BM>
+template <int BM, int NM>
 struct Producer {
-  static constexpr int kXInstr = XCfg<BM>::kXInstr;
-  __amdgpu_buffer_rsrc_t rx, rb;
+  static constexpr int kXInstr = XCfg<BM, NM>::kXInstr;
+  __amdgpu_buffer_rsrc_t rx, rb[NM];
   uint32_t xoff[kXInstr], roff[kRInstr];
   uint32_t wslot;                 // wave's first DMA slot byte offset (uniform)
   uint32_t x_step, r_step;        // bytes per K step in X and B (uniform)
@@ -319,13 +328,15 @@ struct Producer {
   uint32_t st[kUL][4];
   int nk;
 
-  __device__ __forceinline__ void init(const Args& g, const uint8_t* B, int m0, int rows, int j0,
-                                       int t) {
+  __device__ __forceinline__ void init(const Args& g, const uint8_t* const (&B)[NM], int m0,
+                                       int rows, int j0, int t) {
     constexpr uint32_t kOut = 0x80000000u;
     nk = g.nk;
     rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(g.X), (short)0,
                                            (int)((uint32_t)g.M * (uint32_t)g.K * 2u), 0x00020000);
-    rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B), (short)0,
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+      rb[m] = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(B[m]), (short)0,
                                            (int)((uint32_t)g.K * (uint32_t)g.NB * kBlockBytes),
                                            0x00020000);
     const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
@@ -370,7 +381,7 @@ struct Producer {
   // range.
   __device__ __forceinline__ void issue_x(uint8_t* lds, int ks) const {
     const uint32_t so = (uint32_t)min(ks, nk - 1) * x_step;
-    uint8_t* dst = xstage<BM>(lds, ks % kXStages) + wslot;
+    uint8_t* dst = xstage<BM, NM>(lds, ks % kXStages) + wslot;
 #pragma unroll
     for (int i = 0; i < kXInstr; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(dst + i * kGemmThreads * 16), 16,
@@ -378,11 +389,14 @@ struct Producer {
   }
   __device__ __forceinline__ void issue_r(uint8_t* lds, int ks) const {
     const uint32_t so = (uint32_t)min(ks, nk - 1) * r_step;
-    uint8_t* dst = rstage<BM>(lds, ks % kRStages) + wslot / 4;
 #pragma unroll
-    for (int i = 0; i < kRInstr; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(dst + i * kGemmThreads * 4), 4,
-                                               roff[i], so, 0, 0);
+    for (int m = 0; m < NM; ++m) {
+      uint8_t* dst = rstage<BM, NM>(lds, m, ks % kRStages) + wslot / 4;
+#pragma unroll
+      for (int i = 0; i < kRInstr; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[m], (lds_void_t*)(dst + i * kGemmThreads * 4),
+                                                 4, roff[i], so, 0, 0);
+    }
   }
 
   // Raw stage -> fp16 B tile, w = fp16((q - 8) * d).
@@ -428,12 +442,15 @@ struct Producer {
 // 512 lanes: waves 0-3 contract (MFMA only), waves 4-7 produce (copies and
 // dequantization). Both roles pass one barrier per K step, so a step's
 // dequant (VALU) runs on the same SIMDs while the matrix cores run the MFMAs.
-template <int BM>
+template <int BM, int NM>
 __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
-  constexpr int kGroup = XCfg<BM>::kGroup;
+  static_assert(NM == 1 || (NM == 2 && BM == 128), "gate and up together in 128-row tiles");
+  constexpr int kGroup = XCfg<BM, NM>::kGroup;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int m0, rows, tn;
-  const uint8_t* B = g.B;
+  const uint8_t* B[NM];
+  B[0] = g.B;
+  if constexpr (NM == 2) B[1] = g.B1;
   if (g.tiles) {
     // grouped: plain dispatch order (the live tiles come first; the XCD remap
     // would crowd them onto a few XCDs)
@@ -441,7 +458,8 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
     tn = blockIdx.x - tile * g.tiles_n;
     if (tile >= *g.n_tiles) return;  // the whole workgroup, before any barrier
     const int4 tl = g.tiles[tile];
-    B += (size_t)tl.x * g.mat_bytes;
+#pragma unroll
+    for (int m = 0; m < NM; ++m) B[m] += (size_t)tl.x * g.mat_bytes;
     m0 = tl.y;
     rows = tl.z;
   } else {
@@ -456,7 +474,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 
   if (wave >= 4) {
     // ------------------------------------------------------------ producer
-    Producer<BM> pr;
+    Producer<BM, NM> pr;
     pr.init(g, B, m0, rows, j0, (int)threadIdx.x - kGemmThreads);
     // Prologue: X(0), raw(0), raw(1) | X(1), raw(2); then raw(0) -> B(0).
     pr.issue_x(lds, 0);
@@ -465,9 +483,10 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
     pr.issue_x(lds, 1);
     pr.issue_r(lds, 2);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup + kRInstr));  // X(0), raw(0) landed
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup + NM * kRInstr));  // X(0), raw(0) landed
     lds_barrier();                                           // barrier A
-    pr.dequant(rstage<BM>(lds, 0), bstage<BM>(lds, 0));
+#pragma unroll
+    for (int m = 0; m < NM; ++m) pr.dequant(rstage<BM, NM>(lds, m, 0), bstage<BM, NM>(lds, m, 0));
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);  // raw(1); B(0) stores done
     lds_barrier();                                           // barrier B: X(0), B(0) ready
     for (int ks = 0; ks < g.nk; ++ks) {
@@ -478,7 +497,10 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
       __builtin_amdgcn_sched_barrier(0);
       // B(ks+1) from raw(ks+1); on the last step the raw stage holds a
       // repeat of the last step and the tile is never read
-      pr.dequant(rstage<BM>(lds, (ks + 1) % kRStages), bstage<BM>(lds, (ks + 1) & 1));
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+        pr.dequant(rstage<BM, NM>(lds, m, (ks + 1) % kRStages),
+                   bstage<BM, NM>(lds, m, (ks + 1) & 1));
       // X(ks+1), raw(ks+2) (issued one step ago) landed; B(ks+1) stores done
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGroup) & ~0x0f00);
       lds_barrier();
@@ -498,37 +520,45 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   constexpr int MI = WR / 32, NJ = WC / 32;
   const int wm = wave % WGR;
   const int wn = wave / WGR;
-  float16v acc[MI][NJ];
+  float16v acc[NM][MI][NJ];
 #pragma unroll
-  for (int i = 0; i < MI; ++i)
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[m][i][j][r] = 0.0f;
   lds_barrier();  // barrier A
   lds_barrier();  // barrier B
   for (int ks = 0; ks < g.nk; ++ks) {
-    const uint8_t* xs = xstage<BM>(lds, ks % kXStages);
-    const uint8_t* bs = bstage<BM>(lds, ks & 1);
+    const uint8_t* xs = xstage<BM, NM>(lds, ks % kXStages);
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
       const int kc = 2 * kk + (lane >> 5);  // 16-byte k chunk of this lane
-      half8 af[MI], bf[NJ];
+      half8 af[MI], bf[NM][NJ];
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int r = wm * WR + i * 32 + (lane & 31);
         af[i] = *reinterpret_cast<const half8*>(xs + (r * 8 + (kc ^ swz_x(r))) * 16);
       }
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = wn * WC + j * 32 + (lane & 31);
-        bf[j] = *reinterpret_cast<const half8*>(bs + n * (BK * 2) + ((kc ^ swz_b(n)) << 4));
+      for (int m = 0; m < NM; ++m) {
+        const uint8_t* bs = bstage<BM, NM>(lds, m, ks & 1);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int n = wn * WC + j * 32 + (lane & 31);
+          bf[m][j] = *reinterpret_cast<const half8*>(bs + n * (BK * 2) + ((kc ^ swz_b(n)) << 4));
+        }
       }
 #pragma unroll
-      for (int i = 0; i < MI; ++i)
+      for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            acc[m][i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[m][j], acc[m][i][j], 0, 0, 0);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS reads done before the stage is reused
     lds_barrier();
@@ -544,7 +574,15 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rr = wm * WR + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (rr < rows) g.Y[(size_t)(m0 + rr) * g.N + col] = acc[i][j][r];
+        if (rr >= rows) continue;
+        if constexpr (NM == 1) {
+          g.Y[(size_t)(m0 + rr) * g.N + col] = acc[0][i][j][r];
+        } else {
+          // gate and up of one expert: h = fp16(SiLU(gate) * up)
+          const float gt = acc[0][i][j][r];
+          g.H[(size_t)(m0 + rr) * g.N + col] =
+              (_Float16)(gt / (1.0f + expf(-gt)) * acc[1][i][j][r]);
+        }
       }
     }
 }
@@ -581,11 +619,13 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
     f.n_tiles = nullptr;
     f.src = nullptr;
     f.mat_bytes = 0;
+    f.B1 = nullptr;
+    f.H = nullptr;
     constexpr int BM = fast::kDenseBM;
     const long long tiles = (long long)((M + BM - 1) / BM) * f.tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fast::gemm_q4_0_kernel<BM>, dim3((unsigned)tiles), dim3(2 * kGemmThreads),
-                       fast::XCfg<BM>::kLdsBytes, st, f);
+    hipLaunchKernelGGL((fast::gemm_q4_0_kernel<BM, 1>), dim3((unsigned)tiles),
+                       dim3(2 * kGemmThreads), (fast::XCfg<BM, 1>::kLdsBytes), st, f);
     return hipGetLastError();
   }
   const int tiles_m = (M + BM - 1) / BM;
@@ -598,9 +638,12 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
 
 bool gemm_grouped_supported(int N, int K) { return K % fast::BK == 0 && N % fast::BN == 0; }
 
-hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, size_t mat_bytes,
-                               float* Y, int N, int K, const int4* tiles, const int* n_tiles,
-                               int max_tiles, const int32_t* src, hipStream_t st) {
+// Expert-grouped launches: one matrix (B1 null: Y fp32) or the gate and up
+// matrices together (B1 set: H = fp16(SiLU(X . B) * (X . B1))).
+hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, const uint8_t* B1,
+                               size_t mat_bytes, float* Y, _Float16* H, int N, int K,
+                               const int4* tiles, const int* n_tiles, int max_tiles,
+                               const int32_t* src, hipStream_t st) {
   fast::Args f;
   f.X = X;
   f.B = B;
@@ -615,12 +658,18 @@ hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, 
   f.n_tiles = n_tiles;
   f.src = src;
   f.mat_bytes = mat_bytes;
+  f.B1 = B1;
+  f.H = H;
   const long long grid = (long long)max_tiles * f.tiles_n;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
   constexpr int BM = fast::kGroupedBM;
-  hipLaunchKernelGGL(fast::gemm_q4_0_kernel<BM>, dim3((unsigned)grid), dim3(2 * kGemmThreads),
-                     fast::XCfg<BM>::kLdsBytes, st, f);
+  if (B1)
+    hipLaunchKernelGGL((fast::gemm_q4_0_kernel<BM, 2>), dim3((unsigned)grid),
+                       dim3(2 * kGemmThreads), (fast::XCfg<BM, 2>::kLdsBytes), st, f);
+  else
+    hipLaunchKernelGGL((fast::gemm_q4_0_kernel<BM, 1>), dim3((unsigned)grid),
+                       dim3(2 * kGemmThreads), (fast::XCfg<BM, 1>::kLdsBytes), st, f);
   return hipGetLastError();
 }
 

@@ -12,12 +12,12 @@
 //      kernel writes, per sorted row, the token it reads (src[q]), per pair its
 //      sorted row (pos[p], -1 for an id outside [0, E)), and the list of
 //      256-row m-tiles (expert, first row, rows) of every expert's rows.
-//   2. gate and up: the prefill GEMM kernel in its grouped mode (X rows
-//      gathered by src, the expert's Q4_0 matrix, fp32 rows G and U in sorted
-//      order).
-//   3. moe_prefill_act_kernel: h = fp16(SiLU(G) * U), sorted order.
-//   4. down: the grouped GEMM on h (rows in sorted order, no gather) -> D.
-//   5. moe_prefill_combine_kernel: out[t] = sum over slots 0..topk-1 of
+//   2. gate and up together: the prefill GEMM kernel in its grouped mode
+//      with two matrices (X rows gathered by src, the expert's gate and up
+//      Q4_0 matrices against the same X tile); its epilogue writes
+//      h = fp16(SiLU(gate) * up) in sorted order.
+//   3. down: the grouped GEMM on h (rows in sorted order, no gather) -> D.
+//   4. moe_prefill_combine_kernel: out[t] = sum over slots 0..topk-1 of
 //      w[t][s] * D[pos[t * topk + s]] (slot order; invalid slots skipped).
 // Precision: x is given in fp16 and h is rounded to fp16 for the down GEMM;
 // each dequantized weight is rounded to fp16 (the prefill GEMM's rule); all
@@ -129,25 +129,6 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
   }
 }
 
-// Four consecutive values per thread (I % 4 == 0; 16-byte loads, 8-byte stores).
-__global__ __launch_bounds__(256) void moe_prefill_act_kernel(const float* __restrict__ G,
-                                                              const float* __restrict__ U,
-                                                              _Float16* __restrict__ h,
-                                                              const int* __restrict__ counts,
-                                                              int I) {
-  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-  const size_t i4 = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (i4 >= (size_t)counts[1] * (I / 4)) return;
-  const float4 g = reinterpret_cast<const float4*>(G)[i4];
-  const float4 u = reinterpret_cast<const float4*>(U)[i4];
-  half4 r;
-  r[0] = (_Float16)(g.x / (1.0f + expf(-g.x)) * u.x);
-  r[1] = (_Float16)(g.y / (1.0f + expf(-g.y)) * u.y);
-  r[2] = (_Float16)(g.z / (1.0f + expf(-g.z)) * u.z);
-  r[3] = (_Float16)(g.w / (1.0f + expf(-g.w)) * u.w);
-  reinterpret_cast<half4*>(h)[i4] = r;
-}
-
 // Four consecutive outputs per thread (16-byte loads and stores; H % 4 == 0,
 // rows and out 16-byte aligned); every slot's sorted row and weight, then
 // every slot's four values, are loaded before the sum.
@@ -202,10 +183,6 @@ MoePrefillPlan plan_moe_prefill(int T, int H, int I, int E, int topk) {
   off += align256((size_t)p.max_tiles * 16);
   p.off_counts = off;
   off += 256;
-  p.off_g = off;
-  off += align256(np * I * 4);
-  p.off_u = off;
-  off += align256(np * I * 4);
   p.off_h = off;
   off += align256(np * I * 2);
   p.off_d = off;
@@ -223,8 +200,6 @@ hipError_t launch_moe_prefill(const uint16_t* x16, const uint8_t* Wg, const uint
   int32_t* pos = reinterpret_cast<int32_t*>(base + p.off_pos);
   int4* tiles = reinterpret_cast<int4*>(base + p.off_tiles);
   int* counts = reinterpret_cast<int*>(base + p.off_counts);
-  float* G = reinterpret_cast<float*>(base + p.off_g);
-  float* U = reinterpret_cast<float*>(base + p.off_u);
   _Float16* h = reinterpret_cast<_Float16*>(base + p.off_h);
   float* D = reinterpret_cast<float*>(base + p.off_d);
   const int npairs = T * topk;
@@ -234,17 +209,11 @@ hipError_t launch_moe_prefill(const uint16_t* x16, const uint8_t* Wg, const uint
   hipLaunchKernelGGL(moe_prefill_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  err = launch_gemm_grouped(x16, T, Wg, mat, G, I, H, tiles, counts, p.max_tiles, src, st);
+  err = launch_gemm_grouped(x16, T, Wg, Wu, mat, nullptr, h, I, H, tiles, counts, p.max_tiles,
+                            src, st);
   if (err != hipSuccess) return err;
-  err = launch_gemm_grouped(x16, T, Wu, mat, U, I, H, tiles, counts, p.max_tiles, src, st);
-  if (err != hipSuccess) return err;
-  const size_t nh4 = (size_t)npairs * I / 4;
-  hipLaunchKernelGGL(moe_prefill_act_kernel, dim3((unsigned)((nh4 + 255) / 256)), dim3(256), 0,
-                     st, G, U, h, counts, I);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  err = launch_gemm_grouped(reinterpret_cast<const uint16_t*>(h), npairs, Wd, mat, D, H, I, tiles,
-                            counts, p.max_tiles, nullptr, st);
+  err = launch_gemm_grouped(reinterpret_cast<const uint16_t*>(h), npairs, Wd, nullptr, mat, D,
+                            nullptr, H, I, tiles, counts, p.max_tiles, nullptr, st);
   if (err != hipSuccess) return err;
   const size_t total4 = (size_t)T * H / 4;
   hipLaunchKernelGGL(moe_prefill_combine_kernel, dim3((unsigned)((total4 + 255) / 256)), dim3(256),

@@ -69,16 +69,20 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
 // Expert-grouped mode of the aligned prefill kernel (gemm_q4_0.hip): m-tiles
 // (expert, first output row, rows <= kGemmRows) from a device list, X rows
 // gathered through src (null: identity), B = consecutive K x N matrices.
+// With B1 (a second set of matrices of the same shape) the workgroup
+// contracts the same X tile with both and writes H = fp16(SiLU(X.B) * (X.B1))
+// instead of Y.
 constexpr int kGemmRows = 128;  // rows of one grouped m-tile
 bool gemm_grouped_supported(int N, int K);
-hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, size_t mat_bytes,
-                               float* Y, int N, int K, const int4* tiles, const int* n_tiles,
-                               int max_tiles, const int32_t* src, hipStream_t st);
+hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, const uint8_t* B1,
+                               size_t mat_bytes, float* Y, _Float16* H, int N, int K,
+                               const int4* tiles, const int* n_tiles, int max_tiles,
+                               const int32_t* src, hipStream_t st);
 
 // ---- MoE prefill (moe_prefill.hip) -----------------------------------------
 struct MoePrefillPlan {
   int max_tiles;  // upper bound on m-tiles over all experts
-  size_t off_src, off_pos, off_tiles, off_counts, off_g, off_u, off_h, off_d, ws_bytes;
+  size_t off_src, off_pos, off_tiles, off_counts, off_h, off_d, ws_bytes;
 };
 MoePrefillPlan plan_moe_prefill(int T, int H, int I, int E, int topk);
 hipError_t launch_moe_prefill(const uint16_t* x16, const uint8_t* Wg, const uint8_t* Wu,

@@ -189,5 +189,5 @@ def test_moe_prefill_rejects_bad_arguments(lib):
     assert f(*ok[:6], FAKE + 4, 64, 5120, 1536, 160, 6, None, 0, None) == -3  # out not 16-B aligned
     assert f(*ok, 64, 5120, 1536, 160, 6, None, 0, None) == -4
     assert f(*ok, 60000, 5120, 1536, 160, 8, None, 0, None) == -6  # down rows > 2 GiB
-    assert ws(2048, 5120, 1536, 160, 6) > 2048 * 6 * (5120 + 1536) * 4
+    assert ws(2048, 5120, 1536, 160, 6) > 2048 * 6 * (4 * 5120 + 2 * 1536)
     assert ws(64, 5120, 1504, 160, 6) == 0
