@@ -257,10 +257,13 @@ struct Args {
   const int* n_tiles;
   const int32_t* src;
   size_t mat_bytes;
-  // Two matrices (gate B and up B1, same shape): the output is
-  // H = fp16(SiLU(X . B) * (X . B1)) instead of Y.
+  // Two matrices per workgroup. With H set (gate B and up B1, same shape) the
+  // output is H = fp16(SiLU(X . B) * (X . B1)) instead of Y. With H null, B1
+  // is B shifted by one column tile (128 columns) and the workgroup writes
+  // two adjacent column tiles of Y (cpw = 2 column tiles per workgroup).
   const uint8_t* B1;
   _Float16* H;
+  int cpw;
 };
 
 constexpr int vmcnt_imm(int n) { return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8); }
@@ -469,7 +472,7 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
     m0 = tm * BM;
     rows = g.M - m0;
   }
-  const int j0 = tn * (BN / kBlockWeights);
+  const int j0 = tn * g.cpw * (BN / kBlockWeights);
   const int wave = threadIdx.x >> 6;
 
   if (wave >= 4) {
@@ -577,11 +580,15 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
         if (rr >= rows) continue;
         if constexpr (NM == 1) {
           g.Y[(size_t)(m0 + rr) * g.N + col] = acc[0][i][j][r];
-        } else {
+        } else if (g.H) {
           // gate and up of one expert: h = fp16(SiLU(gate) * up)
           const float gt = acc[0][i][j][r];
           g.H[(size_t)(m0 + rr) * g.N + col] =
               (_Float16)(gt / (1.0f + expf(-gt)) * acc[1][i][j][r]);
+        } else {
+          // two adjacent column tiles
+          g.Y[(size_t)(m0 + rr) * g.N + col] = acc[0][i][j][r];
+          g.Y[(size_t)(m0 + rr) * g.N + col + BN] = acc[1][i][j][r];
         }
       }
     }
@@ -621,6 +628,7 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
     f.mat_bytes = 0;
     f.B1 = nullptr;
     f.H = nullptr;
+    f.cpw = 1;
     constexpr int BM = fast::kDenseBM;
     const long long tiles = (long long)((M + BM - 1) / BM) * f.tiles_n;
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -638,8 +646,9 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
 
 bool gemm_grouped_supported(int N, int K) { return K % fast::BK == 0 && N % fast::BN == 0; }
 
-// Expert-grouped launches: one matrix (B1 null: Y fp32) or the gate and up
-// matrices together (B1 set: H = fp16(SiLU(X . B) * (X . B1))).
+// Expert-grouped launches: the gate and up matrices together (B1 set:
+// H = fp16(SiLU(X . B) * (X . B1))), or one matrix into fp32 Y, two adjacent
+// column tiles per workgroup when N % 256 == 0.
 hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, const uint8_t* B1,
                                size_t mat_bytes, float* Y, _Float16* H, int N, int K,
                                const int4* tiles, const int* n_tiles, int max_tiles,
@@ -660,11 +669,17 @@ hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, 
   f.mat_bytes = mat_bytes;
   f.B1 = B1;
   f.H = H;
+  f.cpw = 1;
+  if (!B1 && N % (2 * fast::BN) == 0) {
+    f.B1 = B + (fast::BN / kBlockWeights) * kBlockBytes;  // the next 128 columns of each row
+    f.cpw = 2;
+    f.tiles_n = N / (2 * fast::BN);
+  }
   const long long grid = (long long)max_tiles * f.tiles_n;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
   constexpr int BM = fast::kGroupedBM;
-  if (B1)
+  if (f.B1)
     hipLaunchKernelGGL((fast::gemm_q4_0_kernel<BM, 2>), dim3((unsigned)grid),
                        dim3(2 * kGemmThreads), (fast::XCfg<BM, 2>::kLdsBytes), st, f);
   else
