@@ -17,7 +17,6 @@ SOURCES = ["q4moe_api.cpp", "gemv_q4_0.hip", "gemv_mfma_q4_0.hip", "gemv_q8_0.hi
 # on every batch).
 EXTRA = {"gemv_mfma_q4_0.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
          "moe_q4_0.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
-HEADERS = ["q4_device.hpp", "q4_internal.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -24,6 +24,7 @@
 // sums are fp32.
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
+#include "q4_route.hpp"
 
 namespace q4 {
 namespace {
@@ -31,8 +32,6 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kChunk = 512;                      // pairs ranked per pass (8 waves)
 constexpr int kChunkWaves = kChunk / kWaveSize;
-constexpr int kIdBits = 10;
-static_assert((1 << kIdBits) >= Q4_MOE_MAX_E, "expert ids fit the ballot match");
 static_assert(Q4_MOE_MAX_E <= kRouteThreads, "one lane per expert");
 
 struct PrefillRoute {
@@ -43,22 +42,6 @@ struct PrefillRoute {
   int4* tiles;    // [max_tiles] (expert, first row, rows, 0)
   int* counts;    // [2]: m-tiles, valid rows
 };
-
-__device__ int scan_inclusive(int v, int* wsum) {
-  const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wave = threadIdx.x / kWaveSize;
-#pragma unroll
-  for (int o = 1; o < kWaveSize; o <<= 1) {
-    const int n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
-  if (lane == kWaveSize - 1) wsum[wave] = v;
-  __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wave; ++w) add += wsum[w];
-  __syncthreads();
-  return v + add;
-}
 
 __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(PrefillRoute a) {
   __shared__ int s_cnt[Q4_MOE_MAX_E];
@@ -79,8 +62,8 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
   // expert t: its first sorted row and its m-tiles of 256 rows
   const int cnt = t < a.E ? s_cnt[t] : 0;
   const int nt = (cnt + kGemmRows - 1) / kGemmRows;
-  const int off = scan_inclusive(cnt, s_wsum) - cnt;
-  const int toff = scan_inclusive(nt, s_wsum) - nt;
+  const int off = block_inclusive_scan(cnt, s_wsum) - cnt;
+  const int toff = block_inclusive_scan(nt, s_wsum) - nt;
   for (int i = 0; i < nt; ++i)
     a.tiles[toff + i] = make_int4(t, off + kGemmRows * i, min(kGemmRows, cnt - kGemmRows * i), 0);
   if (t == kRouteThreads - 1) {
@@ -101,13 +84,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
     const bool mine = t < kChunk && p < a.npairs;
     const int e = mine ? a.ids[p] : -1;
     const bool valid = e >= 0 && e < a.E;
-    uint64_t same = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < kIdBits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t set = __ballot(bit);
-      same &= bit ? set : ~set;
-    }
+    const uint64_t same = same_id_lanes(e, valid);
     if (valid && (same & below) == 0) s_wcnt[wave][e] = __popcll(same);
     __syncthreads();
     if (mine) {

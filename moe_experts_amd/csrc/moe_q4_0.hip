@@ -40,6 +40,7 @@
 #include "q4_device.hpp"
 #include "q4_internal.hpp"
 #include "q4_mfma.hpp"
+#include "q4_route.hpp"
 
 namespace q4 {
 namespace {
@@ -80,26 +81,6 @@ struct RouteArgs {
   int* __restrict__ n_mitems;
 };
 
-// Inclusive prefix sum over one value per lane of the whole workgroup.
-__device__ int block_inclusive_scan(int v, int* wsum) {
-  const int lane = threadIdx.x & (kWaveSize - 1);
-  const int wave = threadIdx.x / kWaveSize;
-#pragma unroll
-  for (int o = 1; o < kWaveSize; o <<= 1) {
-    const int n = __shfl_up(v, o);
-    if (lane >= o) v += n;
-  }
-  if (lane == kWaveSize - 1) wsum[wave] = v;
-  __syncthreads();
-  int add = 0;
-  for (int w = 0; w < wave; ++w) add += wsum[w];
-  __syncthreads();
-  return v + add;
-}
-
-// Bits of an expert id (ids are below Q4_MOE_MAX_E).
-constexpr int kIdBits = 10;
-static_assert((1 << kIdBits) >= Q4_MOE_MAX_E, "expert ids fit the ballot match");
 static_assert(Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK <= kRouteThreads, "one lane per pair");
 constexpr int kRouteWaves = Q4_MOE_MAX_T * Q4_MOE_MAX_TOPK / kWaveSize;
 
@@ -117,13 +98,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(RouteArgs a) {
   // find each other with one ballot per id bit: the exact-match mask.
   const int e = t < a.npairs ? a.ids[t] : -1;
   const bool valid = e >= 0 && e < a.E;
-  uint64_t same = __ballot(valid);
-#pragma unroll
-  for (int b = 0; b < kIdBits; ++b) {
-    const bool bit = (e >> b) & 1;
-    const uint64_t set = __ballot(bit);
-    same &= bit ? set : ~set;
-  }
+  const uint64_t same = same_id_lanes(e, valid);
   const uint64_t below = (1ull << lane) - 1;
   s_cnt[t] = 0;
   for (int i = t; i < kRouteWaves * Q4_MOE_MAX_E; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
