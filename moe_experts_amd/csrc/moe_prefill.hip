@@ -54,9 +54,17 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
 
   s_cnt[t] = 0;
   __syncthreads();
-  for (int p = t; p < a.npairs; p += kRouteThreads) {
-    const int e = a.ids[p];
-    if (e >= 0 && e < a.E) atomicAdd(&s_cnt[e], 1);
+  // counts per expert; four ids per lane in flight at a time
+  for (int p0 = t; p0 < a.npairs; p0 += 4 * kRouteThreads) {
+    int ev[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u * kRouteThreads;
+      ev[u] = p < a.npairs ? a.ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (ev[u] >= 0 && ev[u] < a.E) atomicAdd(&s_cnt[ev[u]], 1);
   }
   __syncthreads();
   // expert t: its first sorted row and its m-tiles of 256 rows
@@ -75,14 +83,19 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
 
   // Stable ranks, kChunk pairs at a time: within a wave by an exact-id ballot
   // match, across the chunk's waves by per-wave counts, across chunks by a
-  // running base per expert.
+  // running base per expert. Each pass loads the next pass's id up front.
   const uint64_t below = (1ull << lane) - 1;
+  int e_next = (t < kChunk && t < a.npairs) ? a.ids[t] : -1;
   for (int c0 = 0; c0 < a.npairs; c0 += kChunk) {
-    for (int i = t; i < kChunkWaves * Q4_MOE_MAX_E; i += kRouteThreads) (&s_wcnt[0][0])[i] = 0;
-    __syncthreads();
     const int p = c0 + t;
     const bool mine = t < kChunk && p < a.npairs;
-    const int e = mine ? a.ids[p] : -1;
+    const int e = mine ? e_next : -1;
+    e_next = (t < kChunk && p + kChunk < a.npairs) ? a.ids[p + kChunk] : -1;
+    for (int i = t; i < kChunkWaves * a.E; i += kRouteThreads) {
+      const int w = i / a.E;
+      s_wcnt[w][i - w * a.E] = 0;
+    }
+    __syncthreads();
     const bool valid = e >= 0 && e < a.E;
     const uint64_t same = same_id_lanes(e, valid);
     if (valid && (same & below) == 0) s_wcnt[wave][e] = __popcll(same);
