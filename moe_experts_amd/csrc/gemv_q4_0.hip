@@ -165,12 +165,12 @@ hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStr
 // half blocks for M >= 2 (half the accumulator registers, so more waves per
 // SIMD: measured 4-10 % faster than whole blocks at M = 2..4). The K split S
 // sets the grid size C*S. Measured on MI355X over the dense 7B shapes, the
-// best grid is at most one full round of resident workgroups: up to 512 (two
-// per CU) for M >= 2, where the VALU sets the pace and every SIMD needs two
-// waves, and up to 352 for M = 1, where more splits only add partial-sum
-// traffic; a grid just past a round costs a whole second round. Tiles keep at
-// least 128 rows (8 or 16 per lane), or their fixed cost dominates. S is the
-// largest split within both.
+// best grid is at most one full round of resident workgroups, up to 512 (two
+// per CU), for every batch: at M = 1 a sweep of the cap over 256..1024 gave
+// 11.85 us at 512 against 12.4 at 352 (4096 x 11008) and 12.5 against 13.3
+// (11008 x 4096); a grid just past a round costs a whole second round. Tiles
+// keep at least 128 rows (8 or 16 per lane), or their fixed cost dominates.
+// S is the largest split within both.
 GemvPlan plan_gemv(int M, int N, int K) {
   GemvPlan p{};
   if (plan_gemv_mfma(M, N, K, p)) return p;
@@ -181,7 +181,7 @@ GemvPlan plan_gemv(int M, int N, int K) {
   p.Lr = p.Jt * p.LPB;
   p.P = kThreads / p.Lr;
   p.C = (NB + p.Jt - 1) / p.Jt;
-  const int target = M >= 2 ? 512 : 352;
+  constexpr int target = 512;
   int best_kt = ((K + p.P - 1) / p.P) * p.P;  // S = 1
   int last_S = -1;
   for (int s = 2; s <= K; ++s) {
