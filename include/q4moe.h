@@ -157,6 +157,38 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
                     size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Inspection of the routing table that moe_q4_0_decode builds in its
+ * workspace: the grouping of (token, slot) pairs by expert that lets each
+ * routed expert's weights be streamed once for all the tokens that chose it
+ * (the MoE module's gate hands the experts top-k ids; "Optimization 3" runs
+ * the routed experts as batched GEMVs). Meant for tests and debugging: after
+ * a call with T >= 2 on the same (T, H, I, E, topk), the workspace holds
+ *   counts      int32[2] at *counts_off: the number of vector items and of
+ *               matrix-core items;
+ *   vector items q4_moe_item[counts[0]] at *items_off: one item per expert
+ *               chosen by 1 or 2 pairs, in increasing expert order;
+ *   matrix items q4_moe_item[counts[1]] at *mitems_off: an expert chosen by
+ *               n >= 3 pairs gives c = ceil(n / 8) items holding consecutive
+ *               runs of its pairs, the first n mod c of size n / c + 1 and the
+ *               others n / c, in increasing expert order.
+ * A pair is p = t * topk + slot; within an expert the pairs appear in
+ * increasing p; an id outside [0, E) appears nowhere; pairs[] entries past
+ * count are 0. A single token (T == 1) skips this pass and leaves no table.
+ * The offsets are byte offsets into the workspace (ws); the table lives
+ * there until the next call that uses the workspace. Returns Q4_OK, or the
+ * status moe_q4_0_decode would return for the shape; outputs untouched on error.
+ * ------------------------------------------------------------------------- */
+typedef struct q4_moe_item {
+  int32_t expert;        /* expert id */
+  int32_t count;         /* pairs in this item (1 .. 8) */
+  int32_t reserved[2];
+  int32_t pairs[8];      /* pair indices t * topk + slot */
+} q4_moe_item;
+
+int moe_q4_0_route_layout(int T, int H, int I, int E, int topk, size_t* items_off,
+                          size_t* counts_off, size_t* mitems_off);
+
+/* ---------------------------------------------------------------------------
  * Routed-expert MoE at prefill (many tokens per expert): the same layer as
  * moe_q4_0_decode, with every expert's gate, up and down products run as
  * GEMMs on the fp16 matrix cores. The KTransformers tutorial gives the
@@ -170,7 +202,7 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
  *   1 <= T <= Q4_MOE_PREFILL_MAX_T, 1 <= topk <= Q4_MOE_MAX_TOPK,
  *   1 <= E <= Q4_MOE_MAX_E, H % 128 == 0, I % 128 == 0.
  * Pairs are sorted by expert on the device (stable); each expert's rows go
- * through 256-row tiles. Each dequantized weight and h = SiLU(g) * u are
+ * through 128-row tiles. Each dequantized weight and h = SiLU(g) * u are
  * rounded to fp16 before their products; sums are fp32. Ids outside [0, E)
  * contribute zero; slots are summed in order 0..topk-1.
  *   ws/ws_bytes: workspace of moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)

@@ -60,6 +60,10 @@ _lib.moe_q4_0_layer_workspace_bytes.argtypes = [_I, _I, _I, _I, _I, _I]
 _lib.moe_q4_0_layer.restype = _I
 _lib.moe_q4_0_layer.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 
+_lib.moe_q4_0_route_layout.restype = _I
+_lib.moe_q4_0_route_layout.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_Z), ctypes.POINTER(_Z),
+                                       ctypes.POINTER(_Z)]
+
 BLOCK_BYTES = 18
 Q8_BLOCK_BYTES = 34
 
@@ -212,6 +216,15 @@ def moe_q4_0_decode(x: torch.Tensor, Wg: torch.Tensor, Wu: torch.Tensor, Wd: tor
     return out
 
 
+def moe_q4_0_route_layout(T: int, H: int, I: int, E: int, topk: int):
+    """Byte offsets (items, counts, mitems) of the routing table that
+    moe_q4_0_decode leaves in its workspace (T >= 2)."""
+    a, b, c = _Z(), _Z(), _Z()
+    _check(_lib.moe_q4_0_route_layout(T, H, I, E, topk, ctypes.byref(a), ctypes.byref(b),
+                                      ctypes.byref(c)))
+    return a.value, b.value, c.value
+
+
 def moe_router_workspace_bytes(T: int, H: int, E: int) -> int:
     return int(_lib.moe_router_workspace_bytes(T, H, E))
 
@@ -228,9 +241,11 @@ def _ws_arg(ws, need: int, device):
 
 
 def moe_router_topk(x: torch.Tensor, Wr: torch.Tensor, topk: int, n_shared: int = 0,
-                    ws: torch.Tensor | None = None):
+                    ws: torch.Tensor | None = None, logits: torch.Tensor | None = None,
+                    ids: torch.Tensor | None = None, w: torch.Tensor | None = None):
     """MoE router: x [T, H] fp32, Wr [E, H] fp32. Returns (logits [T, E],
-    topk_ids int32 [T, topk + n_shared], topk_w fp32 [T, topk + n_shared])."""
+    topk_ids int32 [T, topk + n_shared], topk_w fp32 [T, topk + n_shared]),
+    written into the given tensors when passed."""
     if x.dim() != 2 or Wr.dim() != 2:
         raise ValueError("x must be [T, H] and Wr [E, H]")
     T, H = x.shape
@@ -238,12 +253,18 @@ def moe_router_topk(x: torch.Tensor, Wr: torch.Tensor, topk: int, n_shared: int 
     px = _dev(x, "x", torch.float32, T * H)
     pr = _dev(Wr, "Wr", torch.float32, E * H)
     slots = topk + n_shared
-    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
-    ids = torch.empty((T, slots), dtype=torch.int32, device=x.device)
-    w = torch.empty((T, slots), dtype=torch.float32, device=x.device)
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    if ids is None:
+        ids = torch.empty((T, slots), dtype=torch.int32, device=x.device)
+    if w is None:
+        w = torch.empty((T, slots), dtype=torch.float32, device=x.device)
+    pl = _dev(logits, "logits", torch.float32, T * E)
+    pi = _dev(ids, "ids", torch.int32, T * slots)
+    pwt = _dev(w, "w", torch.float32, T * slots)
     pws, nws = _ws_arg(ws, moe_router_workspace_bytes(T, H, E), x.device)
-    _check(_lib.moe_router_topk(px, pr, logits.data_ptr(), ids.data_ptr(), w.data_ptr(), T, H, E,
-                                topk, n_shared, pws, nws, _stream(x.device)))
+    _check(_lib.moe_router_topk(px, pr, pl, pi, pwt, T, H, E, topk, n_shared, pws, nws,
+                                _stream(x.device)))
     return logits, ids, w
 
 

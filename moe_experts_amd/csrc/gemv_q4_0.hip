@@ -161,6 +161,39 @@ hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStr
   return hipGetLastError();
 }
 
+namespace {
+
+// Dynamic LDS bytes of a vector tile of Kt rows with P row phases (as
+// launch_one sizes it); with 16-block tiles the larger of the staged and the
+// per-lane variant, since the matrix alignment decides between them at launch.
+template <int M, int LPB>
+int vector_lds_bytes_t(int Kt, int P, bool wide) {
+  const int rf = 4 * phase_lds_floats<M, LPB>();
+  int m = 4 * tile_x_floats<M>(Kt, P, rows_per_batch<M, LPB>());
+  if (wide) {
+    const int sb = staged_lds_bytes<M, LPB, staged_rows_per_batch<M, LPB>(), kStagedJt,
+                                    staged_buffers<M, LPB>()>(Kt);
+    m = m > sb ? m : sb;
+  }
+  return m > rf ? m : rf;
+}
+
+int vector_lds_bytes(int M, int LPB, int Kt, int P, bool wide) {
+  switch (M) {
+    case 1:
+      return LPB == 1 ? vector_lds_bytes_t<1, 1>(Kt, P, wide) : vector_lds_bytes_t<1, 2>(Kt, P, wide);
+    case 2: return vector_lds_bytes_t<2, 2>(Kt, P, wide);
+    case 3: return vector_lds_bytes_t<3, 2>(Kt, P, wide);
+    case 4: return vector_lds_bytes_t<4, 2>(Kt, P, wide);
+    case 5: return vector_lds_bytes_t<5, 2>(Kt, P, wide);
+    case 6: return vector_lds_bytes_t<6, 2>(Kt, P, wide);
+    case 7: return vector_lds_bytes_t<7, 2>(Kt, P, wide);
+    default: return vector_lds_bytes_t<8, 2>(Kt, P, wide);
+  }
+}
+
+}  // namespace
+
 // Tile plan: 16-block column tiles; whole blocks per lane for a single row,
 // half blocks for M >= 2 (half the accumulator registers, so more waves per
 // SIMD: measured 4-10 % faster than whole blocks at M = 2..4). The K split S
@@ -181,18 +214,28 @@ GemvPlan plan_gemv(int M, int N, int K) {
   p.Lr = p.Jt * p.LPB;
   p.P = kThreads / p.Lr;
   p.C = (NB + p.Jt - 1) / p.Jt;
+  auto kt_for = [&](int s) {
+    const int kt = (K + s - 1) / s;
+    return (kt + p.P - 1) / p.P * p.P;
+  };
   constexpr int target = 512;
-  int best_kt = ((K + p.P - 1) / p.P) * p.P;  // S = 1
+  int best_kt = kt_for(1);  // S = 1
   int last_S = -1;
   for (int s = 2; s <= K; ++s) {
-    int kt = (K + s - 1) / s;
-    kt = (kt + p.P - 1) / p.P * p.P;
+    const int kt = kt_for(s);
     const int S = (K + kt - 1) / kt;
     if (S == last_S) continue;
     last_S = S;
     if (kt < kMinTileRows || p.C * S > target) break;
     best_kt = kt;
   }
+  // The activation tile grows with the rows of a tile: split K further when
+  // the tile would not fit in LDS (wide matrices, where the grid target alone
+  // gives few splits), even past the grid target.
+  const bool wide = p.Jt == kStagedJt;
+  for (int s = (K + best_kt - 1) / best_kt;
+       vector_lds_bytes(M, p.LPB, best_kt, p.P, wide) > kMaxLdsBytes; ++s)
+    best_kt = kt_for(s);
   p.Kt = best_kt;
   p.S = (K + p.Kt - 1) / p.Kt;
   p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;

@@ -210,6 +210,31 @@ hipError_t launch_q8_m(const Q8Args& a, hipStream_t st) {
 // blocks for several (8 columns, fewer accumulators); the K split keeps the
 // grid within one round of resident workgroups (352 for M = 1, 512 else,
 // as the Q4_0 vector tiles) with at least 128 rows per tile.
+namespace {
+
+// Dynamic LDS bytes of a tile of Kt rows (as launch_q8_t sizes it).
+template <int M, int LPB>
+int q8_lds_bytes_t(int Kt, int P) {
+  const int xf = 4 * tile_x_floats<M>(Kt, P, kQ8RB);
+  const int rf = 4 * q8_reduce_floats<M, LPB>();
+  return xf > rf ? xf : rf;
+}
+
+int q8_lds_bytes(int M, int Kt, int P) {
+  switch (M) {
+    case 1: return q8_lds_bytes_t<1, 2>(Kt, P);
+    case 2: return q8_lds_bytes_t<2, 4>(Kt, P);
+    case 3: return q8_lds_bytes_t<3, 4>(Kt, P);
+    case 4: return q8_lds_bytes_t<4, 4>(Kt, P);
+    case 5: return q8_lds_bytes_t<5, 4>(Kt, P);
+    case 6: return q8_lds_bytes_t<6, 4>(Kt, P);
+    case 7: return q8_lds_bytes_t<7, 4>(Kt, P);
+    default: return q8_lds_bytes_t<8, 4>(Kt, P);
+  }
+}
+
+}  // namespace
+
 GemvPlan plan_gemv_q8(int M, int N, int K) {
   GemvPlan p{};
   const int NB = N / kBlockWeights;
@@ -218,18 +243,24 @@ GemvPlan plan_gemv_q8(int M, int N, int K) {
   p.Lr = p.Jt * p.LPB;
   p.P = kThreads / p.Lr;
   p.C = (NB + p.Jt - 1) / p.Jt;
+  auto kt_for = [&](int s) {
+    const int kt = (K + s - 1) / s;
+    return (kt + p.P - 1) / p.P * p.P;
+  };
   const int target = M >= 2 ? 512 : 352;
-  int best_kt = ((K + p.P - 1) / p.P) * p.P;  // S = 1
+  int best_kt = kt_for(1);  // S = 1
   int last_S = -1;
   for (int s = 2; s <= K; ++s) {
-    int kt = (K + s - 1) / s;
-    kt = (kt + p.P - 1) / p.P * p.P;
+    const int kt = kt_for(s);
     const int S = (K + kt - 1) / kt;
     if (S == last_S) continue;
     last_S = S;
     if (kt < 128 || p.C * S > target) break;
     best_kt = kt;
   }
+  // split K further when the activation tile would not fit in LDS
+  for (int s = (K + best_kt - 1) / best_kt; q8_lds_bytes(M, best_kt, p.P) > kMaxLdsBytes; ++s)
+    best_kt = kt_for(s);
   p.Kt = best_kt;
   p.S = (K + p.Kt - 1) / p.Kt;
   p.ws_bytes = p.S > 1 ? (size_t)p.S * M * N * sizeof(float) : 0;

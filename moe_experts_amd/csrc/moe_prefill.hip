@@ -11,7 +11,7 @@
 //      the (token, slot) pairs by expert. Sorted row q holds pair perm[q]; the
 //      kernel writes, per sorted row, the token it reads (src[q]), per pair its
 //      sorted row (pos[p], -1 for an id outside [0, E)), and the list of
-//      256-row m-tiles (expert, first row, rows) of every expert's rows.
+//      128-row m-tiles (expert, first row, rows) of every expert's rows.
 //   2. gate and up together: the prefill GEMM kernel in its grouped mode
 //      with two matrices (X rows gathered by src, the expert's gate and up
 //      Q4_0 matrices against the same X tile); its epilogue writes
@@ -67,7 +67,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
       if (ev[u] >= 0 && ev[u] < a.E) atomicAdd(&s_cnt[ev[u]], 1);
   }
   __syncthreads();
-  // expert t: its first sorted row and its m-tiles of 256 rows
+  // expert t: its first sorted row and its m-tiles of 128 rows (kGemmRows)
   const int cnt = t < a.E ? s_cnt[t] : 0;
   const int nt = (cnt + kGemmRows - 1) / kGemmRows;
   const int off = block_inclusive_scan(cnt, s_wsum) - cnt;

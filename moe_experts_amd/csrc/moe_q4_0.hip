@@ -60,6 +60,12 @@ struct ItemRec {
   int pairs[kMfmaPairs];  // pair index t * topk + slot, in stable expert order
 };
 
+// The routing table's record is the header's q4_moe_item (inspection ABI).
+static_assert(sizeof(ItemRec) == sizeof(q4_moe_item) && offsetof(ItemRec, e) ==
+              offsetof(q4_moe_item, expert) && offsetof(ItemRec, cnt) ==
+              offsetof(q4_moe_item, count) && offsetof(ItemRec, pairs) ==
+              offsetof(q4_moe_item, pairs), "routing table record layout");
+
 constexpr int kMaxRB = 4;       // rows per lane in one pipelined batch (per-lane path)
 constexpr int kStagedRB = 2;    // rows per lane in one batch of the staged path
 constexpr int kStagedBufs = 2;  // weight buffers per wave of the staged path

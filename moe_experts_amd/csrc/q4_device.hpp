@@ -28,6 +28,7 @@ constexpr int kBlockWeights = 32;
 constexpr int kWaveSize = 64;
 constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 constexpr int kThreads = 256;  // lanes per workgroup of the decode tiles
+constexpr int kMaxLdsBytes = 160 * 1024;  // LDS of one workgroup on gfx950
 
 // Workgroups are dispatched round-robin over the XCDs (block b runs on XCD
 // b % 8). Returns a logical tile index such that consecutive logical tiles

@@ -51,6 +51,16 @@ int check_moe_shape(int T, int H, int I, int E, int topk) {
   return Q4_OK;
 }
 
+// The decode kernels address the activations, h and the split-K partial sums
+// with 32-bit byte offsets: each must stay below 2 GiB.
+int check_moe_sizes(const q4::MoePlan& p) {
+  const long long np = (long long)p.T * p.topk;
+  if ((long long)p.T * p.H * 4 > kMaxBytes || np * p.I * 4 > kMaxBytes ||
+      2LL * p.gu_S * np * p.I * 4 > kMaxBytes || (long long)p.dn_S * np * p.H * 4 > kMaxBytes)
+    return Q4_ETOOBIG;
+  return Q4_OK;
+}
+
 int from_hip(hipError_t e) { return e == hipSuccess ? Q4_OK : Q4_EHIP; }
 
 int check_router_shape(int T, int H, int E, int topk, int n_shared) {
@@ -157,7 +167,8 @@ int q4_0_gemm(const uint16_t* X, const q4_0_block* B, float* Y, int M, int N, in
 
 size_t moe_q4_0_workspace_bytes(int T, int H, int I, int E, int topk) {
   if (check_moe_shape(T, H, I, E, topk) != Q4_OK) return 0;
-  return q4::plan_moe(T, H, I, E, topk).ws_bytes;
+  const q4::MoePlan p = q4::plan_moe(T, H, I, E, topk);
+  return check_moe_sizes(p) == Q4_OK ? p.ws_bytes : 0;
 }
 
 int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
@@ -171,12 +182,28 @@ int moe_q4_0_decode(const float* x, const q4_0_block* Wg, const q4_0_block* Wu,
       !aligned(Wg, 2) || !aligned(Wu, 2) || !aligned(Wd, 2))
     return Q4_EALIGN;
   const q4::MoePlan p = q4::plan_moe(T, H, I, E, topk);
+  rc = check_moe_sizes(p);
+  if (rc != Q4_OK) return rc;
   rc = check_ws(ws, ws_bytes, p.ws_bytes);
   if (rc != Q4_OK) return rc;
   return from_hip(q4::launch_moe(x, reinterpret_cast<const uint8_t*>(Wg),
                                  reinterpret_cast<const uint8_t*>(Wu),
                                  reinterpret_cast<const uint8_t*>(Wd), topk_ids, topk_w, out, ws,
                                  p, static_cast<hipStream_t>(stream)));
+}
+
+int moe_q4_0_route_layout(int T, int H, int I, int E, int topk, size_t* items_off,
+                          size_t* counts_off, size_t* mitems_off) {
+  if (!items_off || !counts_off || !mitems_off) return Q4_EINVAL;
+  int rc = check_moe_shape(T, H, I, E, topk);
+  if (rc != Q4_OK) return rc;
+  const q4::MoePlan p = q4::plan_moe(T, H, I, E, topk);
+  rc = check_moe_sizes(p);
+  if (rc != Q4_OK) return rc;
+  *items_off = p.off_items;
+  *counts_off = p.off_n_items;
+  *mitems_off = p.off_mitems;
+  return Q4_OK;
 }
 
 size_t moe_router_workspace_bytes(int T, int H, int E) {
@@ -201,7 +228,8 @@ int moe_router_topk(const float* x, const float* Wr, float* logits, int32_t* top
 
 size_t moe_q4_0_layer_workspace_bytes(int T, int H, int I, int E, int topk, int n_shared) {
   if (check_router_shape(T, H, E, topk, n_shared) != Q4_OK ||
-      check_moe_shape(T, H, I, E + n_shared, topk + n_shared) != Q4_OK)
+      check_moe_shape(T, H, I, E + n_shared, topk + n_shared) != Q4_OK ||
+      check_moe_sizes(q4::plan_moe(T, H, I, E + n_shared, topk + n_shared)) != Q4_OK)
     return 0;
   return layer_ws(T, H, I, E, topk, n_shared).bytes;
 }
@@ -213,6 +241,8 @@ int moe_q4_0_layer(const float* x, const float* Wr, const q4_0_block* Wg, const 
   int rc = check_router_shape(T, H, E, topk, n_shared);
   if (rc != Q4_OK) return rc;
   rc = check_moe_shape(T, H, I, E + n_shared, topk + n_shared);
+  if (rc != Q4_OK) return rc;
+  rc = check_moe_sizes(q4::plan_moe(T, H, I, E + n_shared, topk + n_shared));
   if (rc != Q4_OK) return rc;
   if (!aligned(x, 16) || !aligned(Wr, 16) || !aligned(out, 4) || !aligned(Wg, 2) ||
       !aligned(Wu, 2) || !aligned(Wd, 2))

@@ -40,3 +40,54 @@ def guarded(n: int, dtype=torch.float32, guard: int = 64, fill=1234.5):
 def guards_intact(full: torch.Tensor, n: int, guard: int = 64, fill=1234.5) -> bool:
     h = full.detach().cpu()
     return bool((h[:guard] == fill).all() and (h[guard + n:] == fill).all())
+
+
+WS_GUARD = 4096  # bytes of sentinel before and after a guarded workspace
+
+
+def guarded_ws(nbytes: int, fill: int = 0xA5):
+    """A workspace of nbytes (256-byte aligned) between two sentinel bands.
+    Returns (full buffer, workspace view)."""
+    full = torch.full((nbytes + 2 * WS_GUARD,), fill, dtype=torch.uint8, device=dev())
+    return full, full[WS_GUARD:WS_GUARD + nbytes]
+
+
+def ws_guards_intact(full: torch.Tensor, nbytes: int, fill: int = 0xA5) -> bool:
+    h = full.detach().cpu().numpy()
+    return bool((h[:WS_GUARD] == fill).all() and (h[WS_GUARD + nbytes:] == fill).all())
+
+
+def check_route_table(ws: np.ndarray, ids: np.ndarray, T: int, H: int, I: int, E: int):
+    """Rebuild the routing table of moe_q4_0_decode on the host from the ids
+    (a brute-force grouping by expert) and compare it with the copy the call
+    left in its workspace, entry by entry (layout: include/q4moe.h,
+    moe_q4_0_route_layout). Returns (vector items, matrix-core items)."""
+    from moe_experts_amd import moe_q4_0_route_layout
+    topk = ids.shape[1]
+    io, co, mo = moe_q4_0_route_layout(T, H, I, E, topk)
+    nv, nm = np.frombuffer(ws[co:co + 8].tobytes(), dtype="<i4")
+    rec = np.dtype([("expert", "<i4"), ("count", "<i4"), ("res", "<i4", 2), ("pairs", "<i4", 8)])
+    vit = np.frombuffer(ws[io:io + nv * rec.itemsize].tobytes(), dtype=rec)
+    mit = np.frombuffer(ws[mo:mo + nm * rec.itemsize].tobytes(), dtype=rec)
+    flat = ids.reshape(-1)
+    per = {e: [p for p in range(flat.size) if flat[p] == e] for e in range(E)}
+    exp_v = [(e, per[e]) for e in range(E) if 1 <= len(per[e]) <= 2]
+    exp_m = []
+    for e in range(E):
+        n = len(per[e])
+        if n >= 3:
+            c = -(-n // 8)
+            start = 0
+            for i in range(c):
+                sz = n // c + (1 if i < n % c else 0)
+                exp_m.append((e, per[e][start:start + sz]))
+                start += sz
+    assert (int(nv), int(nm)) == (len(exp_v), len(exp_m)), "item counts"
+    for got, (e, pairs) in list(zip(vit, exp_v)) + list(zip(mit, exp_m)):
+        n = len(pairs)
+        assert int(got["expert"]) == e and int(got["count"]) == n, f"expert {e} item"
+        assert got["pairs"][:n].tolist() == pairs, f"expert {e} pairs"
+        assert (got["pairs"][n:] == 0).all()
+    valid = int(((flat >= 0) & (flat < E)).sum())
+    assert sum(len(p) for _, p in exp_v + exp_m) == valid
+    return exp_v, exp_m

@@ -122,6 +122,34 @@ def test_moe_rejects_bad_arguments(lib):
     assert f(*ok, 1, 5120, 1536, 160, 6, FAKE + 64, need, None) == -3
 
 
+def test_moe_rejects_buffers_past_32_bit_offsets(lib):
+    """h [T * topk][I] and the partial sums must stay below 2 GiB: a shape whose
+    single expert matrix is small but whose per-pair buffers are not is
+    refused before any launch, and has no workspace size."""
+    f = lib.moe_q4_0_decode
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    T, H, I, E, topk = 64, 32, 1 << 20, 4, 8
+    assert lib.moe_q4_0_workspace_bytes(T, H, I, E, topk) == 0
+    assert f(*ok, T, H, I, E, topk, FAKE, 1 << 40, None) == -6
+    assert lib.moe_q4_0_workspace_bytes(T, H, 1 << 14, E, topk) > 0
+
+
+def test_route_layout(lib):
+    Z = ctypes.c_size_t
+    lib.moe_q4_0_route_layout.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(Z)] * 3
+    a, b, c = Z(), Z(), Z()
+    assert lib.moe_q4_0_route_layout(32, 5120, 1536, 160, 6, ctypes.byref(a), ctypes.byref(b),
+                                     ctypes.byref(c)) == 0
+    need = lib.moe_q4_0_workspace_bytes(32, 5120, 1536, 160, 6)
+    # items, counters and matrix-core items are disjoint, in order, inside the workspace
+    assert a.value < b.value < c.value < need
+    assert b.value - a.value >= 160 * 48 and c.value - b.value >= 8
+    assert lib.moe_q4_0_route_layout(32, 5121, 1536, 160, 6, ctypes.byref(a), ctypes.byref(b),
+                                     ctypes.byref(c)) == -2
+    assert lib.moe_q4_0_route_layout(32, 5120, 1536, 160, 6, None, ctypes.byref(b),
+                                     ctypes.byref(c)) == -1
+
+
 def test_router_rejects_bad_arguments(lib):
     f = lib.moe_router_topk
     ok = (FAKE, FAKE, FAKE, FAKE, FAKE)

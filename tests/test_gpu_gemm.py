@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from moe_experts_amd import datagen
-from tests.gpu_util import check_tol, to_dev, to_host
+from tests.gpu_util import check_tol, guarded, guards_intact, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -80,13 +80,21 @@ def test_gemm_doubling_scales_doubles_output():
 
 
 @pytest.mark.parametrize("which", [0, 1])
-def test_gemm_prefill_full_size_sampled_rows(which):
+def test_gemm_prefill_full_size_every_band(which):
+    """The prefill configuration (2048 x 4096 times 4096 x {4096, 11008}):
+    one whole output row in every 32-row MFMA band of every m-tile (64 rows,
+    each at a different offset inside its band), against the oracle; Y is
+    written only inside its bounds."""
+    from moe_experts_amd import q4_0_gemm
     c = datagen.PREFILL
     M, K, N = c["M"], c["K"], c["Ns"][which]
     X16 = datagen.to_f16(datagen.activations(c["x_seed"], M, K))
     B = datagen.q4_0_random(c["b_seeds"][which], K, N)
-    Y = gemm(X16, B, N)
-    rows = np.array([0, 1, 127, 128, 1000, 2047])
+    full, Yv = guarded(M * N)
+    q4_0_gemm(to_dev(X16), to_dev(B), N, Y=Yv)
+    Y = to_host(Yv).reshape(M, N)
+    assert guards_intact(full, M * N), "write outside Y"
+    rows = np.array([32 * b + (7 * b + 3) % 32 for b in range(M // 32)])
     ref, bnd = oracle.q4_0_matmul_f16(X16[rows], B, N, K)
     check_tol(Y[rows], ref, bnd, TOL, f"prefill N={N}")
     assert np.isfinite(Y).all()

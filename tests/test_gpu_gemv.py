@@ -184,6 +184,16 @@ def test_gemv_dense_7b_shapes(name, K, N, seed):
         check_tol(got, ref, bnd, TOL, f"{name} M={M}")
 
 
+@pytest.mark.parametrize("M,K,N", [(8, 8192, 102400), (5, 4096, 152064), (1, 16384, 65536)])
+def test_gemv_wide_matrices_fit_lds(M, K, N):
+    """Wide matrices: the grid target alone would leave tiles whose activation
+    tile does not fit in LDS; the plan splits K further and the call works."""
+    x = datagen.activations(M + K + N, M, K)
+    B = datagen.q4_0_random(K + N, K, N)
+    ref, bnd = oracle.q4_0_matmul(x, B, N, K)
+    check_tol(gemv(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")
+
+
 def test_gemv_rejects_mismatched_tensors():
     from moe_experts_amd import q4_0_gemv
     x = torch.zeros((1, 64), device=dev())

@@ -5,7 +5,8 @@ import torch
 
 import oracle
 from moe_experts_amd import datagen
-from tests.gpu_util import check_tol, to_dev, to_host
+from tests.gpu_util import (check_route_table, check_tol, guarded, guarded_ws, guards_intact,
+                            to_dev, to_host, ws_guards_intact)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -16,6 +17,23 @@ def moe_gpu(x, Wg, Wu, Wd, ids, w, I, E, dev_w=None):
     g, u, d = dev_w if dev_w is not None else (to_dev(Wg), to_dev(Wu), to_dev(Wd))
     return to_host(moe_q4_0_decode(to_dev(x), g, u, d, to_dev(ids.astype(np.int32)),
                                    to_dev(w.astype(np.float32)), I, E))
+
+
+def moe_gpu_guarded(x, dw, ids, w, I, E):
+    """moe_q4_0_decode with sentinel bands around out and around the workspace;
+    checks the bands and returns (out, host copy of the workspace)."""
+    from moe_experts_amd import moe_q4_0_decode, moe_q4_0_workspace_bytes
+    T, H = x.shape
+    topk = ids.shape[1]
+    need = moe_q4_0_workspace_bytes(T, H, I, E, topk)
+    wsfull, ws = guarded_ws(need)
+    ofull, out = guarded(T * H)
+    moe_q4_0_decode(to_dev(x), *dw, to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32)),
+                    I, E, out=out, ws=ws)
+    got = to_host(out).reshape(T, H)
+    assert guards_intact(ofull, T * H), "write outside out"
+    assert ws_guards_intact(wsfull, need), "write outside the workspace"
+    return got, to_host(ws)
 
 
 def small_experts(seed, H, I, E):
@@ -51,6 +69,24 @@ def test_moe_duplicates_out_of_range_and_crowded_expert():
     ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, H, I, E)
     got = moe_gpu(x, Wg, Wu, Wd, ids, w, I, E)
     check_tol(got, ref, bnd, TOL, "edge routing")
+
+
+@pytest.mark.parametrize("T,H,I,E,topk", [(2, 64, 32, 5, 2), (17, 96, 64, 4, 6), (64, 64, 64, 3, 8),
+                                          (33, 512, 768, 12, 6), (40, 128, 96, 160, 6)])
+def test_moe_route_table_and_guards(T, H, I, E, topk):
+    """The grouping step (pairs -> per-expert items) recomputed on the host from
+    the ids matches the table the call left in its workspace; out and the
+    workspace are written only inside their bounds."""
+    x = datagen.activations(T * 3 + I, T, H)
+    Wg, Wu, Wd = small_experts(11 * E + H, H, I, E)
+    ids, w, _ = datagen.routing(7 * T + E, T, E, topk)
+    ids[0, 0] = -1                   # an invalid id appears in no item
+    if T > 3:
+        ids[1, :] = ids[2, 0]        # a token with every slot on one expert (duplicates)
+    got, ws = moe_gpu_guarded(x, (to_dev(Wg), to_dev(Wu), to_dev(Wd)), ids, w, I, E)
+    check_route_table(ws, ids, T, H, I, E)
+    ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, H, I, E)
+    check_tol(got, ref, bnd, TOL, f"T={T} E={E} topk={topk}")
 
 
 @pytest.mark.parametrize("H,I", [(256, 128), (320, 96)])
@@ -94,7 +130,7 @@ def test_moe_dsv2_single_token(dsv2_experts):
     x = datagen.activations(t1["x_seed"], 1, c["H"])
     ids, w, _ = datagen.routing(t1["logit_seed"], 1, c["E"], c["topk"])
     ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, c["H"], c["I"], c["E"])
-    got = moe_gpu(x, None, None, None, ids, w, c["I"], c["E"], dev_w=dw)
+    got, _ = moe_gpu_guarded(x, dw, ids, w, c["I"], c["E"])
     check_tol(got, ref, bnd, TOL, "dsv2 T=1")
     again = moe_gpu(x, None, None, None, ids, w, c["I"], c["E"], dev_w=dw)
     assert (again == got).all()
@@ -108,12 +144,11 @@ def test_moe_dsv2_32_tokens(dsv2_experts, skewed):
     x = datagen.activations(t32["x_seed"], T, c["H"])
     ids, w, _ = datagen.routing(t32["logit_seed"], T, c["E"], c["topk"],
                                 hot_bias=t32["hot_bias"] if skewed else 0.0, n_hot=t32["n_hot"])
-    got = moe_gpu(x, None, None, None, ids, w, c["I"], c["E"], dev_w=dw)
-    # sampled tokens against the oracle
-    for t in (0, 13, 31):
-        ref, bnd, _ = oracle.moe_decode(x[t:t + 1], Wg, Wu, Wd, ids[t:t + 1], w[t:t + 1],
-                                        c["H"], c["I"], c["E"])
-        check_tol(got[t:t + 1], ref, bnd, TOL, f"dsv2 T=32 skewed={skewed} token {t}")
+    got, ws = moe_gpu_guarded(x, dw, ids, w, c["I"], c["E"])
+    check_route_table(ws, ids, T, c["H"], c["I"], c["E"])
+    # every token against the oracle
+    ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, c["H"], c["I"], c["E"])
+    check_tol(got, ref, bnd, TOL, f"dsv2 T=32 skewed={skewed}")
     # batch invariance: every token is bitwise equal to the same token decoded
     # in a batch of two with another token
     for t in range(T):

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from moe_experts_amd import datagen
-from tests.gpu_util import check_tol, to_dev, to_host
+from tests.gpu_util import check_tol, guarded, guards_intact, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -28,7 +28,7 @@ def experts(seed, H, I, E):
 
 
 # one token; several tokens per expert; more than one 512-pair ranking pass
-# and several 256-row tiles per expert; every slot on one expert (duplicates,
+# and several 128-row tiles per expert; every slot on one expert (duplicates,
 # 3 tiles of one expert); wide I
 @pytest.mark.parametrize("T,H,I,E,topk", [(1, 128, 128, 3, 1), (300, 256, 128, 6, 2),
                                           (513, 384, 256, 9, 6), (70, 128, 384, 1, 8),
@@ -77,3 +77,41 @@ def test_prefill_dsv2_shape():
         ref, bnd, _ = oracle.moe_decode(x16[t:t + 1].astype(np.float32), Wg, Wu, Wd,
                                         ids[t:t + 1], w[t:t + 1], H, I, E)
         check_tol(got[t:t + 1], ref, bnd, TOL, f"dsv2 prefill token {t}")
+
+
+def expert_cover(ids, E, limit=64):
+    """Greedy set cover: tokens (at most `limit`) whose routed experts together
+    include every expert the routing uses."""
+    need = set(int(e) for e in ids.ravel() if 0 <= e < E)
+    chosen = []
+    while need and len(chosen) < limit:
+        t = max(range(ids.shape[0]), key=lambda t: len(need & set(ids[t].tolist())))
+        chosen.append(t)
+        need -= set(ids[t].tolist())
+    assert not need, "no cover within the limit"
+    return sorted(chosen)
+
+
+def test_prefill_dsv2_2048_tokens_every_expert():
+    """The benchmarked MoE prefill: 2048 tokens, DeepSeek-V2 experts, the
+    benchmark's first routing table. A set of tokens that together use every
+    routed expert is checked against the oracle; out is written only inside
+    its bounds."""
+    from moe_experts_amd import moe_q4_0_prefill
+    c = datagen.MOE_DSV2
+    H, I, E, topk = c["H"], c["I"], c["E"], c["topk"]
+    T = 2048
+    ids, w, _ = datagen.routing(5301, T, E, topk)
+    Wg, Wu, Wd = datagen.moe_experts(H, I, E)
+    x16 = datagen.to_f16(datagen.activations(5101, T, H))
+    full, outv = guarded(T * H)
+    moe_q4_0_prefill(to_dev(x16), to_dev(Wg), to_dev(Wu), to_dev(Wd), to_dev(ids.astype(np.int32)),
+                     to_dev(w.astype(np.float32)), I, E, out=outv)
+    got = to_host(outv).reshape(T, H)
+    assert guards_intact(full, T * H), "write outside out"
+    toks = expert_cover(ids, E)
+    assert len(set(ids[toks].ravel().tolist())) == E
+    ref, bnd, _ = oracle.moe_decode(x16[toks].astype(np.float32), Wg, Wu, Wd, ids[toks], w[toks],
+                                    H, I, E)
+    check_tol(got[toks], ref, bnd, TOL, f"dsv2 prefill T=2048, {len(toks)} tokens")
+    assert np.isfinite(got).all()

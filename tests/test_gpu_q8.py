@@ -84,3 +84,13 @@ def test_q8_guard_bands_untouched():
     ref, bnd = oracle.q8_0_matmul(x, B, N, K)
     check_tol(to_host(y).reshape(M, N), ref, bnd, TOL, "guarded")
     assert guards_intact(full, M * N)
+
+
+@pytest.mark.parametrize("M,K,N", [(8, 8192, 102400), (5, 4096, 152064)])
+def test_q8_wide_matrices_fit_lds(M, K, N):
+    """As for Q4_0: the plan splits K further when the activation tile would
+    not fit in LDS."""
+    x = datagen.activations(M + K + N + 1, M, K)
+    B = datagen.q8_0_random(K + N + 1, K, N)
+    ref, bnd = oracle.q8_0_matmul(x, B, N, K)
+    check_tol(gemv8(x, B, N), ref, bnd, TOL, f"M={M} K={K} N={N}")

@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from moe_experts_amd import datagen
-from tests.gpu_util import check_tol, to_dev, to_host
+from tests.gpu_util import check_tol, guarded, guards_intact, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-4
@@ -101,9 +101,30 @@ def test_layer_dsv2(dsv2_layer, T):
     seed = datagen.MOE_T1["x_seed"] if T == 1 else datagen.MOE_T32["x_seed"]
     x = datagen.activations(seed, T, c["H"])
     _, ids, w = check_router(x, Wr, c["topk"], L["n_shared"], f"dsv2 router T={T}")
-    got = layer_gpu(x, Wr, dw, c["I"], c["topk"], L["n_shared"])
+    from moe_experts_amd import moe_q4_0_layer
+    full, outv = guarded(T * c["H"])
+    moe_q4_0_layer(to_dev(x), to_dev(Wr), *dw, c["I"], c["topk"], L["n_shared"], out=outv)
+    got = to_host(outv).reshape(T, c["H"])
+    assert guards_intact(full, T * c["H"]), "write outside out"
     Es = c["E"] + L["n_shared"]
-    for t in sorted({0, T // 2, T - 1}):
-        ref, bnd, _ = oracle.moe_decode(x[t:t + 1], Wg, Wu, Wd, ids[t:t + 1], w[t:t + 1],
-                                        c["H"], c["I"], Es)
-        check_tol(got[t:t + 1], ref, bnd, TOL, f"dsv2 layer T={T} token {t}")
+    # every token against the oracle (routed + shared experts)
+    ref, bnd, _ = oracle.moe_decode(x, Wg, Wu, Wd, ids, w, c["H"], c["I"], Es)
+    check_tol(got, ref, bnd, TOL, f"dsv2 layer T={T}")
+
+
+def test_router_outputs_stay_in_bounds():
+    """logits, ids and weights are written only inside their bounds."""
+    import torch
+    from moe_experts_amd import moe_router_topk
+    T, H, E, topk, n_shared = 33, 5120, 160, 6, 2
+    x = datagen.activations(5, T, H)
+    Wr = datagen.router_weights(6, E, H)
+    slots = topk + n_shared
+    lf, lv = guarded(T * E)
+    wf, wv = guarded(T * slots)
+    idf, idv = guarded(T * slots, dtype=torch.int32, fill=-77)
+    moe_router_topk(to_dev(x), to_dev(Wr), topk, n_shared, logits=lv, ids=idv, w=wv)
+    assert guards_intact(lf, T * E) and guards_intact(wf, T * slots)
+    assert guards_intact(idf, T * slots, fill=-77)
+    ref_ids, ref_w = oracle.router_topk(to_host(lv).reshape(T, E), topk, n_shared)
+    assert (to_host(idv).reshape(T, slots) == ref_ids).all()
