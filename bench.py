@@ -15,9 +15,15 @@ MoE decode (5120 hidden, 160 experts of 5120x1536 gate/up and 1536x5120 down,
 top-6) at 1 and 32 tokens (uniform and skewed routing) in tokens/s and GB/s,
 and the prefill GEMM 2048x4096 . 4096x{4096, 11008} in TFLOP/s.
 
-``cpu_baseline``: the CPU oracle (single-threaded, double accumulation) timed
-on this host over whole dense steps for about 10 s, as GB/s of the same
-algorithmic bytes. A reported baseline, not a target.
+Attainable roofs (``also.probes``, from libq4probe.so): a read-only 16-byte
+stream at the byte counts of the decode calls and at 1 GiB, and fp16 / fp32
+MFMA loops; every per-call rate is also given as a fraction of the stream
+rate at its size.
+
+``cpu_baseline``: the CPU oracle (single-threaded, double accumulation) pinned
+to one host core, on bounded samples of every workload (dense steps in GB/s;
+MoE decode in tokens/s; prefill rows in TFLOP/s), about 20 s in all. A
+reported baseline, not a target.
 """
 from __future__ import annotations
 
@@ -54,10 +60,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="budget of the pinned single-core oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true", help="skip the MoE and prefill measurements")
-    ap.add_argument("--only", choices=["dense", "moe", "prefill", "traffic-probe"], default=None,
+    ap.add_argument("--only", choices=["dense", "moe", "prefill", "probes", "traffic-probe"],
+                    default=None,
                     help="run a single workload (for profiling); prints its own JSON line")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write the HBM traffic summary from two counter passes of the probe")
@@ -95,20 +103,34 @@ def capture(torch, fn):
     return g
 
 
-def time_graph(torch, graphs, reps, per_replay):
-    """Mean time per unit of work: replay the graphs round robin between two
-    events; each replay holds `per_replay` units (steps or launches)."""
+def time_graph_dist(torch, graphs, reps, per_replay):
+    """Replay the graphs round robin with an event after every replay; each
+    replay holds `per_replay` units (steps or launches). Returns the mean time
+    per unit over all replays and the per-replay times per unit (seconds)."""
     for g in graphs:
         g.replay()
     torch.cuda.synchronize()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record()
     for r in range(reps):
         graphs[r % len(graphs)].replay()
-    e.record()
+        evs[r + 1].record()
     torch.cuda.synchronize()
-    return s.elapsed_time(e) * 1e-3 / (reps * per_replay)
+    ts = [evs[r].elapsed_time(evs[r + 1]) * 1e-3 / per_replay for r in range(reps)]
+    return evs[0].elapsed_time(evs[-1]) * 1e-3 / (reps * per_replay), ts
+
+
+def time_graph(torch, graphs, reps, per_replay):
+    """Mean time per unit of work over `reps` round-robin replays."""
+    return time_graph_dist(torch, graphs, reps, per_replay)[0]
+
+
+def quantiles_us(ts):
+    """p10, median and p90 of a list of durations (seconds), in microseconds."""
+    v = sorted(ts)
+    q = lambda f: v[min(len(v) - 1, int(round(f * (len(v) - 1))))] * 1e6
+    return {"p10_us": round(q(0.1), 2), "median_us": round(q(0.5), 2), "p90_us": round(q(0.9), 2),
+            "n": len(v)}
 
 
 # ---------------------------------------------------------------------------
@@ -150,34 +172,46 @@ def bench_dense(torch, dev, steps, warmup):
         graphs[r % R].replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    s_ev = torch.cuda.Event(enable_timing=True)
-    e_ev = torch.cuda.Event(enable_timing=True)
-    s_ev.record()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
     for r in range(steps):
         graphs[(warmup + r) % R].replay()
-    e_ev.record()
+        evs[r + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
-    dt = s_ev.elapsed_time(e_ev) * 1e-3 / steps
+    dt = evs[0].elapsed_time(evs[-1]) * 1e-3 / steps
+    step_dist = quantiles_us([evs[r].elapsed_time(evs[r + 1]) * 1e-3 for r in range(steps)])
 
-    # per call: graphs of 8 back-to-back launches (rotating copies) of each call
+    # per call: graphs of 8 back-to-back launches of each call. Each matrix gets
+    # its own rotation of at least 1 GiB of copies (the step's copies plus
+    # clones), and the graphs walk through all of them, so every launch reads
+    # its weights from HBM rather than from the 256 MB Infinity Cache.
     per_call, per_M, call_s = {}, {}, {}
+    rot = []
+    for i, (_, K, N, _) in enumerate(shapes):
+        Ri = max(16, math.ceil(GIB / q4_bytes(K, N)))
+        Ri = (Ri + 7) // 8 * 8
+        rot.append([copies[r][i] for r in range(R)] + [base[i].clone() for _ in range(Ri - R)])
     for (M, i) in calls:
         name, K, N, _ = shapes[i]
-        gs = [capture(torch, lambda c=c: [q4_0_gemv(xs[M][K], copies[(c * 8 + u) % R][i], N,
+        ng = len(rot[i]) // 8
+        gs = [capture(torch, lambda c=c: [q4_0_gemv(xs[M][K], rot[i][c * 8 + u], N,
                                                     y=ys[(M, i)], ws=ws) for u in range(8)])
-              for c in range(2)]
-        t = time_graph(torch, gs, 10, 8)
+              for c in range(ng)]
+        t, ts = time_graph_dist(torch, gs, max(4 * ng, 48), 8)
         call_s[(M, i)] = t
         b = q4_bytes(K, N) + 4 * M * K + 4 * M * N
         per_call[f"{name}_M{M}"] = {"us": round(t * 1e6, 2), "GBps": round(b / t / 1e9, 1),
-                                    "TFLOPs": round(2 * M * K * N / t / 1e12, 2)}
+                                    "TFLOPs": round(2 * M * K * N / t / 1e12, 2),
+                                    "bytes": b, **quantiles_us(ts)}
+        del gs
     for M in Ms:
         t = sum(call_s[(M, i)] for i in range(len(shapes)))
         b = sum(q4_bytes(K, N) + 4 * M * K + 4 * M * N for _, K, N, _ in shapes)
         per_M[M] = (t * 1e3, b)
+    del rot
     return dict(step_s=dt, wall_s=wall, step_bytes=step_bytes, per_call=per_call, per_M=per_M,
-                call_s=call_s,
+                call_s=call_s, step_dist=step_dist,
                 R=R, host=host, shapes=shapes, Ms=Ms)
 
 
@@ -255,7 +289,7 @@ def measured_traffic():
     return blob.get("hbm_bytes_per_call")
 
 
-def dense_roofline(d):
+def dense_roofline(d, probes):
     """Roofline of the dominant unit (see DOMINANT).
 
     The batch-8 call runs on the fp32 matrix cores: every weight is one
@@ -291,6 +325,10 @@ def dense_roofline(d):
             "mfma_bound_us": round(mfma_s * 1e6, 2), "hbm_bound_us": round(hbm_s * 1e6, 2),
             "issue_bound_us": round((mfma_s + valu_s) * 1e6, 2),
             "issue_frac": round((mfma_s + valu_s) / t, 4), "hbm_GBps": round(gbs, 1),
+            "attainable_GBps": attainable_for(probes, algo_bytes),
+            "attainable_frac": round(gbs / attainable_for(probes, algo_bytes), 4),
+            "attainable_mfma_f32_TFLOPs": probes["mfma_f32_TFLOPs"],
+            "attainable_mfma_frac": round(tflops / probes["mfma_f32_TFLOPs"], 4),
             "note": "achieved = 2MKN / call time against the fp32 MFMA peak; issue_bound adds "
                     "the vector unpack work, which issues serially with the MFMAs on a SIMD"}
     return roof
@@ -399,28 +437,148 @@ Commands:
     print(text)
 
 
-def cpu_baseline_dense(d, seconds):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baselines(d, seconds):
+    """The oracle as it stands (single-threaded C++, double accumulation),
+    pinned to one host core in this process, on bounded samples of each
+    workload: whole dense decode steps (GB/s of the same algorithmic bytes),
+    the single-token MoE decode and four tokens of the 32-token batch
+    (tokens/s), and 32 rows of the 2048 x 4096 x 4096 prefill (TFLOP/s)."""
     import oracle
-    shapes, Ms = d["shapes"], d["Ms"]
-    xs = {M: {K: datagen_x(M, K) for K in sorted({K for _, K, _, _ in shapes})} for M in Ms}
-    done_bytes, t0, nsteps = 0, time.perf_counter(), 0
-    while True:
-        for M in Ms:
-            for i, (_, K, N, _) in enumerate(shapes):
-                oracle.q4_0_matmul(xs[M][K], d["host"][i], N, K, with_bound=False)
-                done_bytes += q4_bytes(K, N) + 4 * M * K + 4 * M * N
-        nsteps += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nsteps} whole dense step(s) (12 GEMVs each), {dt:.1f} s, single thread, "
-                      f"double accumulation; host has {os.cpu_count()} logical CPUs"}
+    from moe_experts_amd import datagen
+    allowed = sorted(os.sched_getaffinity(0))
+    core = allowed[0]
+    os.sched_setaffinity(0, {core})
+    try:
+        out = {}
+        # dense decode step
+        shapes, Ms = d["shapes"], d["Ms"]
+        xs = {M: {K: datagen_x(M, K) for K in sorted({K for _, K, _, _ in shapes})} for M in Ms}
+        done, t0, nsteps = 0, time.perf_counter(), 0
+        while True:
+            for M in Ms:
+                for i, (_, K, N, _) in enumerate(shapes):
+                    oracle.q4_0_matmul(xs[M][K], d["host"][i], N, K, with_bound=False)
+                    done += q4_bytes(K, N) + 4 * M * K + 4 * M * N
+            nsteps += 1
+            if time.perf_counter() - t0 >= 0.4 * seconds:
+                break
+        dt = time.perf_counter() - t0
+        out["dense_GBps"] = round(done / dt / 1e9, 4)
+        dense_sample = f"{nsteps} dense step(s) in {dt:.1f} s"
+        # MoE decode: one token, and 4 tokens of the 32-token batch
+        c = datagen.MOE_DSV2
+        H, I, E, topk = c["H"], c["I"], c["E"], c["topk"]
+        for label, T, cfg, ntok in (("moe_t1", 1, datagen.MOE_T1, 1),
+                                    ("moe_t32", 32, datagen.MOE_T32, 4)):
+            x = datagen.activations(cfg["x_seed"], T, H)[:ntok]
+            ids, w, _ = datagen.routing(cfg["logit_seed"], T, E, topk)
+            ids, w = ids[:ntok], w[:ntok]
+            Wg, Wu, Wd = datagen.moe_experts(H, I, E, experts=sorted(set(ids.ravel().tolist())))
+            calls, t0 = 0, time.perf_counter()
+            while True:
+                oracle.moe_decode(x, Wg, Wu, Wd, ids, w, H, I, E, with_bound=False)
+                calls += 1
+                if time.perf_counter() - t0 >= 0.15 * seconds:
+                    break
+            dt = time.perf_counter() - t0
+            out[f"{label}_tokens_per_s"] = round(calls * ntok / dt, 3)
+            del Wg, Wu, Wd
+        # prefill GEMM rows
+        pc = datagen.PREFILL
+        K, N = pc["K"], pc["Ns"][0]
+        X16 = datagen.to_f16(datagen.activations(pc["x_seed"], 32, K))
+        B = datagen.q4_0_random(pc["b_seeds"][0], K, N)
+        calls, t0 = 0, time.perf_counter()
+        while True:
+            oracle.q4_0_matmul_f16(X16, B, N, K, with_bound=False)
+            calls += 1
+            if time.perf_counter() - t0 >= 0.15 * seconds:
+                break
+        dt = time.perf_counter() - t0
+        out["prefill_TFLOPs"] = round(calls * 2 * 32 * K * N / dt / 1e12, 6)
+    finally:
+        os.sched_setaffinity(0, set(allowed))
+    return {"value": out["dense_GBps"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{dense_sample} (12 GEMVs each); MoE: repeated single-token and 4-token "
+                      "calls of the decode configurations; prefill: 32 rows of 2048 x 4096 x "
+                      "4096; single thread pinned to one core, double accumulation",
+            "cpu": cpu_model(), "pinned_core": core, "logical_cpus": os.cpu_count(),
+            "per_config": out}
 
 
 def datagen_x(M, K):
     from moe_experts_amd import datagen
     return datagen.activations(datagen.dense_x_seed(M), M, K)
+
+
+# ---------------------------------------------------------------------------
+# attainable roofs (libq4probe.so)
+# ---------------------------------------------------------------------------
+# Byte counts of the read-only stream probe: the algorithmic bytes of the
+# 4096 x 4096 call at batch 1, of a 4096 x 11008 call at batch 1, of the
+# six routed experts of a single-token MoE decode, and 1 GiB.
+PROBE_SIZES = {"gemv_4096x4096": 9469952, "gemv_4096x11008": 25422848,
+               "moe_t1_experts": 79626240, "1GiB": GIB}
+
+
+def bench_probes(torch, dev):
+    """Attainable rates measured with the probes: a read-only 16-byte stream at
+    the byte counts of the decode calls (each launch reads a different region
+    of a 2 GiB buffer, so the rotation spans far more than the 256 MB Infinity
+    Cache), best over grids of 256..2048 workgroups; and fp16 / fp32 MFMA
+    loops (4 waves per SIMD)."""
+    from moe_experts_amd import probe
+    span = 2 * GIB
+    buf = torch.empty(span + (1 << 20), dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.zeros(65536, dtype=torch.int32, device=dev)
+    res = {"stream": {}}
+    for name, nbytes in PROBE_SIZES.items():
+        stride = (nbytes + 4095) // 4096 * 4096
+        nreg = max(1, span // stride)
+        per = min(nreg, 64)
+        best = None
+        for grid in (256, 512, 1024, 2048):
+            def run(c, grid=grid):
+                for u in range(per):
+                    probe.stream_read(buf, ((c * per + u) % nreg) * stride, nbytes, grid, sink)
+            gs = [capture(torch, lambda c=c: run(c)) for c in range(max(1, min(4, nreg // per)))]
+            t, ts = time_graph_dist(torch, gs, 8 if nbytes < GIB else 4, per)
+            if best is None or t < best[0]:
+                best = (t, grid, ts)
+        t, grid, ts = best
+        res["stream"][name] = {"bytes": nbytes, "us": round(t * 1e6, 2),
+                               "GBps": round(nbytes / t / 1e9, 1), "grid": grid}
+        log(f"[probe] stream {name}: {res['stream'][name]}")
+    del buf
+    msink = torch.zeros(1024 * 256, dtype=torch.float32, device=dev)
+    for kind, iters in (("f16", 4096), ("f32", 8192)):
+        flops = [0]
+
+        def run(kind=kind, iters=iters):
+            flops[0] = probe.mfma_loop(kind, iters, 1024, msink)
+        g = capture(torch, lambda: [run() for _ in range(4)])
+        t = time_graph(torch, [g], 8, 4)
+        res[f"mfma_{kind}_TFLOPs"] = round(flops[0] / t / 1e12, 1)
+        log(f"[probe] mfma {kind}: {res[f'mfma_{kind}_TFLOPs']} TFLOP/s")
+    return res
+
+
+def attainable_for(probes, nbytes):
+    """The stream probe rate measured at the probe size closest to nbytes."""
+    st = probes["stream"]
+    k = min((k for k in st if k != "1GiB"), key=lambda k: abs(math.log(st[k]["bytes"] / nbytes)))
+    return st[k]["GBps"]
 
 
 # ---------------------------------------------------------------------------
@@ -465,12 +623,12 @@ def bench_moe(torch, dev, steps, warmup):
         # one graph per (layer copy, routing) combination in use
         n = max(steps, 16)
         graphs = [capture(torch, lambda r=r: call(r)) for r in range(16)]
-        dt = time_graph(torch, graphs, n, 1)
+        dt, ts = time_graph_dist(torch, graphs, max(n, 64), 1)
         U = np.mean([uniq[r % len(routes)] for r in range(16)])
         b = U * 3 * mat + 2 * 4 * T * H + T * topk * 8
         res[label] = {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 2),
                       "GBps": round(b / dt / 1e9, 1), "hbm_frac": round(b / dt / 1e9 / HBM_PEAK_GBS, 4),
-                      "unique_experts": round(float(U), 2)}
+                      "unique_experts": round(float(U), 2), **quantiles_us(ts)}
         log(f"[moe] {label}: {res[label]}")
     res.update(bench_moe_layer(torch, dev, steps, warmup, dW))
     res.update(bench_moe_prefill(torch, dev, steps, warmup, routed))
@@ -503,11 +661,12 @@ def bench_moe_prefill(torch, dev, steps, warmup, routed):
     for r in range(warmup):
         call(r)
     graphs = [capture(torch, lambda r=r: call(r)) for r in range(4)]
-    dt = time_graph(torch, graphs, max(steps // 2, 8), 1)
+    dt, ts = time_graph_dist(torch, graphs, max(steps // 2, 16), 1)
     flops = T * topk * 3 * 2.0 * H * I
     tf = flops / dt / 1e12
     res = {"prefill_t2048": {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 1),
-                             "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}}
+                             "TFLOPs": round(tf, 1), "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                             **quantiles_us(ts)}}
     log(f"[moe] prefill_t2048: {res['prefill_t2048']}")
     return res
 
@@ -544,12 +703,12 @@ def bench_moe_layer(torch, dev, steps, warmup, dW):
         for r in range(warmup):
             call(r)
         graphs = [capture(torch, lambda r=r: call(r)) for r in range(16)]
-        dt = time_graph(torch, graphs, max(steps, 16), 1)
+        dt, ts = time_graph_dist(torch, graphs, max(steps, 64), 1)
         U = float(np.mean(uniq))
         b = U * 3 * mat + E * H * 4 + 2 * 4 * T * H
         res[label] = {"tokens_per_s": round(T / dt, 1), "us_per_call": round(dt * 1e6, 2),
                       "GBps": round(b / dt / 1e9, 1), "hbm_frac": round(b / dt / 1e9 / HBM_PEAK_GBS, 4),
-                      "unique_experts_incl_shared": round(U, 2)}
+                      "unique_experts_incl_shared": round(U, 2), **quantiles_us(ts)}
         log(f"[moe] {label}: {res[label]}")
     return res
 
@@ -569,10 +728,11 @@ def bench_prefill(torch, dev, steps, warmup):
         for _ in range(warmup):
             q4_0_gemm(X, B, N, Y=Y)
         g = capture(torch, lambda: [q4_0_gemm(X, B, N, Y=Y) for _ in range(4)])
-        ms = time_graph(torch, [g], max(steps, 10) // 4 + 1, 4) * 1e3
+        t, ts = time_graph_dist(torch, [g], max(steps, 64) // 4 + 1, 4)
+        ms = t * 1e3
         tf = 2 * M * N * K / (ms * 1e-3) / 1e12
         res[f"N{N}"] = {"us": round(ms * 1e3, 1), "TFLOPs": round(tf, 1),
-                        "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4)}
+                        "mfma_frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), **quantiles_us(ts)}
         log(f"[prefill] N={N}: {res[f'N{N}']}")
     return res
 
@@ -599,14 +759,21 @@ def main():
     if args.only == "prefill":
         print(json.dumps({"prefill": bench_prefill(torch, dev, args.steps, args.warmup)}), flush=True)
         return
+    if args.only == "probes":
+        print(json.dumps({"probes": bench_probes(torch, dev)}), flush=True)
+        return
 
+    probes = bench_probes(torch, dev)
     d = bench_dense(torch, dev, args.steps, args.warmup)
     value = d["step_bytes"] / d["step_s"] / 1e9
     log(f"[dense] step {d['step_s'] * 1e3:.3f} ms (wall {d['wall_s'] * 1e3:.3f} ms), {value:.1f} GB/s")
     for k, v in d["per_call"].items():
         log(f"  {k:22s} {v}")
-    roof = dense_roofline(d)
-    extras = {}
+    roof = dense_roofline(d, probes)
+    for k, v in d["per_call"].items():
+        v["attainable_GBps"] = attainable_for(probes, v["bytes"])
+        v["attainable_frac"] = round(v["GBps"] / v["attainable_GBps"], 4)
+    extras = {"probes": probes}
     if not args.no_extras and args.only is None:
         extras["moe_decode"] = bench_moe(torch, dev, args.steps, args.warmup)
         extras["prefill_gemm"] = bench_prefill(torch, dev, args.steps, args.warmup)
@@ -617,7 +784,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and args.only is None:
         log("[cpu] timing the oracle")
-        cpu = cpu_baseline_dense(d, args.cpu_seconds)
+        cpu = cpu_baselines(d, args.cpu_seconds)
     line = {
         "metric": "Q4_0 decode GEMV achieved HBM GB/s (dense 7B decode linears)",
         "value": round(value, 2),
@@ -634,7 +801,8 @@ def main():
         "config": {"workload": "dense 7B-shaped decode linears: Q4_0 4096x4096, 4096x11008 (x2), "
                                "11008x4096 at batch 1, 4 and 8 (12 GEMVs per step)",
                    "weights": "Q4_0 (18 B per 32 weights)", "rotation_copies": d["R"],
-                   "hbm_frac": round(value / HBM_PEAK_GBS, 4)},
+                   "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+                   "step_time": d["step_dist"]},
         "roofline": roof,
         "cpu_baseline": cpu,
         "also": extras,

@@ -1,4 +1,5 @@
-"""Build libq4moe.so (gfx950 HIP kernels + C ABI) in-tree with hipcc."""
+"""Build libq4moe.so (gfx950 HIP kernels + C ABI) and libq4probe.so (the
+attainable-roof probes) in-tree with hipcc."""
 from __future__ import annotations
 
 import os
@@ -9,6 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libq4moe.so")
+PROBE_LIB = os.path.join(PKG, "libq4probe.so")
+PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["q4moe_api.cpp", "gemv_q4_0.hip", "gemv_mfma_q4_0.hip", "gemv_q8_0.hip",
            "moe_q4_0.hip", "router_moe.hip", "moe_prefill.hip", "gemm_q4_0.hip"]
 # Per-source extra flags. The matrix-core tiles keep their accumulators in
@@ -30,7 +33,14 @@ FLAGS = [
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source into libq4moe.so (always recompiles)."""
+    """Compile every source into libq4moe.so and the probes into libq4probe.so
+    (always recompiles). Returns the path of libq4moe.so."""
+    _build_lib(SOURCES, LIB, verbose)
+    _build_lib(PROBE_SOURCES, PROBE_LIB, verbose)
+    return LIB
+
+
+def _build_lib(sources, lib, verbose: bool) -> str:
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
@@ -44,26 +54,26 @@ def build(verbose: bool = False) -> str:
                 print(" ".join(cmd), flush=True)
             return obj, subprocess.run(cmd, capture_output=True, text=True)
 
-        with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-            results = list(ex.map(compile_one, SOURCES))
+        with ThreadPoolExecutor(max_workers=min(4, len(sources))) as ex:
+            results = list(ex.map(compile_one, sources))
         objs = []
         for obj, res in results:
             err = "\n".join(l for l in res.stderr.splitlines()
                             if "packed-fp32-ops" not in l and l.strip())
             if res.returncode != 0:
                 sys.stderr.write(err + "\n")
-                raise RuntimeError("hipcc failed building libq4moe.so")
+                raise RuntimeError(f"hipcc failed building {os.path.basename(lib)}")
             if err and verbose:
                 sys.stderr.write(err + "\n")
             objs.append(obj)
-        tmp = LIB + ".tmp%d" % os.getpid()
+        tmp = lib + ".tmp%d" % os.getpid()
         cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             sys.stderr.write(res.stderr + "\n")
-            raise RuntimeError("hipcc failed linking libq4moe.so")
-        os.replace(tmp, LIB)
-    return LIB
+            raise RuntimeError(f"hipcc failed linking {os.path.basename(lib)}")
+        os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

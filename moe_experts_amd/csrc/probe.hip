@@ -1,0 +1,113 @@
+// Attainable-roof probes (include/q4probe.h): a read-only 16-byte stream and
+// matrix-unit loops, built into their own library (libq4probe.so) so the
+// benchmark can measure what the GPU delivers beside the Q4_0 kernels.
+#include "q4probe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "q4moe.h"
+
+namespace {
+
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+constexpr int kLanes = 256;
+constexpr int kUnroll = 8;  // loads in flight per lane
+constexpr uint32_t kOut = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Chunk i (16 bytes) of the buffer is read by lane i % (grid * 256) in round
+// i / (grid * 256); each lane keeps kUnroll rounds in flight. Chunks past the
+// end read out of range (no memory access).
+__global__ __launch_bounds__(kLanes) void probe_stream_kernel(const uint8_t* src, uint32_t bytes,
+                                                              uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(src, bytes);
+  const uint32_t n16 = bytes / 16;
+  const uint32_t stride = gridDim.x * kLanes;
+  uint32_t acc = 0;
+  for (uint32_t i0 = blockIdx.x * kLanes + threadIdx.x; i0 < n16; i0 += kUnroll * stride) {
+    uint32_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t i = i0 + u * stride;
+      const auto q = __builtin_amdgcn_raw_buffer_load_b128(r, i < n16 ? i * 16u : kOut, 0, 0);
+      v[u] = q[0] ^ q[1] ^ q[2] ^ q[3];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+__global__ __launch_bounds__(kLanes) void probe_mfma_f16_kernel(int iters, float* sink) {
+  v4f acc[8];
+  v8h a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    a[i] = (_Float16)(1.0f / 1024.0f);
+    b[i] = (_Float16)(float)(threadIdx.x & 7);
+  }
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  sink[blockIdx.x * kLanes + threadIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kLanes) void probe_mfma_f32_kernel(int iters, float* sink) {
+  v4f acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const float a = 1.0f / 1024.0f;
+  const float b = (float)(threadIdx.x & 7);
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = __builtin_amdgcn_mfma_f32_4x4x1f32(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  sink[blockIdx.x * kLanes + threadIdx.x] = s;
+}
+
+int launched() { return hipGetLastError() == hipSuccess ? Q4_OK : Q4_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+int q4_probe_stream(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream) {
+  if (!src || !sink || bytes < 16 || bytes % 16 != 0 || bytes >= (1ull << 32) || grid < 1 ||
+      grid > 65536)
+    return Q4_EINVAL;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return Q4_EALIGN;
+  hipLaunchKernelGGL(probe_stream_kernel, dim3(grid), dim3(kLanes), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src),
+                     (uint32_t)bytes, sink);
+  return launched();
+}
+
+int q4_probe_mfma_f16(int iters, int grid, float* sink, void* stream) {
+  if (!sink || iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536) return Q4_EINVAL;
+  hipLaunchKernelGGL(probe_mfma_f16_kernel, dim3(grid), dim3(kLanes), 0,
+                     static_cast<hipStream_t>(stream), iters, sink);
+  return launched();
+}
+
+int q4_probe_mfma_f32(int iters, int grid, float* sink, void* stream) {
+  if (!sink || iters < 1 || iters > (1 << 20) || grid < 1 || grid > 65536) return Q4_EINVAL;
+  hipLaunchKernelGGL(probe_mfma_f32_kernel, dim3(grid), dim3(kLanes), 0,
+                     static_cast<hipStream_t>(stream), iters, sink);
+  return launched();
+}
+
+}  // extern "C"

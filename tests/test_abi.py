@@ -36,8 +36,12 @@ def lib():
     return L
 
 
-def declared_functions():
-    text = open(HEADER).read()
+PROBE_HEADER = os.path.join(ROOT, "include", "q4probe.h")
+PROBE_LIB = os.path.join(ROOT, "moe_experts_amd", "libq4probe.so")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_0-9]+)\s*\(", text, flags=re.M)
     return sorted(set(n for n in names if not n.startswith("_") and n != "sizeof"))
@@ -54,6 +58,38 @@ def test_header_declares_the_entry_points():
 def test_library_exports_every_declared_symbol(lib):
     for n in declared_functions():
         assert hasattr(lib, n), f"{n} declared in q4moe.h but not exported"
+
+
+def test_every_header_has_its_library():
+    """Each header under include/ belongs to one in-tree library, which loads
+    and exports every function the header declares."""
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["q4moe.h", "q4probe.h"]
+    if not os.path.exists(PROBE_LIB):
+        from moe_experts_amd import build
+        build.build()
+    probe = ctypes.CDLL(PROBE_LIB)
+    names = declared_functions(PROBE_HEADER)
+    assert names == ["q4_probe_mfma_f16", "q4_probe_mfma_f32", "q4_probe_stream"]
+    for n in names:
+        assert hasattr(probe, n), f"{n} declared in q4probe.h but not exported"
+
+
+def test_probes_reject_bad_arguments():
+    probe = ctypes.CDLL(PROBE_LIB)
+    P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    probe.q4_probe_stream.argtypes = [P, Z, I, P, P]
+    probe.q4_probe_mfma_f16.argtypes = [I, I, P, P]
+    probe.q4_probe_mfma_f32.argtypes = [I, I, P, P]
+    assert probe.q4_probe_stream(None, 1024, 8, FAKE, None) == -1
+    assert probe.q4_probe_stream(FAKE, 1000, 8, FAKE, None) == -1   # not a multiple of 16
+    assert probe.q4_probe_stream(FAKE, 1 << 32, 8, FAKE, None) == -1
+    assert probe.q4_probe_stream(FAKE, 1024, 0, FAKE, None) == -1
+    assert probe.q4_probe_stream(FAKE + 4, 1024, 8, FAKE, None) == -3
+    for f in (probe.q4_probe_mfma_f16, probe.q4_probe_mfma_f32):
+        assert f(0, 8, FAKE, None) == -1
+        assert f(8, 0, FAKE, None) == -1
+        assert f(8, 8, None, None) == -1
 
 
 def test_strerror(lib):
