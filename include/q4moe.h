@@ -104,6 +104,22 @@ size_t q4_0_gemv_workspace_bytes(int M, int N, int K);
 int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K, void* ws,
               size_t ws_bytes, void* stream);
 
+/* Allocation-free q4_0_gemv, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results as q4_0_gemv, without ws:
+ * the K-split partial sums go to a static device array of
+ * Q4_GEMV_NOALLOC_MAX_WS bytes that the library holds on each GPU it runs on
+ * until the process ends. Nothing in it needs to start at zero (every partial
+ * is written before it is read). All calls on one GPU share that array, so
+ * calls that overlap on one GPU (concurrent streams, or threads) race; calls
+ * in one stream do not.
+ * Errors: those of q4_0_gemv, and Q4_ETOOBIG when
+ * q4_0_gemv_workspace_bytes(M, N, K) exceeds Q4_GEMV_NOALLOC_MAX_WS (nothing
+ * enqueued). Calls no allocating routine. */
+#define Q4_GEMV_NOALLOC_MAX_WS (16u << 20)
+int q4_0_gemv_noalloc(const float* x, const q4_0_block* B, float* y, int M, int N, int K,
+                      void* stream);
+
 /* ---------------------------------------------------------------------------
  * Decode GEMV over Q8_0 weights (batch 1..8): y[M x N] = x[M x K] . deq(B[K x N]),
  * the Q8_0 counterpart of q4_0_gemv for the article's Q8_0-versus-Q4_0

@@ -37,6 +37,8 @@ _lib.q4_0_gemv_workspace_bytes.restype = _Z
 _lib.q4_0_gemv_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.q4_0_gemv.restype = _I
 _lib.q4_0_gemv.argtypes = [_P, _P, _P, _I, _I, _I, _P, _Z, _P]
+_lib.q4_0_gemv_noalloc.restype = _I
+_lib.q4_0_gemv_noalloc.argtypes = [_P, _P, _P, _I, _I, _I, _P]
 _lib.q8_0_gemv_workspace_bytes.restype = _Z
 _lib.q8_0_gemv_workspace_bytes.argtypes = [_I, _I, _I]
 _lib.q8_0_gemv.restype = _I
@@ -148,6 +150,26 @@ def q4_0_gemv(x: torch.Tensor, B: torch.Tensor, N: int, y: torch.Tensor | None =
         ws = workspace(need, x.device)
     pw, nw = (None, 0) if ws is None else (_dev(ws, "ws", torch.uint8, ws.numel()), ws.numel())
     _check(_lib.q4_0_gemv(px, pb, py, M, N, K, pw, nw, _stream(x.device)))
+    return y
+
+
+# Largest q4_0_gemv workspace q4_0_gemv_noalloc serves from its static array.
+GEMV_NOALLOC_MAX_WS = 16 << 20
+
+
+def q4_0_gemv_noalloc(x: torch.Tensor, B: torch.Tensor, N: int,
+                      y: torch.Tensor) -> torch.Tensor:
+    """q4_0_gemv into a caller-provided y without any device allocation: the
+    K-split partials live in the library's static per-GPU array."""
+    if x.dim() != 2:
+        raise ValueError("x must be [M, K]")
+    M, K = x.shape
+    if N <= 0 or N % 32:
+        raise ValueError("N must be a positive multiple of 32")
+    px = _dev(x, "x", torch.float32, M * K)
+    pb = _dev(B, "B", torch.uint8, K * (N // 32) * BLOCK_BYTES)
+    py = _dev(y, "y", torch.float32, M * N)
+    _check(_lib.q4_0_gemv_noalloc(px, pb, py, M, N, K, _stream(x.device)))
     return y
 
 

@@ -13,7 +13,8 @@ LIB = os.path.join(PKG, "libq4moe.so")
 PROBE_LIB = os.path.join(PKG, "libq4probe.so")
 PROBE_SOURCES = ["probe.hip"]
 SOURCES = ["q4moe_api.cpp", "gemv_q4_0.hip", "gemv_mfma_q4_0.hip", "gemv_q8_0.hip",
-           "moe_q4_0.hip", "router_moe.hip", "moe_prefill.hip", "gemm_q4_0.hip"]
+           "moe_q4_0.hip", "router_moe.hip", "moe_prefill.hip", "gemm_q4_0.hip",
+           "gemv_noalloc.hip"]
 # Per-source extra flags. The matrix-core tiles keep their accumulators in
 # ordinary VGPRs (MFMA "VGPR form"): with accumulation registers the
 # allocator rotated the accumulators between loop iterations (register copies

@@ -170,6 +170,21 @@ def test_moe_rejects_buffers_past_32_bit_offsets(lib):
     assert lib.moe_q4_0_workspace_bytes(T, H, 1 << 14, E, topk) > 0
 
 
+def test_gemv_noalloc_rejects_workspace_past_its_array(lib):
+    """q4_0_gemv_noalloc serves the K-split partials from a fixed static
+    array: a shape that needs more is refused before any HIP call, and bad
+    arguments get q4_0_gemv's own errors."""
+    P, I = ctypes.c_void_p, ctypes.c_int
+    f = lib.q4_0_gemv_noalloc
+    f.argtypes = [P, P, P, I, I, I, P]
+    M, K, N = 8, 4096, 393216
+    assert lib.q4_0_gemv_workspace_bytes(M, N, K) > (16 << 20)
+    assert f(FAKE, FAKE, FAKE, M, N, K, None) == -6
+    assert f(None, FAKE, FAKE, 1, 64, 64, None) == -1
+    assert f(FAKE, FAKE, FAKE, 1, 48, 64, None) == -2
+    assert f(FAKE, FAKE, FAKE, 9, 64, 64, None) == -2
+
+
 def test_route_layout(lib):
     Z = ctypes.c_size_t
     lib.moe_q4_0_route_layout.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(Z)] * 3
