@@ -319,7 +319,7 @@ def dense_roofline(d, probes):
             "unit": "TFLOP/s", "frac": round(tflops / MFMA_F32_PEAK_TFLOPS, 4),
             "traffic": measured_traffic(),
             "kernel": f"q4_0_gemv M={M} on 4096x11008 (gemv_q4_0_mfma_kernel<2,8,4> + "
-                      "gemv_q4_0_reduce_kernel)",
+                      "gemv_reduce_kernel)",
             "avg_launch_us": round(t * 1e6, 2),
             "algorithmic_bytes": algo_bytes, "algorithmic_flops": flops,
             "mfma_bound_us": round(mfma_s * 1e6, 2), "hbm_bound_us": round(hbm_s * 1e6, 2),
@@ -391,8 +391,8 @@ def traffic_summary(fetch_csv, write_csv, command):
     f_write = copy_bytes / cw
     main_f = med(pick(fetch, MAIN_KERNEL)[4:])
     main_w = med(pick(write, MAIN_KERNEL)[4:])
-    red_f = med(pick(fetch, "gemv_q4_0_reduce_kernel")[4:])
-    red_w = med(pick(write, "gemv_q4_0_reduce_kernel")[4:])
+    red_f = med(pick(fetch, "gemv_reduce_kernel")[4:])
+    red_w = med(pick(write, "gemv_reduce_kernel")[4:])
     M = DOMINANT["M"]
     K, N = 4096, 11008
     algo = q4_bytes(K, N) + 4 * M * K + 4 * M * N
@@ -417,7 +417,7 @@ scale the kernel's counter values to bytes.
 | dispatch | fetched (B) | written (B) |
 |---|---|---|
 | gemv_q4_0_mfma_kernel<2,8,4> | {round(main_f * f_fetch)} | {round(main_w * f_write)} |
-| gemv_q4_0_reduce_kernel | {round(red_f * f_fetch)} | {round(red_w * f_write)} |
+| gemv_reduce_kernel | {round(red_f * f_fetch)} | {round(red_w * f_write)} |
 | **call** | {round((main_f + red_f) * f_fetch)} | {round((main_w + red_w) * f_write)} |
 
 Algorithmic bytes per call: {algo} (weights once, activations, outputs). Measured / algorithmic:

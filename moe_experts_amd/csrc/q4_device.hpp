@@ -153,6 +153,115 @@ __device__ __forceinline__ void load_part_buf(__amdgpu_buffer_rsrc_t r, uint32_t
 }
 
 // ---------------------------------------------------------------------------
+// Block formats of the vector split-K tiles. Every format stores blocks of 32
+// weights along N, a binary16 scale d first; LPB lanes split a block, each
+// holding 32 / LPB consecutive columns. A format supplies:
+//   kBlockBytes             bytes per block;
+//   kOffset                 whether weights carry the "- 8" offset that the
+//                           tile folds into one correction sum per row;
+//   Part<LPB>               the raw bytes of one lane's share (the scale bits
+//                           and kWords dwords of values);
+//   load<LPB>(...)          load a share through a buffer resource (vofs: the
+//                           lane's byte offset of the block, sofs: uniform);
+//   accumulate<M, LPB>(...) unpack a share and add s * value into acc[m][c]
+//                           (c = column within the share) for M rows;
+//   finish(sum, c, csum)    turn column c's summed accumulator into output;
+// and its tile shape: kJt block columns per workgroup, lanes_per_block(M),
+// rows_per_batch(M) (rows per lane in one pipelined batch) and
+// grid_target(M) (workgroups the split-K plan aims at). The tile walk, the
+// activation staging, the phase sums, the split-K plan and the reduction are
+// shared, so a format is a template parameter of one kernel.
+// ---------------------------------------------------------------------------
+
+// Q4_0 ("2000-line C++ DeepSeek inference engine" article, §2.2): 18 bytes,
+// 16 bytes of nibbles after the scale, value (q - 8) * d; arithmetic as set
+// out at the top of this file.
+struct Q4_0Format {
+  static constexpr int kBlockBytes = 18;
+  static constexpr bool kOffset = true;
+  static constexpr int kJt = 16;
+  template <int LPB>
+  using Part = BlockPart<LPB>;
+  __host__ __device__ static constexpr int lanes_per_block(int M) { return M == 1 ? 1 : 2; }
+  __host__ __device__ static constexpr int rows_per_batch(int M) { return M <= 4 ? 8 : 4; }
+  __host__ __device__ static constexpr int grid_target(int) { return 512; }
+  template <int LPB>
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t vofs,
+                                              uint32_t sofs, int part, Part<LPB>& out) {
+    load_part_buf<LPB>(r, vofs, sofs, part, out);
+  }
+  template <int M, int LPB>
+  __device__ __forceinline__ static void accumulate(const float (&xv)[M], const Part<LPB>& b,
+                                                    float (&acc)[M][32 / LPB],
+                                                    float (&corr)[M]) {
+    fma_part<M, LPB>(xv, b, acc, corr);
+  }
+  // even columns hold sum(s * lo), odd ones sum(s * 16 * hi): both minus 8 * sum(s)
+  __device__ __forceinline__ static float finish(float sum, int c, float csum) {
+    return ((c & 1) ? sum * 0.0625f : sum) - 8.0f * csum;
+  }
+};
+
+// Q8_0: the article (§2.2) weighs it against Q4_0 (twice the bytes, about 60 %
+// of Q4_0's token rate on the author's CPU) without defining it; read as 34
+// little-endian bytes, the scale then 32 signed bytes q, weight l = q[l] * d.
+// One convert (sign-extended byte to fp32) and one FMA per weight and row,
+// s = x * d formed once per block and row.
+template <int LPB>
+struct Q8Part {
+  static constexpr int kWords = 8 / LPB;
+  uint32_t d;
+  uint32_t q[kWords];
+};
+
+struct Q8_0Format {
+  static constexpr int kBlockBytes = 34;
+  static constexpr bool kOffset = false;
+  static constexpr int kJt = 8;
+  template <int LPB>
+  using Part = Q8Part<LPB>;
+  __host__ __device__ static constexpr int lanes_per_block(int M) { return M == 1 ? 2 : 4; }
+  __host__ __device__ static constexpr int rows_per_batch(int) { return 4; }
+  __host__ __device__ static constexpr int grid_target(int M) { return M >= 2 ? 512 : 352; }
+  template <int LPB>
+  __device__ __forceinline__ static void load(__amdgpu_buffer_rsrc_t r, uint32_t vofs,
+                                              uint32_t sofs, int part, Part<LPB>& out) {
+    out.d = __builtin_amdgcn_raw_buffer_load_b16(r, vofs, sofs, 0);
+    const uint32_t qo = vofs + 2 + part * (32 / LPB);  // 2-byte aligned: unaligned loads
+    if constexpr (LPB == 2) {
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, qo, sofs, 0);
+      out.q[0] = v[0];
+      out.q[1] = v[1];
+      out.q[2] = v[2];
+      out.q[3] = v[3];
+    } else {
+      static_assert(LPB == 4, "half or quarter blocks");
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, qo, sofs, 0);
+      out.q[0] = v[0];
+      out.q[1] = v[1];
+    }
+  }
+  template <int M, int LPB>
+  __device__ __forceinline__ static void accumulate(const float (&xv)[M], const Part<LPB>& b,
+                                                    float (&acc)[M][32 / LPB], float (&)[M]) {
+    const float d = half_bits_to_float(b.d);
+    float s[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) s[m] = xv[m] * d;
+#pragma unroll
+    for (int w = 0; w < Part<LPB>::kWords; ++w)
+#pragma unroll
+      for (int by = 0; by < 4; ++by) {
+        const float f = static_cast<float>(static_cast<int8_t>(b.q[w] >> (8 * by)));
+        const int c = 4 * w + by;
+#pragma unroll
+        for (int m = 0; m < M; ++m) acc[m][c] = __builtin_fmaf(s[m], f, acc[m][c]);
+      }
+  }
+  __device__ __forceinline__ static float finish(float sum, int, float) { return sum; }
+};
+
+// ---------------------------------------------------------------------------
 // Split-K tile. A workgroup of 256 lanes owns Jt consecutive block columns
 // (j0 .. j0+Jt-1) and the rows [k0, k0 + rows) of a K x NB-block matrix. Its
 // lanes form P = 256 / (Jt*LPB) row phases of Lr = Jt*LPB lanes; lane t is row
@@ -277,11 +386,12 @@ constexpr int vmcnt_imm(int n) {
   return (n & 0xf) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8);
 }
 
-template <int M, int LPB, int RB>
+template <int M, int LPB, int RB, class Fmt = Q4_0Format>
 __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float* __restrict__ x,
                                                 uint32_t x_bytes, const int (&xoff)[M],
                                                 float* __restrict__ xs,
                                                 float (&acc)[M][32 / LPB], float (&corr)[M]) {
+  using Part = typename Fmt::template Part<LPB>;
   constexpr uint32_t kOutOfRange = 0x80000000u;
   constexpr int kLoadsPerBatch = 2 * RB;  // scale + nibble load per row
   static_assert(2 * kLoadsPerBatch < 64, "vmcnt range");
@@ -300,10 +410,10 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
   const int nl = (g.rows + g.P - 1) / g.P;  // rows of the busiest lane (uniform)
   const int nb = (nl + RB - 1) / RB;         // batches (uniform)
   const int rows_pad = nb * RB * g.P;
-  const uint32_t row_bytes = (uint32_t)g.NB * kBlockBytes;
+  const uint32_t row_bytes = (uint32_t)g.NB * Fmt::kBlockBytes;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(g.B, (uint32_t)g.K * row_bytes);
-  const uint32_t vcol = (uint32_t)(g.j0 + jj) * kBlockBytes;  // lane's block in row 0
-  const uint32_t sbase = (uint32_t)g.k0 * row_bytes;           // uniform
+  const uint32_t vcol = (uint32_t)(g.j0 + jj) * Fmt::kBlockBytes;  // lane's block in row 0
+  const uint32_t sbase = (uint32_t)g.k0 * row_bytes;                // uniform
   const int rows = active ? g.rows : 0;
 
   stage_x_tile<M>(x, x_bytes, xoff, g.k0, g.rows, rows_pad, xs);
@@ -311,22 +421,22 @@ __device__ __forceinline__ void tile_accumulate(const SplitTile& g, const float*
   // weight loads.
   __builtin_amdgcn_sched_barrier(0);
 
-  BlockPart<LPB> A[RB], Bs[RB];
-  auto load_batch = [&](int b, BlockPart<LPB>(&R)[RB]) {
+  Part A[RB], Bs[RB];
+  auto load_batch = [&](int b, Part(&R)[RB]) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int tr = (b * RB + i) * g.P + r;  // tile row of this lane
       const uint32_t vo = tr < rows ? vcol + (uint32_t)tr * row_bytes : kOutOfRange;
-      load_part_buf<LPB>(rw, vo, sbase, part, R[i]);
+      Fmt::template load<LPB>(rw, vo, sbase, part, R[i]);
     }
   };
-  auto compute_batch = [&](int b, BlockPart<LPB>(&R)[RB]) {
+  auto compute_batch = [&](int b, Part(&R)[RB]) {
     float xv[RB][M];
 #pragma unroll
     for (int i = 0; i < RB; ++i) read_x_row<M>(xs, (b * RB + i) * g.P + r, xv[i]);
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      if (b * RB + i < nl) fma_part<M, LPB>(xv[i], R[i], acc, corr);
+      if (b * RB + i < nl) Fmt::template accumulate<M, LPB>(xv[i], R[i], acc, corr);
       __builtin_amdgcn_sched_barrier(0);  // one row's unpacked values live at a time
     }
   };
@@ -583,22 +693,24 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
 }
 
 // LDS floats needed by reduce_phases: one activation row's accumulators,
-// the raw corrections of all rows and their phase sums.
-template <int M, int LPB>
+// and for formats with the offset the raw corrections of all rows and their
+// phase sums.
+template <int M, int LPB, class Fmt = Q4_0Format>
 constexpr int phase_lds_floats() {
-  return (32 / LPB) * (256 + 1) + M * (256 + 1) + M * 256;
+  return (32 / LPB) * (256 + 1) + (Fmt::kOffset ? M * (256 + 1) + M * 256 : 0);
 }
 
 // Sum a split-K tile over its P row phases through LDS, in phase order 0..P-1,
-// then finish each output once: even columns sum - 8*csum, odd columns
-// sum/16 - 8*csum (csum = the phase sum of the corrections; both rescalings
-// are exact). The phase sum is linear, so finishing after it equals finishing
-// every lane first, at 1/P of the work; the sums of acc and of 8*corr still
-// run in the same order, so all-8 nibbles still give exactly zero.
+// then finish each output once with Fmt::finish. For Q4_0: even columns
+// sum - 8*csum, odd columns sum/16 - 8*csum (csum = the phase sum of the
+// corrections; both rescalings are exact). The phase sum is linear, so
+// finishing after it equals finishing every lane first, at 1/P of the work;
+// the sums of acc and of 8*corr still run in the same order, so all-8 nibbles
+// still give exactly zero. Formats without the offset skip the corrections.
 // Hands each tile output (m, o), o in [0, ncols) with ncols <= 512, to
 // store(m, o, v). Needs 256 lanes and phase_lds_floats<M, LPB>() floats of
 // smem; contains workgroup barriers; ends with a barrier.
-template <int M, int LPB, class Store>
+template <int M, int LPB, class Fmt = Q4_0Format, class Store>
 __device__ __forceinline__ void reduce_phases(const float (&acc)[M][32 / LPB],
                                               const float (&corr)[M], float* smem, int Lr, int P,
                                               int ncols, Store store) {
@@ -609,15 +721,17 @@ __device__ __forceinline__ void reduce_phases(const float (&acc)[M][32 / LPB],
   float* CS = C + M * kStride;      // [M][256] phase sums of the corrections
   const int t = threadIdx.x;
   __syncthreads();
+  if constexpr (Fmt::kOffset) {
 #pragma unroll
-  for (int m = 0; m < M; ++m) C[m * kStride + t] = corr[m];
-  __syncthreads();
-  for (int q = t; q < M * Lr; q += 256) {
-    const int m = q / Lr;
-    const int v = q - m * Lr;
-    float sum = 0.0f;
-    for (int rr = 0; rr < P; ++rr) sum += C[m * kStride + rr * Lr + v];
-    CS[m * 256 + v] = sum;
+    for (int m = 0; m < M; ++m) C[m * kStride + t] = corr[m];
+    __syncthreads();
+    for (int q = t; q < M * Lr; q += 256) {
+      const int m = q / Lr;
+      const int v = q - m * Lr;
+      float sum = 0.0f;
+      for (int rr = 0; rr < P; ++rr) sum += C[m * kStride + rr * Lr + v];
+      CS[m * 256 + v] = sum;
+    }
   }
   // this thread's outputs o = t and t + 256
   int cc_[2], vv_[2];
@@ -642,8 +756,8 @@ __device__ __forceinline__ void reduce_phases(const float (&acc)[M][32 / LPB],
         const float* src = A + cc_[k] * kStride + vv_[k];
         float sum = 0.0f;
         for (int rr = 0; rr < P; ++rr) sum += src[rr * Lr];
-        const float c8 = 8.0f * CS[m * 256 + vv_[k]];
-        store(m, o, ((cc_[k] & 1) ? sum * 0.0625f : sum) - c8);
+        const float csum = Fmt::kOffset ? CS[m * 256 + vv_[k]] : 0.0f;
+        store(m, o, Fmt::finish(sum, cc_[k], csum));
       }
     }
     __syncthreads();
