@@ -26,6 +26,8 @@
  *    reports a launch failure returned by the HIP runtime.
  *  - Workspace: entry points that take `ws` need at least the number of bytes
  *    the matching *_workspace_bytes() returns, 256-byte aligned device memory.
+ *    A *_workspace_bytes() function returns 0 for every shape its entry point
+ *    refuses (and for shapes that need no workspace); it never fails otherwise.
  *    Its contents are scratch (no initialisation needed). One workspace serves
  *    one call at a time: calls that overlap in time (for example on two
  *    streams) need separate workspaces.

@@ -41,7 +41,21 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
-def _build_lib(sources, lib, verbose: bool) -> str:
+# Host-side sanitizers for the C ABI's argument checks and plans: each
+# -fsanitize applies to the host pass only (-Xarch_host); device code is
+# built as usual.
+SANITIZE_HOST = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                 "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer").split()
+
+
+def build_sanitized(out: str, verbose: bool = False) -> str:
+    """Build libq4moe.so with AddressSanitizer and UndefinedBehaviorSanitizer
+    on its host code into `out` (load it in a process started with clang's
+    ASan runtime preloaded)."""
+    return _build_lib(SOURCES, out, verbose, extra=SANITIZE_HOST)
+
+
+def _build_lib(sources, lib, verbose: bool, extra=()) -> str:
     import tempfile
     from concurrent.futures import ThreadPoolExecutor
 
@@ -49,7 +63,7 @@ def _build_lib(sources, lib, verbose: bool) -> str:
     with tempfile.TemporaryDirectory(prefix="q4moe_build_") as tmpdir:
         def compile_one(src: str):
             obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
-            cmd = [HIPCC, *cflags, *EXTRA.get(src, []), "-c", "-o", obj,
+            cmd = [HIPCC, *cflags, *EXTRA.get(src, []), *extra, "-c", "-o", obj,
                    os.path.join(CSRC, src)]
             if verbose:
                 print(" ".join(cmd), flush=True)
@@ -68,7 +82,7 @@ def _build_lib(sources, lib, verbose: bool) -> str:
                 sys.stderr.write(err + "\n")
             objs.append(obj)
         tmp = lib + ".tmp%d" % os.getpid()
-        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             sys.stderr.write(res.stderr + "\n")

@@ -15,22 +15,30 @@ constexpr long long kMaxBytes = 0x7fffffffLL;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-int check_gemv(const float* x, const q4_0_block* B, const float* y, int M, int N, int K) {
-  if (!x || !B || !y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
+// Shape limits of the decode GEMVs (block_bytes: 18 for Q4_0, 34 for Q8_0).
+// The workspace-size functions apply them too, so a shape the entry point
+// refuses never reaches a plan.
+int check_gemv_shape(int M, int N, int K, int block_bytes) {
+  if (M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
   if (N % 32 != 0 || M > Q4_GEMV_MAX_M) return Q4_ESHAPE;
-  if ((long long)K * (N / 32) * 18 > kMaxBytes || (long long)M * K * 4 > kMaxBytes ||
+  if ((long long)K * (N / 32) * block_bytes > kMaxBytes || (long long)M * K * 4 > kMaxBytes ||
       (long long)M * N * 4 > kMaxBytes)
     return Q4_ETOOBIG;
+  return Q4_OK;
+}
+
+int check_gemv(const float* x, const q4_0_block* B, const float* y, int M, int N, int K) {
+  if (!x || !B || !y) return Q4_EINVAL;
+  const int rc = check_gemv_shape(M, N, K, 18);
+  if (rc != Q4_OK) return rc;
   if (!aligned(x, 4) || !aligned(y, 4) || !aligned(B, 2)) return Q4_EALIGN;
   return Q4_OK;
 }
 
 int check_gemv_q8(const float* x, const q8_0_block* B, const float* y, int M, int N, int K) {
-  if (!x || !B || !y || M <= 0 || N <= 0 || K <= 0) return Q4_EINVAL;
-  if (N % 32 != 0 || M > Q4_GEMV_MAX_M) return Q4_ESHAPE;
-  if ((long long)K * (N / 32) * 34 > kMaxBytes || (long long)M * K * 4 > kMaxBytes ||
-      (long long)M * N * 4 > kMaxBytes)
-    return Q4_ETOOBIG;
+  if (!x || !B || !y) return Q4_EINVAL;
+  const int rc = check_gemv_shape(M, N, K, 34);
+  if (rc != Q4_OK) return rc;
   if (!aligned(x, 4) || !aligned(y, 4) || !aligned(B, 2)) return Q4_EALIGN;
   return Q4_OK;
 }
@@ -122,7 +130,7 @@ const char* q4_strerror(int status) {
 }
 
 size_t q4_0_gemv_workspace_bytes(int M, int N, int K) {
-  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || M > Q4_GEMV_MAX_M) return 0;
+  if (check_gemv_shape(M, N, K, 18) != Q4_OK) return 0;
   return q4::plan_gemv(M, N, K).ws_bytes;
 }
 
@@ -138,7 +146,7 @@ int q4_0_gemv(const float* x, const q4_0_block* B, float* y, int M, int N, int K
 }
 
 size_t q8_0_gemv_workspace_bytes(int M, int N, int K) {
-  if (M <= 0 || N <= 0 || K <= 0 || N % 32 != 0 || M > Q4_GEMV_MAX_M) return 0;
+  if (check_gemv_shape(M, N, K, 34) != Q4_OK) return 0;
   return q4::plan_gemv_q8(M, N, K).ws_bytes;
 }
 

@@ -40,12 +40,25 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
+def build_sanitized(out: str) -> str:
+    """Compile the oracle with AddressSanitizer and UndefinedBehaviorSanitizer
+    (any finding aborts) into `out`. Load it with ORACLE_LIB=out in a Python
+    started with gcc's libasan preloaded."""
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fno-fast-math",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fPIC", "-shared",
+           "-o", out, _SRC]
+    subprocess.check_call(cmd)
+    return out
+
+
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    build()
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("ORACLE_LIB")  # a sanitized build (tests only)
+    if not path:
+        path = build()
+    lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32 = ctypes.c_int
     lib.oracle_fp16_to_double.restype = ctypes.c_double

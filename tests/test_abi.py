@@ -8,7 +8,9 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "q4moe.h")
-LIB = os.path.join(ROOT, "moe_experts_amd", "libq4moe.so")
+# ABI checks can run against another build of the library (the host-sanitizer
+# build of tests/test_sanitizers.py)
+LIB = os.environ.get("Q4MOE_ABI_LIB") or os.path.join(ROOT, "moe_experts_amd", "libq4moe.so")
 
 
 @pytest.fixture(scope="module")
@@ -270,3 +272,39 @@ def test_moe_prefill_rejects_bad_arguments(lib):
     assert f(*ok, 60000, 5120, 1536, 160, 8, None, 0, None) == -6  # down rows > 2 GiB
     assert ws(2048, 5120, 1536, 160, 6) > 2048 * 6 * (4 * 5120 + 2 * 1536)
     assert ws(64, 5120, 1504, 160, 6) == 0
+
+
+EXTREME = [-1, 0, 1, 3, 32, 33, 64, 96, 128, 4096, 5120, 11008, 65536, 1 << 20, (1 << 31) - 32,
+           (1 << 31) - 1]
+
+
+def test_sizing_functions_over_extreme_shapes(lib):
+    """Every workspace-size and layout function answers for any shape, from
+    negative to INT_MAX, without overflowing (run under UndefinedBehaviorSanitizer
+    by tests/test_sanitizers.py): unsupported shapes give 0 (or an error), and
+    a supported one a size that covers at least its largest array."""
+    import itertools
+    Z = ctypes.c_size_t
+    lib.q8_0_gemv_workspace_bytes.restype = Z
+    lib.q8_0_gemv_workspace_bytes.argtypes = [ctypes.c_int] * 3
+    lib.moe_q4_0_prefill_workspace_bytes.restype = Z
+    lib.moe_q4_0_prefill_workspace_bytes.argtypes = [ctypes.c_int] * 5
+    lib.moe_q4_0_route_layout.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(Z)] * 3
+    small = [-1, 0, 1, 2, 6, 8, 9, 64, 65, 160, 1024, 1025, 65536, 65537, (1 << 31) - 1]
+    for M, N, K in itertools.product([-1, 0, 1, 3, 8, 9, (1 << 31) - 1], EXTREME, EXTREME):
+        for f in (lib.q4_0_gemv_workspace_bytes, lib.q8_0_gemv_workspace_bytes):
+            ws = f(M, N, K)
+            if 1 <= M <= 8 and N > 0 and N % 32 == 0 and K > 0 and ws:
+                assert ws >= 4 * M * N  # at least two splits of [M][N] fp32, or 0 for one
+    a, b, c = Z(), Z(), Z()
+    for T, H, I in itertools.product(small, EXTREME, EXTREME):
+        for E, topk in ((160, 6), (1024, 8), (-1, 1), (1, 0)):
+            lib.moe_q4_0_workspace_bytes(T, H, I, E, topk)
+            lib.moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)
+            lib.moe_q4_0_layer_workspace_bytes(T, H, I, E, topk, 2)
+            lib.moe_router_workspace_bytes(T, H, E)
+            rc = lib.moe_q4_0_route_layout(T, H, I, E, topk, ctypes.byref(a), ctypes.byref(b),
+                                           ctypes.byref(c))
+            if rc == 0:
+                need = lib.moe_q4_0_workspace_bytes(T, H, I, E, topk)
+                assert a.value < b.value < c.value < need
