@@ -560,6 +560,52 @@ def bench_probes(torch, dev):
         res["stream"][name] = {"bytes": nbytes, "us": round(t * 1e6, 2),
                                "GBps": round(nbytes / t / 1e9, 1), "grid": grid}
         log(f"[probe] stream {name}: {res['stream'][name]}")
+    # The decode GEMV's access pattern: the same matrices read as split-K
+    # tiles, at the batch-1 plan's tile (16 blocks x Kt rows) and at small
+    # tiles (32 blocks x about 40 rows, about 1024 workgroups).
+    from moe_experts_amd import datagen, q4_0_gemv_workspace_bytes
+    res["tile"] = {}
+    for name, K, N, _seed in datagen.DENSE_7B_SHAPES:
+        if name == "ffn_up":
+            continue
+        pitch = N // 32 * 18
+        nbytes = K * pitch
+        stride = (nbytes + 4095) // 4096 * 4096
+        nreg = max(1, span // stride)
+        per = min(nreg, 64)
+        S = max(1, q4_0_gemv_workspace_bytes(1, N, K) // (4 * N))
+        for label, seg, kt in (("plan_m1", 288, -(-K // S)), ("small", 576, -(-K // max(1, 1024 // -(-pitch // 576))))):
+            def run(c, seg=seg, kt=kt):
+                for u in range(per):
+                    probe.tile_read(buf, ((c * per + u) % nreg) * stride, K, pitch, seg, kt, sink)
+            gs = [capture(torch, lambda c=c: run(c)) for c in range(max(1, min(4, nreg // per)))]
+            t, _ = time_graph_dist(torch, gs, 8, per)
+            grid = -(-pitch // seg) * -(-K // kt)
+            res["tile"][f"{name}_{label}"] = {"bytes": nbytes, "seg": seg, "kt": kt, "grid": grid,
+                                              "us": round(t * 1e6, 2),
+                                              "GBps": round(nbytes / t / 1e9, 1)}
+            log(f"[probe] tile {name} {label}: {res['tile'][f'{name}_{label}']}")
+    # A kernel boundary: empty kernels back to back, and a stream of the 4096 x
+    # 4096 matrix's bytes with and without an empty kernel after each read.
+    nb = PROBE_SIZES["gemv_4096x4096"]
+    stride = (nb + 4095) // 4096 * 4096
+    nreg = span // stride
+    g_empty = capture(torch, lambda: [probe.empty(sink) for _ in range(64)])
+    t_empty = time_graph(torch, [g_empty], 8, 64)
+    per = 64
+
+    def reads(c, with_empty):
+        for u in range(per):
+            probe.stream_read(buf, ((c * per + u) % nreg) * stride, nb, 1024, sink)
+            if with_empty:
+                probe.empty(sink)
+    t_plain = time_graph(torch, [capture(torch, lambda c=c: reads(c, False)) for c in range(2)], 8, per)
+    t_pair = time_graph(torch, [capture(torch, lambda c=c: reads(c, True)) for c in range(2)], 8, per)
+    res["kernel_boundary"] = {"empty_kernel_us": round(t_empty * 1e6, 2),
+                              "stream_9.47MB_us": round(t_plain * 1e6, 2),
+                              "stream_then_empty_us": round(t_pair * 1e6, 2),
+                              "added_by_empty_us": round((t_pair - t_plain) * 1e6, 2)}
+    log(f"[probe] kernel boundary: {res['kernel_boundary']}")
     del buf
     msink = torch.zeros(1024 * 256, dtype=torch.float32, device=dev)
     for kind, iters in (("f16", 4096), ("f32", 8192)):

@@ -32,6 +32,23 @@ extern "C" {
  * Errors: Q4_EINVAL (null pointer, bytes or grid out of range), Q4_EALIGN. */
 int q4_probe_stream(const void* src, size_t bytes, int grid, uint32_t* sink, void* stream);
 
+/* Read-only pass over a K x pitch-byte matrix in split-K tiles, the access
+ * pattern of the decode GEMV: tile (c, s) covers bytes [c*seg, c*seg + seg)
+ * of rows [s*kt, s*kt + kt) (the last column tile may be narrower), one
+ * workgroup of 256 lanes per tile, ceil(pitch/seg) * ceil(K/kt) workgroups.
+ * Lanes read the tile's 16-byte chunks in row-major order, 8 in flight per
+ * lane. sink as for q4_probe_stream (one word per workgroup).
+ *   src 16-byte aligned; pitch and seg multiples of 16; K * pitch < 2^31;
+ *   at most 65536 workgroups.
+ * Errors: Q4_EINVAL, Q4_ETOOBIG (matrix of 2 GiB or more), Q4_EALIGN. */
+int q4_probe_tile(const void* src, int K, int pitch, int seg, int kt, uint32_t* sink,
+                  void* stream);
+
+/* One workgroup of 64 lanes that does nothing: the fixed cost of a kernel
+ * boundary (for example between a GEMV and its split-K sum in a graph).
+ * Errors: Q4_EINVAL (null sink; nothing is written to it). */
+int q4_probe_empty(uint32_t* sink, void* stream);
+
 /* Matrix-unit loops: each of grid workgroups of 256 lanes (4 waves) issues
  * `iters` rounds of 8 independent MFMAs per wave, then writes one value per
  * lane to sink (sink must hold grid * 256 floats).

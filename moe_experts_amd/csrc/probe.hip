@@ -44,6 +44,44 @@ __global__ __launch_bounds__(kLanes) void probe_stream_kernel(const uint8_t* src
   if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
 }
 
+// Split-K tile (c, s) of a K x pitch-byte matrix: bytes [c*seg, c*seg + seg)
+// of rows [s*kt, s*kt + kt), read as 16-byte chunks in row-major order, chunk
+// q by lane q % 256 in round q / 256, kUnroll rounds in flight. The last
+// column tile may be narrower (chunks past the row read out of range).
+__global__ __launch_bounds__(kLanes) void probe_tile_kernel(const uint8_t* src, uint32_t bytes,
+                                                            int K, int pitch, int seg, int C,
+                                                            int kt, uint32_t* sink) {
+  const __amdgpu_buffer_rsrc_t r = rsrc(src, bytes);
+  const int c = blockIdx.x % C, s = blockIdx.x / C;
+  const int cps = seg / 16;
+  const int k0 = s * kt;
+  const int rows = min(kt, K - k0);
+  const int cw = min(seg, pitch - c * seg) / 16;  // chunks of this tile's row segment
+  const int n = rows * cps;
+  uint32_t acc = 0;
+  for (int i0 = threadIdx.x; i0 < n; i0 += kUnroll * kLanes) {
+    uint32_t v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int q = i0 + u * kLanes;
+      const int row = q / cps, ch = q - row * cps;
+      const uint32_t off = (q < n && ch < cw)
+                               ? (uint32_t)(k0 + row) * (uint32_t)pitch + (uint32_t)(c * seg + ch * 16)
+                               : kOut;
+      const auto w = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+      v[u] = w[0] ^ w[1] ^ w[2] ^ w[3];
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
+  }
+  if (acc == 0x9e3779b9u) sink[blockIdx.x] = acc;
+}
+
+// Does nothing (the store never happens for a launch of at most 65536 lanes).
+__global__ void probe_empty_kernel(uint32_t* sink) {
+  if (blockIdx.x * blockDim.x + threadIdx.x == 0xffffffffu) sink[0] = 1;
+}
+
 __global__ __launch_bounds__(kLanes) void probe_mfma_f16_kernel(int iters, float* sink) {
   v4f acc[8];
   v8h a, b;
@@ -93,6 +131,29 @@ int q4_probe_stream(const void* src, size_t bytes, int grid, uint32_t* sink, voi
   hipLaunchKernelGGL(probe_stream_kernel, dim3(grid), dim3(kLanes), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src),
                      (uint32_t)bytes, sink);
+  return launched();
+}
+
+int q4_probe_tile(const void* src, int K, int pitch, int seg, int kt, uint32_t* sink,
+                  void* stream) {
+  if (!src || !sink || K < 1 || pitch < 16 || pitch % 16 != 0 || seg < 16 || seg % 16 != 0 ||
+      kt < 1)
+    return Q4_EINVAL;
+  if ((long long)K * pitch >= (1ll << 31)) return Q4_ETOOBIG;
+  if (reinterpret_cast<uintptr_t>(src) % 16 != 0) return Q4_EALIGN;
+  const int C = (pitch + seg - 1) / seg;
+  const long long grid = (long long)C * ((K + kt - 1) / kt);
+  if (grid > 65536) return Q4_EINVAL;
+  hipLaunchKernelGGL(probe_tile_kernel, dim3((unsigned)grid), dim3(kLanes), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src),
+                     (uint32_t)((long long)K * pitch), K, pitch, seg, C, kt, sink);
+  return launched();
+}
+
+int q4_probe_empty(uint32_t* sink, void* stream) {
+  if (!sink) return Q4_EINVAL;
+  hipLaunchKernelGGL(probe_empty_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                     sink);
   return launched();
 }
 

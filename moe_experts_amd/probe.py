@@ -22,6 +22,10 @@ _lib.q4_probe_mfma_f16.restype = _I
 _lib.q4_probe_mfma_f16.argtypes = [_I, _I, _P, _P]
 _lib.q4_probe_mfma_f32.restype = _I
 _lib.q4_probe_mfma_f32.argtypes = [_I, _I, _P, _P]
+_lib.q4_probe_tile.restype = _I
+_lib.q4_probe_tile.argtypes = [_P, _I, _I, _I, _I, _P, _P]
+_lib.q4_probe_empty.restype = _I
+_lib.q4_probe_empty.argtypes = [_P, _P]
 
 
 def _stream(device) -> int:
@@ -42,6 +46,28 @@ def stream_read(buf: torch.Tensor, offset: int, nbytes: int, grid: int, sink: to
         raise ValueError("sink must be an int32 device tensor of at least grid words")
     _check(_lib.q4_probe_stream(buf.data_ptr() + offset, nbytes, grid, sink.data_ptr(),
                                 _stream(buf.device)), "q4_probe_stream")
+
+
+def tile_read(buf: torch.Tensor, offset: int, K: int, pitch: int, seg: int, kt: int,
+              sink: torch.Tensor) -> int:
+    """Read a K x pitch-byte matrix at byte offset (16-byte aligned) of the
+    uint8 device tensor buf in split-K tiles of seg bytes x kt rows; returns
+    the number of workgroups (sink: int32 device tensor of at least that)."""
+    grid = -(-pitch // seg) * -(-K // kt)
+    if buf.dtype != torch.uint8 or offset < 0 or offset + K * pitch > buf.numel():
+        raise ValueError("matrix outside the buffer")
+    if sink.dtype != torch.int32 or sink.numel() < grid or sink.device != buf.device:
+        raise ValueError("sink must be an int32 device tensor of at least one word per tile")
+    _check(_lib.q4_probe_tile(buf.data_ptr() + offset, K, pitch, seg, kt, sink.data_ptr(),
+                              _stream(buf.device)), "q4_probe_tile")
+    return grid
+
+
+def empty(sink: torch.Tensor):
+    """Launch the empty kernel (sink: any int32 device tensor, not written)."""
+    if sink.dtype != torch.int32 or sink.numel() < 1:
+        raise ValueError("sink must be an int32 device tensor")
+    _check(_lib.q4_probe_empty(sink.data_ptr(), _stream(sink.device)), "q4_probe_empty")
 
 
 def mfma_loop(kind: str, iters: int, grid: int, sink: torch.Tensor) -> int:

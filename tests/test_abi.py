@@ -72,7 +72,8 @@ def test_every_header_has_its_library():
         build.build()
     probe = ctypes.CDLL(PROBE_LIB)
     names = declared_functions(PROBE_HEADER)
-    assert names == ["q4_probe_mfma_f16", "q4_probe_mfma_f32", "q4_probe_stream"]
+    assert names == ["q4_probe_empty", "q4_probe_mfma_f16", "q4_probe_mfma_f32", "q4_probe_stream",
+                     "q4_probe_tile"]
     for n in names:
         assert hasattr(probe, n), f"{n} declared in q4probe.h but not exported"
 
@@ -92,6 +93,17 @@ def test_probes_reject_bad_arguments():
         assert f(0, 8, FAKE, None) == -1
         assert f(8, 0, FAKE, None) == -1
         assert f(8, 8, None, None) == -1
+    probe.q4_probe_tile.argtypes = [P, I, I, I, I, P, P]
+    probe.q4_probe_empty.argtypes = [P, P]
+    t = probe.q4_probe_tile
+    assert t(None, 4096, 2304, 288, 128, FAKE, None) == -1
+    assert t(FAKE, 4096, 2300, 288, 128, FAKE, None) == -1   # pitch not a multiple of 16
+    assert t(FAKE, 4096, 2304, 280, 128, FAKE, None) == -1   # tile width not a multiple of 16
+    assert t(FAKE, 4096, 2304, 288, 0, FAKE, None) == -1
+    assert t(FAKE, 4096, 2304, 16, 1, FAKE, None) == -1      # 589824 workgroups
+    assert t(FAKE, 1 << 20, 4096, 288, 128, FAKE, None) == -6  # 4 GiB matrix
+    assert t(FAKE + 2, 4096, 2304, 288, 128, FAKE, None) == -3
+    assert probe.q4_probe_empty(None, None) == -1
 
 
 def test_strerror(lib):
