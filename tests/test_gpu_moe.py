@@ -72,7 +72,8 @@ def test_moe_duplicates_out_of_range_and_crowded_expert():
 
 
 @pytest.mark.parametrize("T,H,I,E,topk", [(2, 64, 32, 5, 2), (17, 96, 64, 4, 6), (64, 64, 64, 3, 8),
-                                          (33, 512, 768, 12, 6), (40, 128, 96, 160, 6)])
+                                          (33, 512, 768, 12, 6), (40, 128, 96, 160, 6),
+                                          (64, 64, 64, 1024, 8)])  # every limit at once
 def test_moe_route_table_and_guards(T, H, I, E, topk):
     """The grouping step (pairs -> per-expert items) recomputed on the host from
     the ids matches the table the call left in its workspace; out and the

@@ -115,3 +115,24 @@ def test_prefill_dsv2_2048_tokens_every_expert():
                                     H, I, E)
     check_tol(got[toks], ref, bnd, TOL, f"dsv2 prefill T=2048, {len(toks)} tokens")
     assert np.isfinite(got).all()
+
+
+@pytest.mark.slow
+def test_prefill_at_the_token_limit():
+    """65536 tokens (Q4_MOE_PREFILL_MAX_T) x 8 slots (the topk limit): 524288
+    pairs in 1024 ranking passes and 4096 m-tiles; out between guard bands;
+    64 tokens spread over the batch checked against the oracle."""
+    from moe_experts_amd import moe_q4_0_prefill
+    T, H, I, E, topk = 65536, 128, 128, 8, 8
+    x16 = datagen.to_f16(datagen.activations(8101, T, H))
+    (Wg, Wu, Wd), dw = experts(8102, H, I, E)
+    ids, w, _ = datagen.routing(8103, T, E, topk)
+    ofull, out = guarded(T * H)
+    moe_q4_0_prefill(to_dev(x16), *dw, to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32)),
+                     I, E, out=out.view(T, H))
+    assert guards_intact(ofull, T * H), "write outside out"
+    got = to_host(out).reshape(T, H)
+    tok = np.linspace(0, T - 1, 64).astype(np.int64)
+    ref, bnd, _ = oracle.moe_decode(x16[tok].astype(np.float32), Wg, Wu, Wd, ids[tok], w[tok],
+                                    H, I, E)
+    check_tol(got[tok], ref, bnd, TOL, "65536 tokens x 8 slots")
