@@ -18,20 +18,32 @@ namespace {
 // SMAX > 0 (S <= SMAX) all SMAX loads are issued before the first add, so the
 // sum costs one memory round trip: split indices past S - 1 are clamped (the
 // repeated values are loaded but not added; adding +0.0 instead leaves the
-// sum bitwise unchanged, since a sum started at +0.0 is never -0.0). SMAX = 0
-// takes any S in groups of 8.
+// sum bitwise unchanged, since a sum started at +0.0 is never -0.0). The
+// partials are read once, with non-temporal loads. SMAX = 0 takes any S in
+// groups of 8. Workgroups of one wave spread the few outputs of a decode call
+// over more CUs (same-box A/B against 256 lanes: 0.2-0.3 us per call).
+constexpr int kReduceThreads = 64;
+constexpr int kNonTemporal = 2;  // buffer-load cache policy: nt
+
 template <int SMAX>
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restrict__ part,
-                                                          float* __restrict__ y, int MN, int S) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(kReduceThreads) void gemv_reduce_kernel(const float* __restrict__ part,
+                                                                     float* __restrict__ y,
+                                                                     int MN, int S) {
+  const int i = blockIdx.x * kReduceThreads + threadIdx.x;
   if (i >= MN) return;
   if constexpr (SMAX == 0) {
     y[i] = sum_strided(part + i, (size_t)MN, S);
   } else {
     __builtin_assume(S >= 1);
+    // S * MN floats of partials are below 2^30 (the plans keep tiles of at
+    // least 64 rows and the matrix below 2 GiB), so byte offsets fit 32 bits.
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(part, (uint32_t)((size_t)S * MN * 4u));
     float t[SMAX];
 #pragma unroll
-    for (int s = 0; s < SMAX; ++s) t[s] = part[(size_t)min(s, S - 1) * MN + i];
+    for (int s = 0; s < SMAX; ++s)
+      t[s] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           r, (uint32_t)(min(s, S - 1) * MN + i) * 4u, 0,
+                                           kNonTemporal));
     float v = 0.0f;
 #pragma unroll
     for (int s = 0; s < SMAX; ++s) v += s < S ? t[s] : 0.0f;
@@ -42,7 +54,7 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float* __restric
 }  // namespace
 
 hipError_t launch_gemv_reduce(const float* part, float* y, int MN, int S, hipStream_t st) {
-  const dim3 grid((MN + 255) / 256), block(256);
+  const dim3 grid((MN + kReduceThreads - 1) / kReduceThreads), block(kReduceThreads);
   if (S <= 8)
     hipLaunchKernelGGL(gemv_reduce_kernel<8>, grid, block, 0, st, part, y, MN, S);
   else if (S <= 16)
