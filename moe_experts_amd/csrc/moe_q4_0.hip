@@ -384,10 +384,14 @@ __global__ __launch_bounds__(kThreads) void moe_expert_mixed_kernel(ExpertArgs a
 // ---------------------------------------------------------------------------
 // 3. h = SiLU(gate) * up from the split-K partials (split order)
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void moe_act_kernel(const float* __restrict__ part,
-                                                      float* __restrict__ h, int npairs, int I,
-                                                      int S) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+// One-wave workgroups and non-temporal loads of the partials (read once), as
+// in the decode GEMV's split-K sum; the combine below does the same.
+constexpr int kSumThreads = 64;
+
+__global__ __launch_bounds__(kSumThreads) void moe_act_kernel(const float* __restrict__ part,
+                                                              float* __restrict__ h, int npairs,
+                                                              int I, int S) {
+  const size_t idx = (size_t)blockIdx.x * kSumThreads + threadIdx.x;
   if (idx >= (size_t)npairs * I) return;
   // Pairs with an invalid expert id have no partial sums; their h is never
   // read, so they are not filtered here (no dependent id load).
@@ -399,8 +403,8 @@ __global__ __launch_bounds__(256) void moe_act_kernel(const float* __restrict__ 
 #pragma unroll
     for (int k = 0; k < kSplitLoads; ++k) {
       const size_t sk = (size_t)min(k, S - 1);
-      tg[k] = part[sk * slab + idx];
-      tu[k] = part[((size_t)S + sk) * slab + idx];
+      tg[k] = __builtin_nontemporal_load(part + sk * slab + idx);
+      tu[k] = __builtin_nontemporal_load(part + ((size_t)S + sk) * slab + idx);
     }
     g = 0.0f;
     u = 0.0f;
@@ -420,12 +424,10 @@ __global__ __launch_bounds__(256) void moe_act_kernel(const float* __restrict__ 
 // ---------------------------------------------------------------------------
 // 5. combine: slot order 0..topk-1, split order inside each slot
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ part,
-                                                          const int32_t* __restrict__ ids,
-                                                          const float* __restrict__ w,
-                                                          float* __restrict__ out, int T, int H,
-                                                          int E, int topk, int S) {
-  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+__global__ __launch_bounds__(kSumThreads) void moe_combine_kernel(
+    const float* __restrict__ part, const int32_t* __restrict__ ids, const float* __restrict__ w,
+    float* __restrict__ out, int T, int H, int E, int topk, int S) {
+  const size_t idx = (size_t)blockIdx.x * kSumThreads + threadIdx.x;
   if (idx >= (size_t)T * H) return;
   const int t = (int)(idx / H);
   const int n = (int)(idx - (size_t)t * H);
@@ -443,7 +445,8 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
       wv[sl] = w[p];
 #pragma unroll
       for (int k = 0; k < kCombineSplits; ++k)
-        pv[sl][k] = part[(size_t)min(k, S - 1) * slab + (size_t)p * H + n];
+        pv[sl][k] =
+            __builtin_nontemporal_load(part + (size_t)min(k, S - 1) * slab + (size_t)p * H + n);
     }
 #pragma unroll
     for (int sl = 0; sl < Q4_MOE_MAX_TOPK; ++sl) {
@@ -632,7 +635,8 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   const bool fuse_act = p.MC == 1 && staged_dn && p.gu_S <= kActMaxSplits &&
                         tile_rows_padded(p.dn_Kt, kP, kStagedRB) <= kActMaxVals * kThreads;
   if (!fuse_act) {
-    hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + kSumThreads - 1) / kSumThreads)),
+                       dim3(kSumThreads), 0, st,
                        gu_part, h, npairs, p.I, p.gu_S);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -664,7 +668,8 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, st,
+  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + kSumThreads - 1) / kSumThreads)),
+                     dim3(kSumThreads), 0, st,
                      dn_part, ids, w, out, p.T, p.H, p.E, p.topk, p.dn_S);
   return hipGetLastError();
 }
