@@ -220,7 +220,7 @@ int moe_q4_0_route_layout(int T, int H, int I, int E, int topk, size_t* items_of
  *   1 <= T <= Q4_MOE_PREFILL_MAX_T, 1 <= topk <= Q4_MOE_MAX_TOPK,
  *   1 <= E <= Q4_MOE_MAX_E, H % 128 == 0, I % 128 == 0.
  * Pairs are sorted by expert on the device (stable); each expert's rows go
- * through 128-row tiles. Each dequantized weight and h = SiLU(g) * u are
+ * through Q4_MOE_PREFILL_TILE_ROWS-row tiles. Each dequantized weight and h = SiLU(g) * u are
  * rounded to fp16 before their products; sums are fp32. Ids outside [0, E)
  * contribute zero; slots are summed in order 0..topk-1.
  *   ws/ws_bytes: workspace of moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)
@@ -231,6 +231,31 @@ int moe_q4_0_prefill(const uint16_t* x16, const q4_0_block* Wg, const q4_0_block
                      const q4_0_block* Wd, const int32_t* topk_ids, const float* topk_w,
                      float* out, int T, int H, int I, int E, int topk, void* ws,
                      size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Where moe_q4_0_prefill leaves its routing, a stable sort of the (token,
+ * slot) pairs by expert, in its workspace (the expert grouping that the
+ * KTransformers tutorial's "Optimization 3" schedules by; here it orders the
+ * GEMM rows). Meant for tests and debugging: after a call on the same
+ * (T, H, I, E, topk), the workspace holds
+ *   counts  int32[2] at *counts_off: the number of m-tiles and of valid pairs
+ *           (sorted rows);
+ *   src     int32[counts[1]] at *src_off: the token t of sorted row q;
+ *   pos     int32[T * topk] at *pos_off: the sorted row of pair
+ *           p = t * topk + slot, -1 for an id outside [0, E);
+ *   tiles   int32[counts[0]][4] at *tiles_off: (expert, first sorted row,
+ *           rows, 0); each expert's rows cut into Q4_MOE_PREFILL_TILE_ROWS-row
+ *           tiles (the last one shorter), in increasing expert order.
+ * Sorted rows run over the experts in increasing id and, within an expert,
+ * over its pairs in increasing p. The offsets are byte offsets into ws; the
+ * data lives there until the next call that uses the workspace. Returns Q4_OK,
+ * or the status moe_q4_0_prefill would return for the shape; outputs untouched
+ * on error.
+ * ------------------------------------------------------------------------- */
+#define Q4_MOE_PREFILL_TILE_ROWS 96   /* rows of one expert m-tile */
+
+int moe_q4_0_prefill_route_layout(int T, int H, int I, int E, int topk, size_t* src_off,
+                                  size_t* pos_off, size_t* tiles_off, size_t* counts_off);
 
 /* ---------------------------------------------------------------------------
  * MoE router: the gate in front of moe_q4_0_decode, on the device. The

@@ -12,7 +12,7 @@ _EXPORTS = ("q4_0_gemv", "q8_0_gemv", "q8_0_gemv_workspace_bytes", "q4_0_gemm", 
             "moe_q4_0_prefill_workspace_bytes", "moe_router_topk", "moe_q4_0_layer",
             "q4_0_gemv_workspace_bytes", "moe_q4_0_workspace_bytes",
             "moe_router_workspace_bytes", "moe_q4_0_layer_workspace_bytes", "q4_strerror",
-            "moe_q4_0_route_layout", "q4_0_gemv_noalloc", "GEMV_NOALLOC_MAX_WS",
+            "moe_q4_0_route_layout", "moe_q4_0_prefill_route_layout", "q4_0_gemv_noalloc", "GEMV_NOALLOC_MAX_WS",
             "Q4Error")
 
 

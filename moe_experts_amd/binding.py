@@ -66,6 +66,9 @@ _lib.moe_q4_0_route_layout.restype = _I
 _lib.moe_q4_0_route_layout.argtypes = [_I, _I, _I, _I, _I, ctypes.POINTER(_Z), ctypes.POINTER(_Z),
                                        ctypes.POINTER(_Z)]
 
+_lib.moe_q4_0_prefill_route_layout.restype = _I
+_lib.moe_q4_0_prefill_route_layout.argtypes = [_I, _I, _I, _I, _I] + [ctypes.POINTER(_Z)] * 4
+
 BLOCK_BYTES = 18
 Q8_BLOCK_BYTES = 34
 
@@ -245,6 +248,14 @@ def moe_q4_0_route_layout(T: int, H: int, I: int, E: int, topk: int):
     _check(_lib.moe_q4_0_route_layout(T, H, I, E, topk, ctypes.byref(a), ctypes.byref(b),
                                       ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def moe_q4_0_prefill_route_layout(T: int, H: int, I: int, E: int, topk: int):
+    """Byte offsets (src, pos, tiles, counts) of the routing that
+    moe_q4_0_prefill leaves in its workspace."""
+    o = [_Z() for _ in range(4)]
+    _check(_lib.moe_q4_0_prefill_route_layout(T, H, I, E, topk, *[ctypes.byref(v) for v in o]))
+    return tuple(v.value for v in o)
 
 
 def moe_router_workspace_bytes(T: int, H: int, E: int) -> int:

@@ -211,8 +211,9 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_q4_0_generic_kernel(GemmArg
 // Aligned-shape kernel
 // ---------------------------------------------------------------------------
 namespace fast {
-// Tile heights: 256 rows for a plain GEMM, 128 for expert-grouped m-tiles
-// (a prefill expert has tens to hundreds of rows).
+// Tile heights: 256 rows for a plain GEMM, 96 for expert-grouped m-tiles
+// (a prefill expert has tens to hundreds of rows: about 77 for DeepSeek-V2
+// at 2048 tokens, which fill a 96-row tile 80 % and a 128-row tile 60 %).
 constexpr int kDenseBM = 256, kGroupedBM = kGemmRows;
 constexpr int BN = 128, BK = 64;
 constexpr int kXStages = 3, kRStages = 4;
@@ -239,7 +240,7 @@ struct XCfg {
   static constexpr int kMatBytes = kRStages * kRBytes + 2 * kBBytes;
   static constexpr int kLdsBytes = kXStages * kXBytes + NM * kMatBytes;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
-  static_assert(BM % 128 == 0, "4 consumer waves of 32-row multiples");
+  static_assert(BM % 32 == 0 && kXChunks % kGemmThreads == 0, "32-row bands, whole copy passes");
 };
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -447,7 +448,7 @@ struct Producer {
 // dequant (VALU) runs on the same SIMDs while the matrix cores run the MFMAs.
 template <int BM, int NM>
 __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
-  static_assert(NM == 1 || (NM == 2 && BM == 128), "gate and up together in 128-row tiles");
+  static_assert(NM == 1 || (NM == 2 && BM != 256), "gate and up together in grouped tiles");
   constexpr int kGroup = XCfg<BM, NM>::kGroup;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   int m0, rows, tn;
@@ -516,10 +517,11 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   const int lane = threadIdx.x & 63;
   // Consumer wave tiles: 256-row tiles give each wave 64 rows x all 128
   // columns; 128-row tiles a 2 x 2 grid of 64 x 64 (each wave then reads half
-  // the B tile instead of all of it: 64 instead of 80 KB of LDS reads per step).
-  constexpr int WGR = BM == 256 ? 4 : 2;  // waves along the rows
-  constexpr int WR = BM / WGR;            // rows per wave (64)
-  constexpr int WC = BN / (4 / WGR);      // columns per wave (128 or 64)
+  // the B tile instead of all of it: 64 instead of 80 KB of LDS reads per step);
+  // 96-row tiles give each wave all 96 rows x 32 columns.
+  constexpr int WGR = BM == 256 ? 4 : (BM == 128 ? 2 : 1);  // waves along the rows
+  constexpr int WR = BM / WGR;            // rows per wave (64 or 96)
+  constexpr int WC = BN / (4 / WGR);      // columns per wave (128, 64 or 32)
   constexpr int MI = WR / 32, NJ = WC / 32;
   const int wm = wave % WGR;
   const int wn = wave / WGR;

@@ -8,10 +8,10 @@
 // the two: the decode path's expert grouping with the prefill GEMM's tiles.
 //
 //   1. moe_prefill_route_kernel (one workgroup): a stable counting sort of
-//      the (token, slot) pairs by expert. Sorted row q holds pair perm[q]; the
+//      the (token, slot) pairs by expert, each wave over its own run of pairs. Sorted row q holds pair perm[q]; the
 //      kernel writes, per sorted row, the token it reads (src[q]), per pair its
 //      sorted row (pos[p], -1 for an id outside [0, E)), and the list of
-//      128-row m-tiles (expert, first row, rows) of every expert's rows.
+//      96-row m-tiles (expert, first row, rows) of every expert's rows.
 //   2. gate and up together: the prefill GEMM kernel in its grouped mode
 //      with two matrices (X rows gathered by src, the expert's gate and up
 //      Q4_0 matrices against the same X tile); its epilogue writes
@@ -30,8 +30,7 @@ namespace q4 {
 namespace {
 
 constexpr int kRouteThreads = 1024;
-constexpr int kChunk = 512;                      // pairs ranked per pass (8 waves)
-constexpr int kChunkWaves = kChunk / kWaveSize;
+constexpr int kRouteWaves = kRouteThreads / kWaveSize;
 static_assert(Q4_MOE_MAX_E <= kRouteThreads, "one lane per expert");
 
 struct PrefillRoute {
@@ -43,32 +42,54 @@ struct PrefillRoute {
   int* counts;    // [2]: m-tiles, valid rows
 };
 
+// LDS of the route kernel: per-wave counts (later bases) [waves][E], then one
+// int per wave for the scans.
+size_t route_lds_bytes(int E) { return ((size_t)kRouteWaves * E + kRouteWaves) * sizeof(int); }
+
+// Wave w owns a contiguous run of 64-pair groups and walks it twice, in pair
+// order. Pass 1 counts its pairs per expert (lanes with the same id find each
+// other with one ballot per id bit; the lowest such lane adds their number).
+// Between the passes, lane e sums expert e's counts, the workgroup scans them
+// into each expert's first sorted row and its m-tiles, and lane e turns its
+// per-wave counts into per-wave first rows (waves in order). Pass 2 gives each
+// pair its sorted row: its wave's current row for the expert plus its rank
+// among the group's lanes with that id; the group's lowest such lane then
+// moves the row on. Pair order is kept within every expert (a stable sort),
+// with two workgroup barriers around the scan instead of barriers per group.
 __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(PrefillRoute a) {
-  __shared__ int s_cnt[Q4_MOE_MAX_E];
-  __shared__ int s_base[Q4_MOE_MAX_E];
-  __shared__ int s_wcnt[kChunkWaves][Q4_MOE_MAX_E];
-  __shared__ int s_wsum[kRouteThreads / kWaveSize];
+  extern __shared__ int route_lds[];
+  int* s_wc = route_lds;                         // [kRouteWaves][E]
+  int* s_wsum = route_lds + kRouteWaves * a.E;   // [kRouteWaves]
   const int t = threadIdx.x;
   const int lane = t & (kWaveSize - 1);
   const int wave = t / kWaveSize;
+  const uint64_t below = (1ull << lane) - 1;
+  const int groups = (a.npairs + kWaveSize - 1) / kWaveSize;
+  const int per_wave = (groups + kRouteWaves - 1) / kRouteWaves;
+  const int g0 = wave * per_wave;
+  const int g1 = min(groups, g0 + per_wave);
+  int* wc = s_wc + wave * a.E;  // this wave's row: only this wave touches it in the passes
+  for (int e = lane; e < a.E; e += kWaveSize) wc[e] = 0;
 
-  s_cnt[t] = 0;
-  __syncthreads();
-  // counts per expert; four ids per lane in flight at a time
-  for (int p0 = t; p0 < a.npairs; p0 += 4 * kRouteThreads) {
-    int ev[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = p0 + u * kRouteThreads;
-      ev[u] = p < a.npairs ? a.ids[p] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (ev[u] >= 0 && ev[u] < a.E) atomicAdd(&s_cnt[ev[u]], 1);
+  auto load_id = [&](int g) {
+    const int p = g * kWaveSize + lane;
+    return (g < g1 && p < a.npairs) ? a.ids[p] : -1;
+  };
+  // pass 1: counts per expert, the next group's id loaded ahead
+  int e_next = load_id(g0);
+  for (int g = g0; g < g1; ++g) {
+    const int e = e_next;
+    e_next = load_id(g + 1);
+    const bool valid = e >= 0 && e < a.E;
+    const uint64_t same = same_id_lanes(e, valid);
+    if (valid && (same & below) == 0) wc[e] += __popcll(same);
   }
   __syncthreads();
-  // expert t: its first sorted row and its m-tiles of 128 rows (kGemmRows)
-  const int cnt = t < a.E ? s_cnt[t] : 0;
+
+  // expert t: total rows, first sorted row, m-tiles of kGemmRows rows
+  int cnt = 0;
+  if (t < a.E)
+    for (int w = 0; w < kRouteWaves; ++w) cnt += s_wc[w * a.E + t];
   const int nt = (cnt + kGemmRows - 1) / kGemmRows;
   const int off = block_inclusive_scan(cnt, s_wsum) - cnt;
   const int toff = block_inclusive_scan(nt, s_wsum) - nt;
@@ -78,44 +99,32 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
     a.counts[0] = toff + nt;
     a.counts[1] = off + cnt;
   }
-  s_base[t] = off;
+  if (t < a.E) {
+    int row = off;
+    for (int w = 0; w < kRouteWaves; ++w) {
+      const int c = s_wc[w * a.E + t];
+      s_wc[w * a.E + t] = row;
+      row += c;
+    }
+  }
   __syncthreads();
 
-  // Stable ranks, kChunk pairs at a time: within a wave by an exact-id ballot
-  // match, across the chunk's waves by per-wave counts, across chunks by a
-  // running base per expert. Each pass loads the next pass's id up front.
-  const uint64_t below = (1ull << lane) - 1;
-  int e_next = (t < kChunk && t < a.npairs) ? a.ids[t] : -1;
-  for (int c0 = 0; c0 < a.npairs; c0 += kChunk) {
-    const int p = c0 + t;
-    const bool mine = t < kChunk && p < a.npairs;
-    const int e = mine ? e_next : -1;
-    e_next = (t < kChunk && p + kChunk < a.npairs) ? a.ids[p + kChunk] : -1;
-    for (int i = t; i < kChunkWaves * a.E; i += kRouteThreads) {
-      const int w = i / a.E;
-      s_wcnt[w][i - w * a.E] = 0;
-    }
-    __syncthreads();
+  // pass 2: sorted rows
+  e_next = load_id(g0);
+  for (int g = g0; g < g1; ++g) {
+    const int e = e_next;
+    e_next = load_id(g + 1);
+    const int p = g * kWaveSize + lane;
     const bool valid = e >= 0 && e < a.E;
     const uint64_t same = same_id_lanes(e, valid);
-    if (valid && (same & below) == 0) s_wcnt[wave][e] = __popcll(same);
-    __syncthreads();
-    if (mine) {
-      int q = -1;
-      if (valid) {
-        q = s_base[e] + __popcll(same & below);
-        for (int w = 0; w < wave; ++w) q += s_wcnt[w][e];
-        a.src[q] = p / a.topk;
-      }
-      a.pos[p] = q;
+    int q = -1;
+    if (valid) {
+      const int row = wc[e];  // read by every lane of the id before its lowest lane moves it
+      q = row + __popcll(same & below);
+      if ((same & below) == 0) wc[e] = row + __popcll(same);
+      a.src[q] = p / a.topk;
     }
-    __syncthreads();
-    if (t < a.E) {
-      int add = 0;
-      for (int w = 0; w < kChunkWaves; ++w) add += s_wcnt[w][t];
-      s_base[t] += add;
-    }
-    __syncthreads();
+    if (p < a.npairs) a.pos[p] = q;
   }
 }
 
@@ -196,7 +205,8 @@ hipError_t launch_moe_prefill(const uint16_t* x16, const uint8_t* Wg, const uint
   const size_t mat = (size_t)H * (I / kBlockWeights) * kBlockBytes;
 
   PrefillRoute r{ids, npairs, E, topk, src, pos, tiles, counts};
-  hipLaunchKernelGGL(moe_prefill_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, r);
+  hipLaunchKernelGGL(moe_prefill_route_kernel, dim3(1), dim3(kRouteThreads), route_lds_bytes(E),
+                     st, r);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   err = launch_gemm_grouped(x16, T, Wg, Wu, mat, nullptr, h, I, H, tiles, counts, p.max_tiles,

@@ -72,7 +72,7 @@ hipError_t launch_gemm(const uint16_t* X, const uint8_t* B, float* Y, int M, int
 // With B1 (a second set of matrices of the same shape) the workgroup
 // contracts the same X tile with both and writes H = fp16(SiLU(X.B) * (X.B1))
 // instead of Y.
-constexpr int kGemmRows = 128;  // rows of one grouped m-tile
+constexpr int kGemmRows = Q4_MOE_PREFILL_TILE_ROWS;  // rows of one grouped m-tile
 bool gemm_grouped_supported(int N, int K);
 hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, const uint8_t* B1,
                                size_t mat_bytes, float* Y, _Float16* H, int N, int K,

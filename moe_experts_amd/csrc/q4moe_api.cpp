@@ -274,6 +274,19 @@ int moe_q4_0_layer(const float* x, const float* Wr, const q4_0_block* Wg, const 
                                  base + l.off_moe, p, st));
 }
 
+int moe_q4_0_prefill_route_layout(int T, int H, int I, int E, int topk, size_t* src_off,
+                                  size_t* pos_off, size_t* tiles_off, size_t* counts_off) {
+  if (!src_off || !pos_off || !tiles_off || !counts_off) return Q4_EINVAL;
+  const int rc = check_prefill_shape(T, H, I, E, topk);
+  if (rc != Q4_OK) return rc;
+  const q4::MoePrefillPlan p = q4::plan_moe_prefill(T, H, I, E, topk);
+  *src_off = p.off_src;
+  *pos_off = p.off_pos;
+  *tiles_off = p.off_tiles;
+  *counts_off = p.off_counts;
+  return Q4_OK;
+}
+
 size_t moe_q4_0_prefill_workspace_bytes(int T, int H, int I, int E, int topk) {
   if (check_prefill_shape(T, H, I, E, topk) != Q4_OK) return 0;
   return q4::plan_moe_prefill(T, H, I, E, topk).ws_bytes;

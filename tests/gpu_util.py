@@ -91,3 +91,41 @@ def check_route_table(ws: np.ndarray, ids: np.ndarray, T: int, H: int, I: int, E
     valid = int(((flat >= 0) & (flat < E)).sum())
     assert sum(len(p) for _, p in exp_v + exp_m) == valid
     return exp_v, exp_m
+
+
+def prefill_tile_rows() -> int:
+    """Q4_MOE_PREFILL_TILE_ROWS from the C header."""
+    import os
+    import re
+    hdr = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include",
+                       "q4moe.h")
+    m = re.search(r"#define\s+Q4_MOE_PREFILL_TILE_ROWS\s+(\d+)", open(hdr).read())
+    return int(m.group(1))
+
+
+def check_prefill_route(ws: np.ndarray, ids: np.ndarray, T: int, H: int, I: int, E: int):
+    """Rebuild the stable sort of the (token, slot) pairs by expert that
+    moe_q4_0_prefill leaves in its workspace (layout: include/q4moe.h,
+    moe_q4_0_prefill_route_layout) with numpy's stable argsort, and compare the
+    sorted rows' tokens, every pair's row, the m-tile list and the counters
+    entry by entry."""
+    from moe_experts_amd import moe_q4_0_prefill_route_layout
+    topk = ids.shape[1]
+    so, po, to, co = moe_q4_0_prefill_route_layout(T, H, I, E, topk)
+    i4 = lambda off, n: np.frombuffer(ws[off:off + 4 * n].tobytes(), dtype="<i4")
+    flat = ids.reshape(-1).astype(np.int64)
+    vp = np.nonzero((flat >= 0) & (flat < E))[0]
+    order = vp[np.argsort(flat[vp], kind="stable")]  # pair of each sorted row
+    rows = np.bincount(flat[vp], minlength=E)
+    R = prefill_tile_rows()
+    tiles, first = [], 0
+    for e in range(E):
+        tiles += [(e, first + i, min(R, int(rows[e]) - i), 0) for i in range(0, int(rows[e]), R)]
+        first += int(rows[e])
+    ntiles, nrows = i4(co, 2)
+    assert (int(ntiles), int(nrows)) == (len(tiles), order.size), "counters"
+    pos = np.full(flat.size, -1, dtype=np.int64)
+    pos[order] = np.arange(order.size)
+    assert (i4(po, flat.size) == pos).all(), "sorted row of each pair"
+    assert (i4(so, order.size) == order // topk).all(), "token of each sorted row"
+    assert (i4(to, 4 * len(tiles)).reshape(-1, 4) == np.array(tiles).reshape(-1, 4)).all(), "tiles"

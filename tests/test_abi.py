@@ -215,6 +215,25 @@ def test_route_layout(lib):
                                      ctypes.byref(c)) == -1
 
 
+def test_prefill_route_layout(lib):
+    Z = ctypes.c_size_t
+    lib.moe_q4_0_prefill_route_layout.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(Z)] * 4
+    lib.moe_q4_0_prefill_workspace_bytes.restype = Z
+    T, H, I, E, topk = 2048, 5120, 1536, 160, 6
+    o = [Z() for _ in range(4)]
+    refs = [ctypes.byref(v) for v in o]
+    assert lib.moe_q4_0_prefill_route_layout(T, H, I, E, topk, *refs) == 0
+    src, pos, tiles, counts = (v.value for v in o)
+    need = lib.moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)
+    # src, pos, the tile list and the counters are disjoint, in order, inside the workspace
+    assert src < pos < tiles < counts and counts + 8 <= need
+    assert pos - src >= T * topk * 4 and tiles - pos >= T * topk * 4
+    assert counts - tiles >= 16 * (T * topk // 128 + E)
+    assert lib.moe_q4_0_prefill_route_layout(T, H + 1, I, E, topk, *refs) == -2
+    assert lib.moe_q4_0_prefill_route_layout(T, H, I, E, topk, None, *refs[1:]) == -1
+    assert lib.moe_q4_0_prefill_route_layout(T, H, I, E, topk, *refs[:3], None) == -1
+
+
 def test_router_rejects_bad_arguments(lib):
     f = lib.moe_router_topk
     ok = (FAKE, FAKE, FAKE, FAKE, FAKE)

@@ -5,10 +5,12 @@ every product and sum in double. Tolerance: the prefill GEMM's relative bound,
 and h are rounded to fp16 on the GPU)."""
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from moe_experts_amd import datagen
-from tests.gpu_util import check_tol, guarded, guards_intact, to_dev, to_host
+from tests.gpu_util import (check_prefill_route, check_tol, guarded, guarded_ws, guards_intact,
+                            to_dev, to_host, ws_guards_intact)
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
@@ -27,9 +29,8 @@ def experts(seed, H, I, E):
     return (Wg, Wu, Wd), (to_dev(Wg), to_dev(Wu), to_dev(Wd))
 
 
-# one token; several tokens per expert; more than one 512-pair ranking pass
-# and several 128-row tiles per expert; every slot on one expert (duplicates,
-# 3 tiles of one expert); wide I
+# one token; several tokens per expert; several m-tiles per expert; every slot
+# on one expert (duplicates, 6 tiles of one expert); wide I
 @pytest.mark.parametrize("T,H,I,E,topk", [(1, 128, 128, 3, 1), (300, 256, 128, 6, 2),
                                           (513, 384, 256, 9, 6), (70, 128, 384, 1, 8),
                                           (40, 256, 640, 20, 4)])
@@ -117,20 +118,53 @@ def test_prefill_dsv2_2048_tokens_every_expert():
     assert np.isfinite(got).all()
 
 
+# The routing the call leaves in its workspace, rebuilt on the host: one group
+# of 64 pairs; several groups per wave; waves with no pairs; invalid ids; one
+# expert taking every pair; the benchmarked 2048-token routing.
+@pytest.mark.parametrize("T,E,topk,seed,bad", [(1, 3, 1, 1, False), (33, 4, 3, 6, True),
+                                               (513, 9, 6, 11, True), (70, 1, 8, 2, False),
+                                               (2048, 160, 6, 5301, False),
+                                               (5000, 1024, 8, 12, True)])
+def test_prefill_route_table(T, E, topk, seed, bad):
+    from moe_experts_amd import moe_q4_0_prefill, moe_q4_0_prefill_workspace_bytes
+    H, I = 128, 128
+    if E > 1:
+        ids, w, _ = datagen.routing(seed, T, E, topk)
+    else:
+        ids = np.zeros((T, topk), dtype=np.int32)
+        w = np.ones((T, topk), dtype=np.float32)
+    if bad:
+        g = np.random.Generator(np.random.PCG64(seed))
+        ids[g.random(ids.shape) < 0.05] = -1
+        ids[g.random(ids.shape) < 0.05] = E + 3
+    x16 = datagen.to_f16(datagen.activations(seed + 1, T, H))
+    _, dw = experts(seed + 2, H, I, E)
+    need = moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk)
+    wsfull, ws = guarded_ws(need)
+    moe_q4_0_prefill(to_dev(x16), *dw, to_dev(ids.astype(np.int32)), to_dev(w), I, E, ws=ws)
+    assert ws_guards_intact(wsfull, need), "write outside the workspace"
+    check_prefill_route(to_host(ws), ids, T, H, I, E)
+
+
 @pytest.mark.slow
 def test_prefill_at_the_token_limit():
     """65536 tokens (Q4_MOE_PREFILL_MAX_T) x 8 slots (the topk limit): 524288
-    pairs in 1024 ranking passes and 4096 m-tiles; out between guard bands;
-    64 tokens spread over the batch checked against the oracle."""
+    pairs, 512 groups of 64 per ranking wave, about 5500 m-tiles; out between guard
+    bands; the routing rebuilt on the host; 64 tokens spread over the batch
+    checked against the oracle."""
     from moe_experts_amd import moe_q4_0_prefill
     T, H, I, E, topk = 65536, 128, 128, 8, 8
     x16 = datagen.to_f16(datagen.activations(8101, T, H))
     (Wg, Wu, Wd), dw = experts(8102, H, I, E)
     ids, w, _ = datagen.routing(8103, T, E, topk)
     ofull, out = guarded(T * H)
+    from moe_experts_amd import moe_q4_0_prefill_workspace_bytes
+    ws = torch.empty(moe_q4_0_prefill_workspace_bytes(T, H, I, E, topk), dtype=torch.uint8,
+                     device=out.device)
     moe_q4_0_prefill(to_dev(x16), *dw, to_dev(ids.astype(np.int32)), to_dev(w.astype(np.float32)),
-                     I, E, out=out.view(T, H))
+                     I, E, out=out.view(T, H), ws=ws)
     assert guards_intact(ofull, T * H), "write outside out"
+    check_prefill_route(to_host(ws), ids, T, H, I, E)
     got = to_host(out).reshape(T, H)
     tok = np.linspace(0, T - 1, 64).astype(np.int64)
     ref, bnd, _ = oracle.moe_decode(x16[tok].astype(np.float32), Wg, Wu, Wd, ids[tok], w[tok],
