@@ -6,13 +6,14 @@
 //
 // Arithmetic used on the GPU for one block and one activation value a:
 //   s       = a * d                      (one fp32 multiply per block and row)
-//   acc[2i]   += s * lo_i                (lo_i = q & 0x0F converted exactly)
-//   acc[2i+1] += s * (16 * hi_i)         (the byte masked with 0xF0 converted
-//                                         exactly; the factor 16 is removed at
-//                                         the end, which is exact in binary32)
+//   acc[2i]   += s * lo_i                (lo_i = q & 0x0F, exact)
+//   acc[2i+1] += s * (16 * hi_i)         (the byte masked with 0xF0, exact; the
+//                                         factor 16 is removed at the end,
+//                                         which is exact in binary32)
 //   corr      += s
-//   result    = acc - 8 * corr           (so each weight costs one convert and
-//                                         one FMA per activation row)
+//   result    = acc - 8 * corr           (so each weight costs one FMA per
+//                                         activation row, plus its share of a
+//                                         few bit operations: fma_part)
 // Scaling by 16 commutes with every rounding step (no overflow or underflow for
 // finite inputs of the decode workloads), so the odd-column accumulators equal
 // 16x the plain accumulation bit for bit.
@@ -66,11 +67,19 @@ __device__ __forceinline__ void load_part(const uint8_t* __restrict__ p, int par
 // Accumulate one block share for M activation rows.
 //   xv[m] : activation of row m at this k (0 for rows past the end)
 //   acc[m][c] : c indexes the lane's 32/LPB columns
+// Even columns accumulate s * q, odd ones s * 16q (the high nibble left in
+// place), with s = x * d; corr sums s. The nibbles are not converted one by
+// one: a masked field q (or 16q) in the low bits of a 16-bit half is the
+// binary16 subnormal q * 2^-24, which v_fma_mix_f32 takes as an fp16 operand
+// and widens exactly. With s' = s * 2^24 (exact), s' * (q * 2^-24) is the same
+// real number as s * q, so every FMA rounds exactly as fma(s, q, acc) would.
+// Unpacking costs five bit operations per dword (eight weights) instead of
+// two masks and eight byte conversions.
 template <int M, int LPB>
 __device__ __forceinline__ void fma_part(const float (&xv)[M], const BlockPart<LPB>& b,
                                          float (&acc)[M][32 / LPB], float (&corr)[M]) {
   const float d = half_bits_to_float(b.d);
-  float s[M];
+  float s[M], sw[M];
   {
     // corr must sum exactly the rounded s that the FMAs below use, so that
     // acc - 8 * corr cancels exactly when every nibble is 8: no contraction
@@ -80,25 +89,27 @@ __device__ __forceinline__ void fma_part(const float (&xv)[M], const BlockPart<L
     for (int m = 0; m < M; ++m) {
       s[m] = xv[m] * d;
       corr[m] += s[m];
+      sw[m] = s[m] * 16777216.0f;  // 2^24
     }
   }
 #pragma unroll
   for (int w = 0; w < BlockPart<LPB>::kWords; ++w) {
-    uint32_t lo = b.q[w] & 0x0f0f0f0fu;
-    uint32_t hi = b.q[w] & 0xf0f0f0f0u;
-    // Hide the masks from the optimizer: otherwise it folds each
-    // (masked >> 8n) & 0xff into a 4-bit field extract plus a convert, instead
-    // of one v_cvt_f32_ubyteN per nibble.
-    asm volatile("" : "+v"(lo), "+v"(hi));
+    const uint32_t q = b.q[w];
+    const uint32_t q8 = q >> 8;
+    // halves (low, high): bytes 0 and 2, then bytes 1 and 3, of the dword;
+    // columns 2*byte (low nibble) and 2*byte + 1 (16 x high nibble)
+    const uint32_t h[4] = {q & 0x000f000fu, q & 0x00f000f0u, q8 & 0x000f000fu,
+                           q8 & 0x00f000f0u};
+    constexpr int kCol[4][2] = {{0, 4}, {1, 5}, {2, 6}, {3, 7}};
 #pragma unroll
-    for (int by = 0; by < 4; ++by) {
-      const float fl = static_cast<float>((lo >> (8 * by)) & 0xffu);  // v_cvt_f32_ubyteN
-      const float fh = static_cast<float>((hi >> (8 * by)) & 0xffu);  // 16 * high nibble
-      const int c = 2 * (4 * w + by);
+    for (int k = 0; k < 4; ++k) {
+      const float v0 = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)h[k]));
+      const float v1 = static_cast<float>(__builtin_bit_cast(_Float16, (uint16_t)(h[k] >> 16)));
+      const int c0 = 8 * w + kCol[k][0], c1 = 8 * w + kCol[k][1];
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        acc[m][c] = __builtin_fmaf(s[m], fl, acc[m][c]);
-        acc[m][c + 1] = __builtin_fmaf(s[m], fh, acc[m][c + 1]);
+        acc[m][c0] = __builtin_fmaf(sw[m], v0, acc[m][c0]);
+        acc[m][c1] = __builtin_fmaf(sw[m], v1, acc[m][c1]);
       }
     }
   }
