@@ -31,6 +31,7 @@ namespace {
 
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / kWaveSize;
+constexpr int kIdRun = 16;  // 64-pair groups whose ids a wave loads at once
 static_assert(Q4_MOE_MAX_E <= kRouteThreads, "one lane per expert");
 
 struct PrefillRoute {
@@ -47,15 +48,17 @@ struct PrefillRoute {
 size_t route_lds_bytes(int E) { return ((size_t)kRouteWaves * E + kRouteWaves) * sizeof(int); }
 
 // Wave w owns a contiguous run of 64-pair groups and walks it twice, in pair
-// order. Pass 1 counts its pairs per expert (lanes with the same id find each
-// other with one ballot per id bit; the lowest such lane adds their number).
-// Between the passes, lane e sums expert e's counts, the workgroup scans them
-// into each expert's first sorted row and its m-tiles, and lane e turns its
-// per-wave counts into per-wave first rows (waves in order). Pass 2 gives each
-// pair its sorted row: its wave's current row for the expert plus its rank
-// among the group's lanes with that id; the group's lowest such lane then
-// moves the row on. Pair order is kept within every expert (a stable sort),
-// with two workgroup barriers around the scan instead of barriers per group.
+// order. Pass 1 counts its pairs per expert (LDS atomic adds into the wave's
+// own row). Between the passes, lane e sums expert e's counts, the workgroup
+// scans them into each expert's first sorted row and its m-tiles, and lane e
+// turns its per-wave counts into per-wave first rows (waves in order). Pass 2
+// gives each pair its sorted row: its wave's current row for the expert plus
+// its rank among the group's lanes with that id (they find each other with
+// one ballot per id bit); the group's lowest such lane then moves the row on.
+// Pair order is kept within every expert (a stable sort), with two workgroup
+// barriers around the scan instead of barriers per group. The whole sort runs
+// on one CU: the second pass's id match (about 60 vector instructions per
+// group) is most of its time.
 __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(PrefillRoute a) {
   extern __shared__ int route_lds[];
   int* s_wc = route_lds;                         // [kRouteWaves][E]
@@ -71,18 +74,28 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
   int* wc = s_wc + wave * a.E;  // this wave's row: only this wave touches it in the passes
   for (int e = lane; e < a.E; e += kWaveSize) wc[e] = 0;
 
-  auto load_id = [&](int g) {
-    const int p = g * kWaveSize + lane;
-    return (g < g1 && p < a.npairs) ? a.ids[p] : -1;
+  // The ids of kIdRun groups are loaded at once (one memory round trip per
+  // run instead of one per group), then the groups are taken in order.
+  int ev[kIdRun];
+  auto load_run = [&](int gr) {
+#pragma unroll
+    for (int u = 0; u < kIdRun; ++u) {
+      const int p = (gr + u) * kWaveSize + lane;
+      ev[u] = (gr + u < g1 && p < a.npairs) ? a.ids[p] : -1;
+    }
   };
-  // pass 1: counts per expert, the next group's id loaded ahead
-  int e_next = load_id(g0);
-  for (int g = g0; g < g1; ++g) {
-    const int e = e_next;
-    e_next = load_id(g + 1);
-    const bool valid = e >= 0 && e < a.E;
-    const uint64_t same = same_id_lanes(e, valid);
-    if (valid && (same & below) == 0) wc[e] += __popcll(same);
+  // pass 1: counts per expert
+  for (int gr = g0; gr < g1; gr += kIdRun) {
+    load_run(gr);
+    // fully unrolled (a guard, not a break): the ids stay in registers with
+    // static indices and the waits count only their loads
+#pragma unroll
+    for (int u = 0; u < kIdRun; ++u) {
+      if (gr + u < g1) {  // uniform
+        const int e = ev[u];
+        if (e >= 0 && e < a.E) atomicAdd(&wc[e], 1);  // counts only: no ranks needed
+      }
+    }
   }
   __syncthreads();
 
@@ -110,21 +123,25 @@ __global__ __launch_bounds__(kRouteThreads) void moe_prefill_route_kernel(Prefil
   __syncthreads();
 
   // pass 2: sorted rows
-  e_next = load_id(g0);
-  for (int g = g0; g < g1; ++g) {
-    const int e = e_next;
-    e_next = load_id(g + 1);
-    const int p = g * kWaveSize + lane;
-    const bool valid = e >= 0 && e < a.E;
-    const uint64_t same = same_id_lanes(e, valid);
-    int q = -1;
-    if (valid) {
-      const int row = wc[e];  // read by every lane of the id before its lowest lane moves it
-      q = row + __popcll(same & below);
-      if ((same & below) == 0) wc[e] = row + __popcll(same);
-      a.src[q] = p / a.topk;
+  for (int gr = g0; gr < g1; gr += kIdRun) {
+    load_run(gr);
+#pragma unroll
+    for (int u = 0; u < kIdRun; ++u) {
+      if (gr + u < g1) {  // uniform
+        const int e = ev[u];
+        const int p = (gr + u) * kWaveSize + lane;
+        const bool valid = e >= 0 && e < a.E;
+        const uint64_t same = same_id_lanes(e, valid);
+        int q = -1;
+        if (valid) {
+          const int row = wc[e];  // read by every lane of the id before its lowest lane moves it
+          q = row + __popcll(same & below);
+          if ((same & below) == 0) wc[e] = row + __popcll(same);
+          a.src[q] = p / a.topk;
+        }
+        if (p < a.npairs) a.pos[p] = q;
+      }
     }
-    if (p < a.npairs) a.pos[p] = q;
   }
 }
 
