@@ -456,10 +456,16 @@ __global__ __launch_bounds__(2 * kGemmThreads) void gemm_q4_0_kernel(Args g) {
   B[0] = g.B;
   if constexpr (NM == 2) B[1] = g.B1;
   if (g.tiles) {
-    // grouped: plain dispatch order (the live tiles come first; the XCD remap
-    // would crowd them onto a few XCDs)
-    const int tile = blockIdx.x / g.tiles_n;
-    tn = blockIdx.x - tile * g.tiles_n;
+    // grouped: all column tiles of an m-tile on one XCD (they read the same X
+    // rows, and neighbouring 72-byte row segments of the weights share 128-byte
+    // lines, so that XCD's L2 fetches both once), m-tiles round robin over the
+    // 8 XCDs (the live m-tiles come first in the list). Workgroup b runs on XCD
+    // b % 8 as that XCD's (b / 8)-th workgroup. With plain dispatch order the
+    // column tiles of an m-tile landed on different XCDs and the gate/up pass
+    // read 2.9x its algorithmic bytes from HBM.
+    const int i = blockIdx.x / kNumXcd;
+    const int tile = (int)(blockIdx.x % kNumXcd) + kNumXcd * (i / g.tiles_n);
+    tn = i % g.tiles_n;
     if (tile >= *g.n_tiles) return;  // the whole workgroup, before any barrier
     const int4 tl = g.tiles[tile];
 #pragma unroll
@@ -677,7 +683,8 @@ hipError_t launch_gemm_grouped(const uint16_t* X, int x_rows, const uint8_t* B, 
     f.cpw = 2;
     f.tiles_n = N / (2 * fast::BN);
   }
-  const long long grid = (long long)max_tiles * f.tiles_n;
+  // every XCD gets ceil(max_tiles / 8) m-tile slots of tiles_n workgroups
+  const long long grid = (long long)((max_tiles + kNumXcd - 1) / kNumXcd) * kNumXcd * f.tiles_n;
   if (grid > 0x7fffffffLL) return hipErrorInvalidValue;
   if (grid == 0) return hipSuccess;
   constexpr int BM = fast::kGroupedBM;

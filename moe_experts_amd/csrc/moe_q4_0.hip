@@ -350,13 +350,31 @@ __device__ void mfma_item_tile(const ExpertArgs& a, const ItemRec& it, int r, fl
 }
 
 // A batch: the vector items (a) and the matrix-core items (am) in one grid.
-// The grid is sized for the most items the routing can make; the live tiles
-// of both kinds come first, evenly interleaved (tile b is a matrix-core tile
-// when floor(b * Lm / (Lv + Lm)) steps up at b), so the vector tiles' unpack
-// and FMA work and the matrix-core tiles' MFMA work share every CU; tiles past
-// the live count exit at once. Two kernels would run one after the other on
-// the stream, each with its own ramp and tail. Plain dispatch order spreads
-// the live tiles over all 8 XCDs.
+// The grid is sized for the most items the routing can make; tiles past the
+// live count exit at once. The live tiles are handed out in chunks of
+// kTileChunk consecutive tiles of one kind: the column tiles of the same rows
+// (consecutive in both kinds' tile order) share 128-byte lines at their edges,
+// so a chunk runs on one XCD and those lines are fetched into its L2 once
+// (at 32 tokens this cut the expert kernels' HBM reads from 1.6x to about 1.1x
+// the experts' bytes).
+// Chunks go round robin over the 8 XCDs (all of them get live work), and the
+// vector and matrix-core chunks are interleaved (chunk q is a matrix-core
+// chunk when floor(q * Cm / (Cv + Cm)) steps up at q), so the vector tiles'
+// unpack and FMA work and the matrix-core tiles' MFMA work share every XCD.
+// Two kernels would run one after the other on the stream, each with its own
+// ramp and tail.
+// 12: the gate/up column tiles of one matrix-core row run, or four vector
+// ones (3 each); same-box sweep at 32 tokens: 12 / 24 / 48 tiles gave
+// 341 / 343 / 346 us (smaller chunks spread the live tiles more evenly).
+constexpr int kTileChunk = 12;
+
+// Workgroups to launch for Lv vector and Lm matrix-core tiles at most: every
+// XCD needs a whole number of chunk slots for the chunks it can be given.
+inline long long mixed_grid(long long Lv, long long Lm) {
+  const long long chunks = (Lv + kTileChunk - 1) / kTileChunk + (Lm + kTileChunk - 1) / kTileChunk;
+  return (chunks + kNumXcd - 1) / kNumXcd * kNumXcd * kTileChunk;
+}
+
 template <bool STAGED>
 __global__ __launch_bounds__(kThreads) void moe_expert_mixed_kernel(ExpertArgs a, ExpertArgs am) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -364,17 +382,28 @@ __global__ __launch_bounds__(kThreads) void moe_expert_mixed_kernel(ExpertArgs a
   const int pm = am.nmat * am.C * am.S;
   const int Lv = *a.n_items * pv;
   const int Lm = *am.n_items * pm;
-  const int total = Lv + Lm;
-  const int b = blockIdx.x;
-  if (b >= total) return;
-  const int m0 = (int)((long long)b * Lm / total);
-  const int m1 = (int)((long long)(b + 1) * Lm / total);
-  if (m1 > m0) {
-    const int item = m0 / pm;
+  constexpr int G = kTileChunk;
+  const int Cv = (Lv + G - 1) / G;
+  const int Cm = (Lm + G - 1) / G;
+  const int Ct = Cv + Cm;
+  // Workgroup b runs on XCD b % 8 as that XCD's (b / 8)-th workgroup: there it
+  // takes tile o of chunk q, the XCD's (b / 8 / G)-th chunk.
+  const int x = blockIdx.x % kNumXcd;
+  const int i = blockIdx.x / kNumXcd;
+  const int q = x + kNumXcd * (i / G);
+  const int o = i % G;
+  if (q >= Ct) return;
+  const int qm0 = (int)((long long)q * Cm / Ct);
+  const int qm1 = (int)((long long)(q + 1) * Cm / Ct);
+  if (qm1 > qm0) {
+    const int m = qm0 * G + o;
+    if (m >= Lm) return;
+    const int item = m / pm;
     const ItemRec it = am.items[item];
-    mfma_item_tile(am, it, m0 - item * pm, smem);
+    mfma_item_tile(am, it, m - item * pm, smem);
   } else {
-    const int v = b - m0;
+    const int v = (q - qm0) * G + o;
+    if (v >= Lv) return;
     const int item = v / pv;
     const ItemRec it = a.items[item];
     vector_item_tile<kMaxChunk, STAGED>(a, it, v - item * pv, smem);
@@ -511,7 +540,10 @@ hipError_t launch_expert_single(const ExpertArgs& a, int max_items, bool staged,
 
 hipError_t launch_expert_mixed(const ExpertArgs& a, const ExpertArgs& am, int max_items,
                                int max_mitems, bool staged, hipStream_t st) {
-  const dim3 grid(max_items * a.nmat * a.C * a.S + max_mitems * am.nmat * am.C * am.S);
+  const long long g = mixed_grid((long long)max_items * a.nmat * a.C * a.S,
+                                 (long long)max_mitems * am.nmat * am.C * am.S);
+  if (g > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)g);
   const int lv = vector_lds_bytes<kMaxChunk>(a.Kt, staged);
   const int lm = max_mitems > 0 ? mfma_item_lds_bytes(am.Kt) : 0;
   const int lds = lv > lm ? lv : lm;
