@@ -12,7 +12,8 @@
 //      the K chunk [256 s, 256 s + 256). It stages that chunk of its 16 router
 //      rows and of every token's activations in LDS (all loads in flight at
 //      once); a wave takes 4 experts, its lanes the tokens (one token per
-//      lane), and reads the 4 rows as LDS broadcasts. Each lane forms its 4
+//      lane), and reads the 4 rows as LDS broadcasts. A single token instead
+//      spreads the chunk's k over the lanes (below). Each lane forms its 4
 //      dot products over the chunk in k order and writes them as K-split
 //      partials, part[t][e][s]; the split
 //      count is padded to a multiple of 4 by chunks past H, which write zeros.
@@ -49,6 +50,43 @@ __global__ __launch_bounds__(kRouterWaves * kWaveSize) void router_logits_kernel
   const int k0 = s * kRouterKc;
   const int n4 = max(0, min(kRouterKc, H - k0) / 4);  // float4 of this chunk (H % 4 == 0)
   constexpr int kThr = kRouterWaves * kWaveSize;
+  if (T == 1) {
+    // A single token: lane c takes float4 c of the chunk for each of the
+    // wave's 4 experts (16-byte loads straight from memory, no staging) and the
+    // wave adds the 64 lane sums with a fixed butterfly (every lane ends with
+    // the same value), instead of one lane running all 256 FMAs. A single
+    // token's logits therefore match its batched ones to rounding, not
+    // bitwise, as for the single-token expert tiles. No barrier on this path.
+    const int lane = threadIdx.x % kWaveSize;
+    const int e0 = g * kRouterEG + (threadIdx.x / kWaveSize) * kRouterEW;
+    if (e0 >= E) return;
+    const bool in = lane < n4;
+    const float4 xv = in ? *reinterpret_cast<const float4*>(x + k0 + 4 * lane)
+                         : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    float4 rv[kRouterEW];
+#pragma unroll
+    for (int j = 0; j < kRouterEW; ++j)
+      rv[j] = (in && e0 + j < E)
+                  ? *reinterpret_cast<const float4*>(Wr + (size_t)(e0 + j) * H + k0 + 4 * lane)
+                  : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    float acc[kRouterEW];
+#pragma unroll
+    for (int j = 0; j < kRouterEW; ++j) {
+      float a = xv.x * rv[j].x;
+      a = __builtin_fmaf(xv.y, rv[j].y, a);
+      a = __builtin_fmaf(xv.z, rv[j].z, a);
+      a = __builtin_fmaf(xv.w, rv[j].w, a);
+#pragma unroll
+      for (int off = kWaveSize / 2; off > 0; off >>= 1) a += __shfl_xor(a, off);
+      acc[j] = a;
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kRouterEW; ++j)
+        if (e0 + j < E) part[(size_t)(e0 + j) * Sp + s] = acc[j];
+    }
+    return;
+  }
   // one round trip: the chunk of the workgroup's router rows and of every
   // token's activations (zeros past the chunk or past E)
   for (int i = threadIdx.x; i < kRouterEG * (kRouterKc / 4); i += kThr) {
