@@ -103,10 +103,27 @@ def capture(torch, fn):
     return g
 
 
+def time_replays(torch, graphs, reps):
+    """Total seconds of `reps` round-robin replays, with events only around all
+    of them: an event recorded between two replays adds a gap of its own (about
+    5 us per replay on MI355X), so it stays out of the mean."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for r in range(reps):
+        graphs[r % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
 def time_graph_dist(torch, graphs, reps, per_replay):
-    """Replay the graphs round robin with an event after every replay; each
-    replay holds `per_replay` units (steps or launches). Returns the mean time
-    per unit over all replays and the per-replay times per unit (seconds)."""
+    """Replay the graphs round robin; each replay holds `per_replay` units
+    (steps or launches). Returns the mean time per unit, from a pass with events
+    only around all replays, and the per-replay times per unit, from a pass
+    before it with an event after every replay (those include the events' own
+    gaps, so their quantiles sit a few microseconds per replay above the mean;
+    the pass also warms the clocks up for the mean's)."""
     for g in graphs:
         g.replay()
     torch.cuda.synchronize()
@@ -117,7 +134,8 @@ def time_graph_dist(torch, graphs, reps, per_replay):
         evs[r + 1].record()
     torch.cuda.synchronize()
     ts = [evs[r].elapsed_time(evs[r + 1]) * 1e-3 / per_replay for r in range(reps)]
-    return evs[0].elapsed_time(evs[-1]) * 1e-3 / (reps * per_replay), ts
+    mean = time_replays(torch, graphs, reps) / (reps * per_replay)
+    return mean, ts
 
 
 def time_graph(torch, graphs, reps, per_replay):
@@ -134,7 +152,7 @@ def time_calls(torch, call, reps):
     and routings rotate inside a graph as they do across graphs), replayed round
     robin. A decode step's graph holds the MoE call of every layer, so a graph
     replay's own start-up cost is shared by many calls there; timing one call per
-    graph instead adds that cost (9-16 us on this GPU) to every call. The one-call
+    graph instead adds that cost (about 4 us on MI355X) to every call. The one-call
     figure is returned too. Returns (mean s, per-replay s per call, one-call mean s)."""
     G = MOE_CALLS_PER_GRAPH
     graphs = [capture(torch, lambda c=c: [call(c * G + u) for u in range(G)]) for c in range(16)]
@@ -191,15 +209,18 @@ def bench_dense(torch, dev, steps, warmup):
     for r in range(warmup):
         graphs[r % R].replay()
     torch.cuda.synchronize()
+    # the timed steps: events only before the first and after the last
+    order = [graphs[(warmup + r) % R] for r in range(R)]
     t0 = time.perf_counter()
+    dt = time_replays(torch, order, steps) / steps
+    wall = (time.perf_counter() - t0) / steps
+    # the distribution, from the same steps again with an event after each
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for r in range(steps):
-        graphs[(warmup + r) % R].replay()
+        order[r % R].replay()
         evs[r + 1].record()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    dt = evs[0].elapsed_time(evs[-1]) * 1e-3 / steps
     step_dist = quantiles_us([evs[r].elapsed_time(evs[r + 1]) * 1e-3 for r in range(steps)])
 
     # per call: graphs of 8 back-to-back launches of each call. Each matrix gets
