@@ -261,7 +261,8 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
 // cores (mfma_tile_accumulate), one weight per lane against 4 pairs' rows per
 // instruction. That instruction rounds like v_fma_f32, so every accumulator is
 // the FMA chain a vector tile forms for that phase and column; the phases and
-// the corrections are then summed in phase order 0..15 and finished with the
+// the corrections are then summed in the vector tiles' fixed order (groups of
+// four as (p0 + p2) + (p1 + p3), the groups in turn) and finished with the
 // vector tiles' expression. A pair's partial sums are therefore bitwise the same
 // whichever kind of item carries it: results stay independent of how many
 // other pairs chose the same expert.
@@ -318,10 +319,16 @@ __device__ void expert_mfma_tile(const ExpertArgs& a, const ItemRec& it, int mat
       const int n = o - r * kMfmaCols;
       const int m = r + 4 * h;
       if (m < it.cnt && n0 + n < a.N) {
-        float sum = 0.0f, cs = 0.0f;
-        for (int pp = 0; pp < kMfmaPhases; ++pp) {
-          sum += sa[(pp * 4 + r) * kMfmaCols + n];
-          cs += sc[(pp * 8 + m) * JW + n / kBlockWeights];
+        // the 16 phases in the vector tiles' order (reduce_phases): per group
+        // of four, (p0 + p2) + (p1 + p3), then the groups in order
+        auto ph = [&](int pp) { return sa[(pp * 4 + r) * kMfmaCols + n]; };
+        auto pc = [&](int pp) { return sc[(pp * 8 + m) * JW + n / kBlockWeights]; };
+        float sum = (ph(0) + ph(2)) + (ph(1) + ph(3));
+        float cs = (pc(0) + pc(2)) + (pc(1) + pc(3));
+#pragma unroll
+        for (int w = 1; w < kMfmaPhases / 4; ++w) {
+          sum += (ph(4 * w) + ph(4 * w + 2)) + (ph(4 * w + 1) + ph(4 * w + 3));
+          cs += (pc(4 * w) + pc(4 * w + 2)) + (pc(4 * w + 1) + pc(4 * w + 3));
         }
         const float c8 = 8.0f * cs;
         // the pair of row m, selected without indexing the record at run time

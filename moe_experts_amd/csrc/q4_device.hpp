@@ -703,28 +703,146 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no copy may land after the tile
 }
 
-// LDS floats needed by reduce_phases: one activation row's accumulators,
-// and for formats with the offset the raw corrections of all rows and their
-// phase sums.
+// LDS floats needed by reduce_phases: the larger of its two paths. Full
+// 16-block tiles: one activation row's wave sums (4 waves x 16 block columns x
+// kPhaseBlockPitch) and, for formats with the offset, the wave sums of the
+// corrections of all rows. Narrower tiles: one row's accumulators of all
+// phases and, with the offset, the raw corrections and their phase sums.
+constexpr int kPhaseBlockPitch = 36;  // floats per block column: 16-byte rows, banks spread
 template <int M, int LPB, class Fmt = Q4_0Format>
 constexpr int phase_lds_floats() {
-  return (32 / LPB) * (256 + 1) + (Fmt::kOffset ? M * (256 + 1) + M * 256 : 0);
+  constexpr int tree = 4 * 16 * kPhaseBlockPitch + (Fmt::kOffset ? 4 * M * 16 * LPB : 0);
+  constexpr int flat = (32 / LPB) * (256 + 1) + (Fmt::kOffset ? M * (256 + 1) + M * 256 : 0);
+  return tree > flat ? tree : flat;
 }
 
-// Sum a split-K tile over its P row phases through LDS, in phase order 0..P-1,
-// then finish each output once with Fmt::finish. For Q4_0: even columns
-// sum - 8*csum, odd columns sum/16 - 8*csum (csum = the phase sum of the
-// corrections; both rescalings are exact). The phase sum is linear, so
-// finishing after it equals finishing every lane first, at 1/P of the work;
-// the sums of acc and of 8*corr still run in the same order, so all-8 nibbles
-// still give exactly zero. Formats without the offset skip the corrections.
-// Hands each tile output (m, o), o in [0, ncols) with ncols <= 512, to
-// store(m, o, v). Needs 256 lanes and phase_lds_floats<M, LPB>() floats of
-// smem; contains workgroup barriers; ends with a barrier.
+// a + b where a comes from this lane and b from the lane 32 (or 16) away:
+// lanes below the distance return a_lo + a_hi, lanes above it b_lo + b_hi.
+__device__ __forceinline__ float swap_sum32(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ float swap_sum16(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
+                                                  __builtin_bit_cast(uint32_t, b), false, false);
+  const uint32_t r0 = r[0];
+  const uint32_t r1 = r[1];
+  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
+}
+
+// Sum a split-K tile over its P row phases, then finish each output once with
+// Fmt::finish. For Q4_0: even columns sum - 8*csum, odd columns sum/16 -
+// 8*csum (csum = the phase sum of the corrections; both rescalings are exact).
+// The phase sum is linear, so finishing after it equals finishing every lane
+// first, at 1/P of the work; the corrections run through the same order as
+// the accumulators, so acc - 8*corr still cancels exactly when every nibble is
+// 8 (8 and 128 are powers of two). Formats without the offset skip the
+// corrections. Hands each tile output (m, o), o in [0, ncols) with ncols <=
+// 512, to store(m, o, v). Needs 256 lanes and phase_lds_floats<M, LPB>()
+// floats of smem; contains workgroup barriers; ends with a barrier.
+//
+// Full tiles (16 block columns, Lr = 16*LPB lanes per phase, P = 16/LPB):
+// lane l of wave w holds row phase 4w/LPB + l/Lr. Inside the wave the phases
+// are summed by reduce-scatter lane swaps (distance 32, then 16 for LPB = 1),
+// which leaves each lane 8 columns of its block share; the 4 waves' sums then
+// meet in LDS once. The order is fixed: with p the 16 phases at LPB = 1, wave w
+// gives W_w = (p[4w] + p[4w+2]) + (p[4w+1] + p[4w+3]) and the tile sum is
+// ((W_0 + W_1) + W_2) + W_3 (at LPB = 2, W_w = p[2w] + p[2w+1]; at LPB = 4,
+// W_w = p[w]). The MoE matrix-core tiles sum their 16 phases in the same order.
+// Narrower tiles (fewer block columns, or Q8_0's 8) sum the phases through LDS
+// in phase order 0..P-1.
+template <int M, int LPB, class Fmt = Q4_0Format, class Store>
+__device__ __forceinline__ void reduce_phases_full(const float (&acc)[M][32 / LPB],
+                                                   const float (&corr)[M], float* smem,
+                                                   int ncols, Store store) {
+  constexpr int CPL = 32 / LPB;  // columns per lane share
+  constexpr int PW = 4 / LPB;    // row phases per wave
+  constexpr int NV = CPL / PW;   // columns per lane after the in-wave sums
+  constexpr int Lr = 16 * LPB;
+  static_assert(NV == 8 && kThreads == 256, "16 block columns, 4 waves");
+  float* W = smem;                                   // [wave][block][kPhaseBlockPitch]
+  float* CW = W + 4 * 16 * kPhaseBlockPitch;         // [wave][m][Lr] corrections
+  const int t = threadIdx.x;
+  const int lane = t & (kWaveSize - 1);
+  const int wave = t / kWaveSize;
+  const int v = lane & (Lr - 1);  // block share: block v / LPB, part v % LPB
+  const int g = lane / Lr;        // phase within the wave
+  float* wdst = W + (wave * 16 + v / LPB) * kPhaseBlockPitch + (v % LPB) * CPL + NV * g;
+
+  // corrections: wave sums of all rows (every lane of a phase group gets them)
+  float cw[M];
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float c = corr[m];
+    if constexpr (PW >= 2) c += __shfl_xor(c, 32);
+    if constexpr (PW == 4) c += __shfl_xor(c, 16);
+    cw[m] = c;
+  }
+  __syncthreads();  // smem may still hold the tile's staging
+  if constexpr (Fmt::kOffset) {
+    if (g == 0) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) CW[(wave * M + m) * Lr + v] = cw[m];
+    }
+  }
+  // this thread's outputs o = t and t + 256: block, column, lane share
+  int bo_[2], c32_[2], vv_[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int o = t + 256 * k;
+    bo_[k] = o / kBlockWeights;
+    c32_[k] = o - bo_[k] * kBlockWeights;
+    vv_[k] = bo_[k] * LPB + c32_[k] / CPL;
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    float R[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) R[c] = acc[m][c];
+    if constexpr (PW >= 2) {
+#pragma unroll
+      for (int u = 0; u < CPL / 2; ++u) R[u] = swap_sum32(R[u], R[u + CPL / 2]);
+    }
+    if constexpr (PW == 4) {
+#pragma unroll
+      for (int u = 0; u < CPL / 4; ++u) R[u] = swap_sum16(R[u], R[u + CPL / 4]);
+    }
+    *reinterpret_cast<float4*>(wdst) = float4{R[0], R[1], R[2], R[3]};
+    *reinterpret_cast<float4*>(wdst + 4) = float4{R[4], R[5], R[6], R[7]};
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int o = t + 256 * k;
+      if (o < ncols) {
+        const float* src = W + bo_[k] * kPhaseBlockPitch + c32_[k];
+        float sum = src[0];
+#pragma unroll
+        for (int w = 1; w < 4; ++w) sum += src[w * 16 * kPhaseBlockPitch];
+        float csum = 0.0f;
+        if constexpr (Fmt::kOffset) {
+          const float* cs = CW + m * Lr + vv_[k];
+          csum = cs[0];
+#pragma unroll
+          for (int w = 1; w < 4; ++w) csum += cs[w * M * Lr];
+        }
+        store(m, o, Fmt::finish(sum, c32_[k] % CPL, csum));
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <int M, int LPB, class Fmt = Q4_0Format, class Store>
 __device__ __forceinline__ void reduce_phases(const float (&acc)[M][32 / LPB],
                                               const float (&corr)[M], float* smem, int Lr, int P,
                                               int ncols, Store store) {
+  if (Lr == 16 * LPB) {  // uniform: full 16-block tiles
+    reduce_phases_full<M, LPB, Fmt>(acc, corr, smem, ncols, store);
+    return;
+  }
   constexpr int CPL = 32 / LPB;
   constexpr int kStride = 256 + 1;
   float* A = smem;                  // [CPL][kStride] accumulators of one row m

@@ -61,23 +61,6 @@ __host__ __device__ constexpr int mfma_xs_bytes(int rows) {
   return (mfma_rows_pad<MH, JW, NW>(rows) * SH::XW + SH::NT - 1) / SH::NT * SH::NT * 4;
 }
 
-// a + b where a comes from this lane and b from the lane 32 (or 16) away:
-// lanes below the distance return a_lo + a_hi, lanes above it b_lo + b_hi.
-__device__ __forceinline__ float swap_sum32(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a),
-                                                  __builtin_bit_cast(uint32_t, b), false, false);
-  const uint32_t r0 = r[0];
-  const uint32_t r1 = r[1];
-  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
-}
-__device__ __forceinline__ float swap_sum16(float a, float b) {
-  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a),
-                                                  __builtin_bit_cast(uint32_t, b), false, false);
-  const uint32_t r0 = r[0];
-  const uint32_t r1 = r[1];
-  return __builtin_bit_cast(float, r0) + __builtin_bit_cast(float, r1);
-}
-
 // One row of the lane: s = x * d (and its correction sum), then the 8 nibbles
 // of its qs dword against the MH activation halves.
 template <int MH>
