@@ -517,6 +517,24 @@ void plan_tiles(int K, int NB, int kt_target, int& C, int& Kt, int& S) {
   S = (K + Kt - 1) / Kt;
 }
 
+// A single token's K split: the largest S (at most max_S) whose grid of
+// C column tiles x nmat matrices x S splits x npairs items stays within
+// kSingleGrid workgroups (two per CU). Same-box sweeps of the gate/up tile
+// height: 6 experts 576 / 504 / 432 / 360 workgroups gave 30.2 / 28.5 / 29.3 /
+// 30.4 us per call, 8 experts (the whole layer) 768 / 672 / 576 / 480 gave
+// 45.7 / 46.1 / 47.4 / 45.4 us: about 500 workgroups either way. Sizing the
+// down tiles by the same rule made the whole layer slower (55 against 45 us),
+// so down keeps its fixed 384-row tiles.
+constexpr int kSingleGrid = 512;
+void plan_single_tiles(int K, int NB, int nmat, int npairs, int max_S, int& C, int& Kt, int& S) {
+  constexpr int P = kThreads / (kJt * kLPB);
+  C = (NB + kJt - 1) / kJt;
+  int s = kSingleGrid / (C * nmat * npairs);
+  s = s < 1 ? 1 : (s > max_S ? max_S : s);
+  plan_tiles(K, NB, (K + s - 1) / s, C, Kt, S);
+  if (Kt < P) plan_tiles(K, NB, P, C, Kt, S);
+}
+
 // LDS of the vector tiles for items of up to MC pairs (activation tile or
 // weight staging, then the phase sums).
 template <int MC>
@@ -579,10 +597,14 @@ MoePlan plan_moe(int T, int H, int I, int E, int topk) {
   p.max_items = (T == 1) ? npairs : (npairs < E ? npairs : E);
   p.max_mitems = (T == 1) ? 0 : npairs / (kMaxChunk + 1);
   // K tiles: a single token has only 6 experts' worth of tiles, so it splits
-  // K finer (more workgroups); batches use long tiles (less partial-sum
-  // traffic, fewer tile epilogues). The choice depends only on whether T is 1.
+  // K finer (more workgroups: gate/up by plan_single_tiles, sized by its
+  // number of items); batches use long tiles (less partial-sum traffic, fewer
+  // tile epilogues) that depend only on (H, I), never on T or the routing.
   const bool single = (T == 1);
-  plan_tiles(H, I / kBlockWeights, single ? 320 : 1280, p.gu_C, p.gu_Kt, p.gu_S);
+  if (single)
+    plan_single_tiles(H, I / kBlockWeights, 2, npairs, kActMaxSplits, p.gu_C, p.gu_Kt, p.gu_S);
+  else
+    plan_tiles(H, I / kBlockWeights, 1280, p.gu_C, p.gu_Kt, p.gu_S);
   plan_tiles(I, H / kBlockWeights, single ? 384 : 768, p.dn_C, p.dn_Kt, p.dn_S);
   p.gu_Cm = (I / kBlockWeights + kMfmaJW - 1) / kMfmaJW;
   p.dn_Cm = (H / kBlockWeights + kMfmaJW - 1) / kMfmaJW;
