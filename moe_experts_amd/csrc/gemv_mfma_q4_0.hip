@@ -21,10 +21,10 @@
 namespace q4 {
 namespace {
 
-// LDS of the GEMV tile: the activation tile, later reused by the phase sums.
+// LDS of the GEMV tile: the activation rings, later reused by the phase sums.
 template <int MH, int JW, int NW>
-constexpr int mfma_lds_bytes(int Kt) {
-  const int xs = mfma_xs_bytes<MH, JW, NW>(Kt);
+constexpr int mfma_lds_bytes() {
+  const int xs = mfma_ring_bytes<MH, JW, NW>();
   const int red = NW * MfmaShape<MH, JW, NW>::OUT * 4;
   return xs > red ? xs : red;
 }
@@ -89,7 +89,7 @@ __device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)
 #pragma unroll
   for (int r = 0; r < 4; ++r) cb[r] = __shfl(ch, (lane & ~3) | r);
 
-  __syncthreads();  // the activation tile is reused as the phase-sum scratch
+  __syncthreads();  // the activation rings are reused as the phase-sum scratch
   float* red = smem + wave * SH::OUT;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -148,7 +148,7 @@ __global__ __launch_bounds__(NW * kWaveSize) void gemv_q4_0_mfma_kernel(MfmaArgs
 
 template <int MH, int JW, int NW>
 hipError_t launch_mfma_t(const MfmaArgs& a, hipStream_t st) {
-  const int lds = mfma_lds_bytes<MH, JW, NW>(a.Kt);
+  constexpr int lds = mfma_lds_bytes<MH, JW, NW>();
   hipLaunchKernelGGL((gemv_q4_0_mfma_kernel<MH, JW, NW>), dim3(a.C * a.S), dim3(NW * kWaveSize),
                      lds, st, a);
   return hipGetLastError();
@@ -176,12 +176,10 @@ uint64_t mfma_offset_span(int Kt, int JW, int NW, uint32_t pitch) {
 // used, n / (256 * ceil(n / 256)), over the candidates with at most 2048
 // waves in all (two per SIMD; measured: more waves only add partial sums) and
 // at least 64 rows per tile; ties go to more waves, then to fewer splits (less
-// partial-sum traffic). Tiles are capped so that the activation tile fits in
-// kMfmaMaxXs bytes of LDS.
+// partial-sum traffic).
 bool plan_gemv_mfma(int M, int N, int K, GemvPlan& p) {
   if (M < 3 || M > 8) return false;
   const int NB = N / kBlockWeights;
-  const int XW = M > 4 ? 8 : 4;
   const uint32_t pitch = (uint32_t)NB * kBlockBytes;
   double best = -1.0;
   for (int NW : {4, 8})
@@ -198,8 +196,6 @@ bool plan_gemv_mfma(int M, int N, int K, GemvPlan& p) {
         const long long n = (long long)C * S;
         if (n * NW > 2048) break;
         if (S > 1 && kt < 64) break;
-        const int rows_pad = ((kt + PT - 1) / PT + kMfmaRB - 1) / kMfmaRB * kMfmaRB * PT;
-        if (rows_pad * XW * 4 > kMfmaMaxXs) continue;
         if (mfma_offset_span(kt, JW, NW, pitch) >= (1ull << 31)) continue;
         const double rounds = (double)((n + 255) / 256);
         const double score = (double)n / (256.0 * rounds) + 1e-7 * (double)(n * NW) - 1e-9 * S;

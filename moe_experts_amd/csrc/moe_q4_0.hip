@@ -266,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void moe_expert_kernel(ExpertArgs a) {
 // vector tiles' expression. A pair's partial sums are therefore bitwise the same
 // whichever kind of item carries it: results stay independent of how many
 // other pairs chose the same expert.
-// LDS: the activation tile, then [16 phases][4 rows][128 columns] accumulator
+// LDS: the activation rings, then [16 phases][4 rows][128 columns] accumulator
 // scratch (one activation half at a time) and [16][8][4] corrections.
 // ---------------------------------------------------------------------------
 constexpr int kMfmaPhases = kMfmaNW * (16 / kMfmaJW);
@@ -298,7 +298,7 @@ __device__ void expert_mfma_tile(const ExpertArgs& a, const ItemRec& it, int mat
 
   float* sa = smem;                                  // [phase][row r][column]
   float* sc = smem + kMfmaPhases * 4 * kMfmaCols;    // [phase][m][block]
-  __syncthreads();  // the activation tile is done with
+  __syncthreads();  // every wave is done with its activation ring
 #pragma unroll
   for (int h = 0; h < MH; ++h) sc[(p * 8 + q + 4 * h) * JW + jj] = corr[h];
   const int n0 = g.j0 * kBlockWeights;
@@ -546,9 +546,9 @@ int vector_lds_bytes(int Kt, bool staged) {
   return t > rf ? t : rf;
 }
 
-// LDS of the matrix-core tiles: the activation tile, then the phase sums.
-int mfma_item_lds_bytes(int Kt) {
-  const int xs = mfma_xs_bytes<2, kMfmaJW, kMfmaNW>(Kt);
+// LDS of the matrix-core tiles: the activation rings, then the phase sums.
+int mfma_item_lds_bytes() {
+  const int xs = mfma_ring_bytes<2, kMfmaJW, kMfmaNW>();
   const int sc = 4 * kMfmaScratchFloats;
   return xs > sc ? xs : sc;
 }
@@ -570,7 +570,7 @@ hipError_t launch_expert_mixed(const ExpertArgs& a, const ExpertArgs& am, int ma
   if (g > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)g);
   const int lv = vector_lds_bytes<kMaxChunk>(a.Kt, staged);
-  const int lm = max_mitems > 0 ? mfma_item_lds_bytes(am.Kt) : 0;
+  const int lm = max_mitems > 0 ? mfma_item_lds_bytes() : 0;
   const int lds = lv > lm ? lv : lm;
   if (staged)
     hipLaunchKernelGGL((moe_expert_mixed_kernel<true>), grid, dim3(kThreads), lds, st, a, am);

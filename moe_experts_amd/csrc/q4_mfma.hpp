@@ -21,7 +21,10 @@
 // Each lane loads its 4-byte qs dword and 2-byte scale per row with buffer
 // loads from a buffer over the tile's rows only (rows past the tile read zeros
 // with no memory access), kMfmaRB rows per batch, kMfmaSets batches in flight
-// in a register ring. Activations are staged once per tile in LDS.
+// in a register ring. Each wave copies the activations of its own rows batch
+// by batch into a private LDS ring (LDS-DMA, issued with the batch's weight
+// loads), so no wave waits for a workgroup-wide activation tile before its
+// first products and the loop needs no barrier.
 #pragma once
 
 #include "q4_device.hpp"
@@ -32,7 +35,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMfmaRB = 4;      // rows per lane and batch
 constexpr int kMfmaSets = 2;    // batches in flight (measured: 3 or 4 are slower)
-constexpr int kMfmaMaxXs = 64 * 1024;  // LDS bytes for the activation tile
 
 template <int MH, int JW, int NW>
 struct MfmaShape {
@@ -43,22 +45,16 @@ struct MfmaShape {
   static constexpr int NE = 8 * MH / PW;    // accumulator quads per lane after the wave sum
   static constexpr int TW = JW * 32;        // tile columns
   static constexpr int OUT = TW * 4 * MH;   // tile outputs (rows 0 .. 4*MH-1)
+  static constexpr int XB = kMfmaRB * PW * XW;                 // activations of a wave's batch
+  static constexpr int XI = (XB + kWaveSize - 1) / kWaveSize;  // LDS-DMA copies per batch
+  static constexpr int XSLOT = XI * kWaveSize;                 // ring slot (whole copies)
   static_assert(JW == 4 || JW == 8, "tile widths of 4 or 8 blocks");
 };
 
+// LDS bytes of the activation rings of a workgroup (kMfmaSets slots per wave).
 template <int MH, int JW, int NW>
-__host__ __device__ constexpr int mfma_rows_pad(int rows) {
-  using SH = MfmaShape<MH, JW, NW>;
-  const int nl = (rows + SH::PT - 1) / SH::PT;
-  return (nl + kMfmaRB - 1) / kMfmaRB * kMfmaRB * SH::PT;
-}
-
-// LDS bytes of the activation tile of a tile of `rows` rows (whole staging
-// passes of NT words, so every DMA lane of the last pass writes inside it).
-template <int MH, int JW, int NW>
-__host__ __device__ constexpr int mfma_xs_bytes(int rows) {
-  using SH = MfmaShape<MH, JW, NW>;
-  return (mfma_rows_pad<MH, JW, NW>(rows) * SH::XW + SH::NT - 1) / SH::NT * SH::NT * 4;
+__host__ __device__ constexpr int mfma_ring_bytes() {
+  return NW * kMfmaSets * MfmaShape<MH, JW, NW>::XSLOT * 4;
 }
 
 // One row of the lane: s = x * d (and its correction sum), then the 8 nibbles
@@ -104,8 +100,8 @@ struct MfmaTileGeom {
 // Accumulate one tile (raw acc and corr per lane; see above). Activation row m
 // of the tile is x + xoff[m] floats, indexed by the matrix row, for m < M;
 // rows m >= M are zero. x_bytes bounds every activation read. smem must hold
-// mfma_xs_bytes<MH, JW, NW>(rows) bytes; the tile ends with the activation
-// tile still in LDS (callers that reuse it start with a barrier).
+// mfma_ring_bytes<MH, JW, NW>() bytes; every copy into it has landed when the
+// function returns (callers that reuse it for phase sums start with a barrier).
 template <int MH, int JW, int NW>
 __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
                                                      const float* __restrict__ x,
@@ -114,6 +110,7 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
                                                      float (&corr)[MH]) {
   using SH = MfmaShape<MH, JW, NW>;
   constexpr int PW = SH::PW, PT = SH::PT, XW = SH::XW, RB = kMfmaRB;
+  constexpr int XI = SH::XI, XSLOT = SH::XSLOT;
   constexpr uint32_t kOut = 0x80000000u;
   const int t = threadIdx.x;
   const int lane = t % kWaveSize;
@@ -126,31 +123,37 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
   const int rows = g.rows;
   const int nl = (rows + PT - 1) / PT;  // rows of the busiest lane (uniform)
   const int nb = (nl + RB - 1) / RB;     // batches (uniform)
-  const int rows_pad = nb * RB * PT;
   const int myph = wave * PW + ph;
   const int j0 = g.j0;
+  constexpr int NSET = kMfmaSets;
 
-  // Activation tile xs[row * XW + e]: e = 2q + h holds row m = q + 4h (MH = 2),
-  // e = q holds m = q (MH = 1), so a lane reads its values with one LDS load.
-  // LDS-DMA copies, zeros for rows m >= M; padding rows zeroed below.
-  float* xs = smem;
-  {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
-    for (int q0 = 0; q0 < rows * XW; q0 += SH::NT) {
-      const int idx = q0 + t;
-      const int row = idx / XW;
-      const int e = idx - row * XW;
-      const int m = MH == 2 ? (e >> 1) + 4 * (e & 1) : e;
-      int xo = 0;
+  // Activation ring of this wave: slot k holds batch b (b % NSET == k) as
+  // [row i][phase p][e], e = 2q + h holding row m = q + 4h (MH = 2) or e = q
+  // holding m = q (MH = 1), so a lane reads a row's values with one LDS load.
+  // DMA lane c of copy u fills element u*64 + c: its matrix row and activation
+  // row are fixed per lane, the batch moves the row by RB*PT. Lanes past the
+  // batch, rows m >= M and rows past the tile read zeros.
+  float* ring = smem + wave * NSET * XSLOT;
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, x_bytes);
+  uint32_t xo[XI];
+  int xrow[XI];
 #pragma unroll
-      for (int mm = 0; mm < 4 * MH; ++mm)
-        if (mm == m) xo = xoff[mm];
-      const uint32_t off = (m < M && row < rows) ? (uint32_t)(xo + k0 + row) * 4u : kOut;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_t*)(xs + q0 + wave * kWaveSize), 4,
-                                               off, 0, 0, 0);
-    }
+  for (int u = 0; u < XI; ++u) {
+    const int l = u * kWaveSize + lane;
+    const int i = l / (PW * XW);
+    const int rem = l - i * (PW * XW);
+    const int p = rem / XW;
+    const int e = rem - p * XW;
+    const int m = MH == 2 ? (e >> 1) + 4 * (e & 1) : e;
+    int xm = 0;
+#pragma unroll
+    for (int mm = 0; mm < 4 * MH; ++mm)
+      if (mm == m) xm = xoff[mm];
+    xrow[u] = i * PT + wave * PW + p;
+    const bool ok = l < SH::XB && m < M;
+    xo[u] = ok ? (uint32_t)(xm + k0 + xrow[u]) * 4u : kOut;
+    if (!ok) xrow[u] = 0x40000000;
   }
-  __builtin_amdgcn_sched_barrier(0);
 
   // Weights: a buffer over this tile's rows, so rows past the tile are out of
   // range; blocks past the matrix's last column get bit 31 (out of range too).
@@ -163,9 +166,16 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
   const uint32_t step = (uint32_t)PT * pitch;  // bytes between a lane's rows
 
   // Register sets of NSET batches in a ring: batch b lives in set b % NSET.
-  constexpr int NSET = kMfmaSets;
+  // A batch issues its activation copies first, then its weight loads.
   uint32_t Q[NSET][RB], D[NSET][RB];
   auto load = [&](int b, int k) {
+    const int brow = b * RB * PT;
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+      const uint32_t o = brow + xrow[u] < rows ? xo[u] + (uint32_t)brow * 4u : kOut;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rx, (lds_void_t*)(ring + k * XSLOT + u * kWaveSize), 4, o, 0, 0, 0);
+    }
     const uint32_t bo = (uint32_t)(b * RB) * step;
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
@@ -179,36 +189,39 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[h][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   }
-  // Rows past the tile load zeros (zero scale) against a zero-padded
-  // activation, so every batch runs whole.
+  // Rows past the tile load zeros (zero scale) against zero activations, so
+  // every batch runs whole. Batch b's copies have landed once at most its own
+  // weight loads and the NSET - 1 batches issued after it are outstanding (the
+  // loop issues batches in order, also past the last one).
   auto compute = [&](int b, int k) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * RB + (NSET - 1) * (XI + 2 * RB)));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const float* xs = ring + k * XSLOT;
+    float xv[RB][MH];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      const int tr = (b * RB + i) * PT + myph;
-      float xv[MH];
+      const int tr = i * PW + ph;
       if constexpr (MH == 2) {
         const float2 v = *reinterpret_cast<const float2*>(xs + tr * XW + 2 * q);
-        xv[0] = v.x;
-        xv[1] = v.y;
+        xv[i][0] = v.x;
+        xv[i][1] = v.y;
       } else {
-        xv[0] = xs[tr * XW + q];
+        xv[i][0] = xs[tr * XW + q];
       }
-      mfma_row<MH>(xv, D[k][i], Q[k][i], acc, corr);
     }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) mfma_row<MH>(xv[i], D[k][i], Q[k][i], acc, corr);
   };
 
 #pragma unroll
   for (int k = 0; k < NSET; ++k) load(k, k);
   __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * NSET * RB));  // the activation copies have landed
-  for (int idx = rows * XW + t; idx < rows_pad * XW; idx += SH::NT) xs[idx] = 0.0f;
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): only LDS stores need a wait
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 
   // The scheduling barriers keep each batch's loads in issue order, so the
-  // compiler's wait before a batch counts only that batch's loads.
+  // waits before a batch count only that batch's loads. A slot is refilled
+  // only after the batch that read it has used its values (the LDS reads are
+  // waited for before the products that follow them).
   int b = 0;
   for (; b + NSET <= nb; b += NSET) {
 #pragma unroll
@@ -219,6 +232,7 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  static_assert(NSET == 2, "the tail's wait assumes one batch issued after it");
 #pragma unroll
   for (int k = 0; k < NSET - 1; ++k)
     if (b + k < nb) compute(b + k, k);
