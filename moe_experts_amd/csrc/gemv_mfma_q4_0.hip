@@ -21,12 +21,11 @@
 namespace q4 {
 namespace {
 
-// LDS of the GEMV tile: the activation rings, later reused by the phase sums.
+// LDS of the GEMV tile: the activation rings, then the waves' phase sums
+// (after the rings, so a wave that finishes early writes its sums at once).
 template <int MH, int JW, int NW>
 constexpr int mfma_lds_bytes() {
-  const int xs = mfma_ring_bytes<MH, JW, NW>();
-  const int red = NW * MfmaShape<MH, JW, NW>::OUT * 4;
-  return xs > red ? xs : red;
+  return mfma_ring_bytes<MH, JW, NW>() + NW * MfmaShape<MH, JW, NW>::OUT * 4;
 }
 
 struct MfmaArgs {
@@ -89,8 +88,8 @@ __device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)
 #pragma unroll
   for (int r = 0; r < 4; ++r) cb[r] = __shfl(ch, (lane & ~3) | r);
 
-  __syncthreads();  // the activation rings are reused as the phase-sum scratch
-  float* red = smem + wave * SH::OUT;
+  float* sums = smem + mfma_ring_bytes<MH, JW, NW>() / 4;
+  float* red = sums + wave * SH::OUT;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int m = r + 4 * hsel;
@@ -108,17 +107,25 @@ __device__ __forceinline__ void mfma_tile_store(v4f (&acc)[MH][8], float (&corr)
     }
   }
   __syncthreads();
+  // Every LDS read of the sum is issued before the first store.
+  constexpr int IT = SH::OUT / SH::NT;
+  static_assert(IT * SH::NT == SH::OUT, "whole passes over the tile");
   float* out = (a.S == 1) ? a.y : a.part + (size_t)s * a.M * a.N;
   const int n0 = j0 * kBlockWeights;
-  for (int o = threadIdx.x; o < SH::OUT; o += SH::NT) {
+  float sum[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int o = it * SH::NT + threadIdx.x;
+    sum[it] = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum[it] += sums[w * SH::OUT + o];
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int o = it * SH::NT + threadIdx.x;
     const int m = o / SH::TW;
     const int n = o - m * SH::TW;
-    if (m < a.M && n0 + n < a.N) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) sum += smem[w * SH::OUT + o];
-      out[(size_t)m * a.N + n0 + n] = sum;
-    }
+    if (m < a.M && n0 + n < a.N) out[(size_t)m * a.N + n0 + n] = sum[it];
   }
 }
 
