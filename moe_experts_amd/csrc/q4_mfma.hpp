@@ -57,8 +57,36 @@ __host__ __device__ constexpr int mfma_ring_bytes() {
   return NW * kMfmaSets * MfmaShape<MH, JW, NW>::XSLOT * 4;
 }
 
-// One row of the lane: s = x * d (and its correction sum), then the 8 nibbles
-// of its qs dword against the MH activation halves.
+// One row of the lane: s = x * d (and its correction sum) and the 8 nibbles
+// of its qs dword as floats (low nibbles 0..15, high nibbles 16x).
+template <int MH>
+struct MfmaRowOps {
+  float s[MH];
+  float f[8];
+};
+template <int MH>
+__device__ __forceinline__ void mfma_row_prep(const float (&xv)[MH], uint32_t dbits, uint32_t qs,
+                                              MfmaRowOps<MH>& r, float (&corr)[MH]) {
+  const float d = half_bits_to_float(dbits);
+  {
+    // corr sums exactly the rounded s the products use (all-8 nibbles cancel)
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int h = 0; h < MH; ++h) {
+      r.s[h] = xv[h] * d;
+      corr[h] += r.s[h];
+    }
+  }
+  uint32_t lo = qs & 0x0f0f0f0fu;
+  uint32_t hi = qs & 0xf0f0f0f0u;
+  asm volatile("" : "+v"(lo), "+v"(hi));  // keep one v_cvt_f32_ubyteN per nibble
+#pragma unroll
+  for (int by = 0; by < 4; ++by) {
+    r.f[2 * by] = static_cast<float>((lo >> (8 * by)) & 0xffu);
+    r.f[2 * by + 1] = static_cast<float>((hi >> (8 * by)) & 0xffu);
+  }
+}
+// One row, conversions and products interleaved (fewer live registers).
 template <int MH>
 __device__ __forceinline__ void mfma_row(const float (&xv)[MH], uint32_t dbits, uint32_t qs,
                                          v4f (&acc)[MH][8], float (&corr)[MH]) {
@@ -89,6 +117,16 @@ __device__ __forceinline__ void mfma_row(const float (&xv)[MH], uint32_t dbits, 
   }
 }
 
+// The row's products: nibble i against the MH activation halves.
+template <int MH>
+__device__ __forceinline__ void mfma_row_products(const MfmaRowOps<MH>& r, v4f (&acc)[MH][8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int h = 0; h < MH; ++h)
+      acc[h][i] = __builtin_amdgcn_mfma_f32_4x4x1f32(r.s[h], r.f[i], acc[h][i], 0, 0, 0);
+}
+
 // Geometry of one tile.
 struct MfmaTileGeom {
   const uint8_t* B;  // the matrix (K rows of NB blocks)
@@ -102,7 +140,7 @@ struct MfmaTileGeom {
 // rows m >= M are zero. x_bytes bounds every activation read. smem must hold
 // mfma_ring_bytes<MH, JW, NW>() bytes; every copy into it has landed when the
 // function returns (callers that reuse it for phase sums start with a barrier).
-template <int MH, int JW, int NW>
+template <int MH, int JW, int NW, bool PHASED = false>
 __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
                                                      const float* __restrict__ x,
                                                      uint32_t x_bytes, const int (&xoff)[4 * MH],
@@ -210,8 +248,20 @@ __device__ __forceinline__ void mfma_tile_accumulate(const MfmaTileGeom& g,
         xv[i][0] = xs[tr * XW + q];
       }
     }
+    if constexpr (PHASED) {
+      // All conversions of the batch first, then its products: no product
+      // waits on the conversion just before it, and one wave's products can
+      // run on the matrix core while another wave converts (more registers).
+      MfmaRowOps<MH> ops[RB];
 #pragma unroll
-    for (int i = 0; i < RB; ++i) mfma_row<MH>(xv[i], D[k][i], Q[k][i], acc, corr);
+      for (int i = 0; i < RB; ++i) mfma_row_prep<MH>(xv[i], D[k][i], Q[k][i], ops[i], corr);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < RB; ++i) mfma_row_products<MH>(ops[i], acc);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RB; ++i) mfma_row<MH>(xv[i], D[k][i], Q[k][i], acc, corr);
+    }
   };
 
 #pragma unroll
