@@ -148,8 +148,7 @@ __global__ __launch_bounds__(NW * kWaveSize) void gemv_q4_0_mfma_kernel(MfmaArgs
   MfmaTileGeom g{a.B, a.NB, j0, k0, rows};
   v4f acc[MH][8];
   float corr[MH];
-  mfma_tile_accumulate<MH, JW, NW, true>(g, a.x, (uint32_t)(4 * a.M * a.K), xoff, a.M, smem, acc,
-                                         corr);
+  mfma_tile_accumulate<MH, JW, NW>(g, a.x, (uint32_t)(4 * a.M * a.K), xoff, a.M, smem, acc, corr);
 
   mfma_tile_store<MH, JW, NW>(acc, corr, smem, a, s, j0, lane, wave, q, jj);
 }
