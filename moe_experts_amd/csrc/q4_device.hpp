@@ -684,16 +684,19 @@ __device__ __forceinline__ void tile_accumulate_staged(const SplitTile& g,
     __builtin_amdgcn_s_waitcnt(vmcnt_imm((NBUF - 1) * SS::NI));
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t* buf = wbuf + (b % NBUF) * SS::kBufBytes;
+    // Every LDS read of the batch first (rows past the tile read the zeros
+    // their copies wrote and the zero-padded activations), so the batch waits
+    // once for LDS instead of once per row.
+    BlockPart<LPB> bp[RB];
+    float xv[RB][M];
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
-      if (b * RB + i < nl) {  // uniform
-        BlockPart<LPB> bp;
-        read_block_part_lds<LPB>(buf, (i * SS::WP + seg0) * (SS::CPS * 16) + in_seg, part, bp);
-        float xv[M];
-        read_x_row<M>(xs, (b * RB + i) * P + r, xv);
-        fma_part<M, LPB>(xv, bp, acc, corr);
-      }
+      read_block_part_lds<LPB>(buf, (i * SS::WP + seg0) * (SS::CPS * 16) + in_seg, part, bp[i]);
+      read_x_row<M>(xs, (b * RB + i) * P + r, xv[i]);
     }
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      if (b * RB + i < nl) fma_part<M, LPB>(xv[i], bp[i], acc, corr);  // uniform
     // every read of this buffer has returned before it is refilled
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
