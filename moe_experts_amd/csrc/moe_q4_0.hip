@@ -647,7 +647,7 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   ra.mitems = mitems;
   ra.n_mitems = n_mitems;
   hipError_t err = hipSuccess;
-  if (p.MC > 1) {  // single token: items are the pairs themselves
+  if (p.T > 1) {  // a single token needs no route: its items are the pairs
     hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, st, ra);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -684,8 +684,8 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   gm.items = mitems;
   gm.n_items = n_mitems;
   gm.C = p.gu_Cm;
-  err = (p.MC == 1) ? launch_expert_single(g, p.max_items, staged_gu, st)
-                    : launch_expert_mixed(g, gm, p.max_items, p.max_mitems, staged_gu, st);
+  err = (p.T == 1) ? launch_expert_single(g, p.max_items, staged_gu, st)
+                   : launch_expert_mixed(g, gm, p.max_items, p.max_mitems, staged_gu, st);
   if (err != hipSuccess) return err;
 
   const size_t nh = (size_t)npairs * p.I;
@@ -693,7 +693,7 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   // gate/up partial sums while staging their activation tile (same sums, same
   // order, same expression as moe_act_kernel), which saves a kernel launch.
   constexpr int kP = kThreads / (kJt * kLPB);
-  const bool fuse_act = p.MC == 1 && staged_dn && p.gu_S <= kActMaxSplits &&
+  const bool fuse_act = p.T == 1 && staged_dn && p.gu_S <= kActMaxSplits &&
                         tile_rows_padded(p.dn_Kt, kP, kStagedRB) <= kActMaxVals * kThreads;
   if (!fuse_act) {
     hipLaunchKernelGGL(moe_act_kernel, dim3((unsigned)((nh + kSumThreads - 1) / kSumThreads)),
@@ -724,8 +724,8 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   dm.items = mitems;
   dm.n_items = n_mitems;
   dm.C = p.dn_Cm;
-  err = (p.MC == 1) ? launch_expert_single(d, p.max_items, staged_dn, st)
-                    : launch_expert_mixed(d, dm, p.max_items, p.max_mitems, staged_dn, st);
+  err = (p.T == 1) ? launch_expert_single(d, p.max_items, staged_dn, st)
+                   : launch_expert_mixed(d, dm, p.max_items, p.max_mitems, staged_dn, st);
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;
