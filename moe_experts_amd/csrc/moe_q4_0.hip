@@ -51,7 +51,7 @@ constexpr int kMfmaPairs = 8;  // pairs per matrix-core work item (3 .. 8)
 constexpr int kMfmaJW = 4;     // matrix-core tiles: 4 block columns, 4 waves: 16 row
 constexpr int kMfmaNW = 4;     // phases, the same phases as the vector tiles
 constexpr int kSplitLoads = 16;    // act: splits summed with all loads in flight
-constexpr int kCombineSplits = 4;  // combine: same, per slot
+constexpr int kCombineSplits = 16;  // combine: splits it sums with every load in flight
 constexpr int kLPB = 1;       // whole-block lane shares, for every item size
 constexpr int kJt = 16;       // block columns per tile: 288-byte row segments
 
@@ -460,6 +460,7 @@ __global__ __launch_bounds__(kSumThreads) void moe_act_kernel(const float* __res
 // ---------------------------------------------------------------------------
 // 5. combine: slot order 0..topk-1, split order inside each slot
 // ---------------------------------------------------------------------------
+template <int SMAX>
 __global__ __launch_bounds__(kSumThreads) void moe_combine_kernel(
     const float* __restrict__ part, const int32_t* __restrict__ ids, const float* __restrict__ w,
     float* __restrict__ out, int T, int H, int E, int topk, int S) {
@@ -469,18 +470,19 @@ __global__ __launch_bounds__(kSumThreads) void moe_combine_kernel(
   const int n = (int)(idx - (size_t)t * H);
   const size_t slab = (size_t)T * topk * H;
   float acc = 0.0f;
-  if (S <= kCombineSplits) {
+  if (SMAX > 0) {
     // ids, weights and every split partial of every slot in flight at once
     // (indices clamped; values of invalid slots are loaded but not used)
+    constexpr int SM = SMAX > 0 ? SMAX : 1;
     int ev[Q4_MOE_MAX_TOPK];
-    float wv[Q4_MOE_MAX_TOPK], pv[Q4_MOE_MAX_TOPK][kCombineSplits];
+    float wv[Q4_MOE_MAX_TOPK], pv[Q4_MOE_MAX_TOPK][SM];
 #pragma unroll
     for (int sl = 0; sl < Q4_MOE_MAX_TOPK; ++sl) {
       const int p = t * topk + min(sl, topk - 1);
       ev[sl] = ids[p];
       wv[sl] = w[p];
 #pragma unroll
-      for (int k = 0; k < kCombineSplits; ++k)
+      for (int k = 0; k < SM; ++k)
         pv[sl][k] =
             __builtin_nontemporal_load(part + (size_t)min(k, S - 1) * slab + (size_t)p * H + n);
     }
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(kSumThreads) void moe_combine_kernel(
       if (sl >= topk || ev[sl] < 0 || ev[sl] >= E) continue;
       float yd = 0.0f;
 #pragma unroll
-      for (int k = 0; k < kCombineSplits; ++k)
+      for (int k = 0; k < SM; ++k)
         if (k < S) yd += pv[sl][k];
       acc = __builtin_fmaf(wv[sl], yd, acc);
     }
@@ -522,9 +524,10 @@ void plan_tiles(int K, int NB, int kt_target, int& C, int& Kt, int& S) {
 // kSingleGrid workgroups (two per CU). Same-box sweeps of the gate/up tile
 // height: 6 experts 576 / 504 / 432 / 360 workgroups gave 30.2 / 28.5 / 29.3 /
 // 30.4 us per call, 8 experts (the whole layer) 768 / 672 / 576 / 480 gave
-// 45.7 / 46.1 / 47.4 / 45.4 us: about 500 workgroups either way. Sizing the
-// down tiles by the same rule made the whole layer slower (55 against 45 us),
-// so down keeps its fixed 384-row tiles.
+// 45.7 / 46.1 / 47.4 / 45.4 us: about 500 workgroups either way. The down
+// tiles follow the same rule (480 workgroups of 192 rows instead of 240 of
+// 384: 28.45 -> 27.55 us per call, 45.0 -> 43.55 us per layer), with the
+// combine summing up to kCombineSplits splits with every load in flight.
 constexpr int kSingleGrid = 512;
 void plan_single_tiles(int K, int NB, int nmat, int npairs, int max_S, int& C, int& Kt, int& S) {
   constexpr int P = kThreads / (kJt * kLPB);
@@ -605,7 +608,10 @@ MoePlan plan_moe(int T, int H, int I, int E, int topk) {
     plan_single_tiles(H, I / kBlockWeights, 2, npairs, kActMaxSplits, p.gu_C, p.gu_Kt, p.gu_S);
   else
     plan_tiles(H, I / kBlockWeights, 1280, p.gu_C, p.gu_Kt, p.gu_S);
-  plan_tiles(I, H / kBlockWeights, single ? 384 : 768, p.dn_C, p.dn_Kt, p.dn_S);
+  if (single)
+    plan_single_tiles(I, H / kBlockWeights, 1, npairs, kCombineSplits, p.dn_C, p.dn_Kt, p.dn_S);
+  else
+    plan_tiles(I, H / kBlockWeights, 768, p.dn_C, p.dn_Kt, p.dn_S);
   p.gu_Cm = (I / kBlockWeights + kMfmaJW - 1) / kMfmaJW;
   p.dn_Cm = (H / kBlockWeights + kMfmaJW - 1) / kMfmaJW;
   size_t off = 0;
@@ -729,9 +735,19 @@ hipError_t launch_moe(const float* x, const uint8_t* Wg, const uint8_t* Wu, cons
   if (err != hipSuccess) return err;
 
   const size_t total = (size_t)p.T * p.H;
-  hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)((total + kSumThreads - 1) / kSumThreads)),
-                     dim3(kSumThreads), 0, st,
-                     dn_part, ids, w, out, p.T, p.H, p.E, p.topk, p.dn_S);
+  const dim3 cgrid((unsigned)((total + kSumThreads - 1) / kSumThreads)), cblock(kSumThreads);
+  if (p.dn_S <= 4)
+    hipLaunchKernelGGL(moe_combine_kernel<4>, cgrid, cblock, 0, st, dn_part, ids, w, out, p.T,
+                       p.H, p.E, p.topk, p.dn_S);
+  else if (p.dn_S <= 8)
+    hipLaunchKernelGGL(moe_combine_kernel<8>, cgrid, cblock, 0, st, dn_part, ids, w, out, p.T,
+                       p.H, p.E, p.topk, p.dn_S);
+  else if (p.dn_S <= kCombineSplits)
+    hipLaunchKernelGGL(moe_combine_kernel<kCombineSplits>, cgrid, cblock, 0, st, dn_part, ids, w,
+                       out, p.T, p.H, p.E, p.topk, p.dn_S);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<0>, cgrid, cblock, 0, st, dn_part, ids, w, out, p.T,
+                       p.H, p.E, p.topk, p.dn_S);
   return hipGetLastError();
 }
 
