@@ -126,8 +126,11 @@ def test_gemv_invariants_bitwise(M):
 # columns with a partial last tile (N/32 = 13, 21, 43), fewer rows than the
 # tile's row phases (K = 1, 3, 15), one and two activation halves, odd batches,
 # and a matrix too wide for that kernel's plan (the vector tiles take it).
+# N/32 a multiple of 8 plans only 8-block tiles: one column tile (N = 256), two,
+# three, with ragged row counts.
 MATRIX_CORE = [(3, 1, 416), (5, 3, 672), (7, 15, 416), (8, 17, 96), (4, 129, 4128),
-               (6, 300, 1376), (8, 700, 11008), (3, 5000, 672), (8, 64, 262144)]
+               (6, 300, 1376), (8, 700, 11008), (3, 5000, 672), (8, 64, 262144),
+               (5, 77, 256), (3, 2049, 512), (4, 130, 768), (8, 4099, 256)]
 
 
 @pytest.mark.parametrize("M,K,N", MATRIX_CORE)

@@ -46,7 +46,10 @@ def small_experts(seed, H, I, E):
 @pytest.mark.parametrize("T,H,I,E,topk", [(1, 64, 32, 5, 1), (3, 64, 32, 5, 2), (17, 96, 64, 4, 6),
                                           (5, 320, 160, 7, 3), (64, 64, 64, 3, 8), (2, 1024, 512, 9, 6),
                                           (9, 768, 256, 6, 4), (33, 512, 768, 12, 6),
-                                          (1, 512, 256, 6, 4), (1, 1024, 768, 9, 6)])
+                                          (1, 512, 256, 6, 4), (1, 1024, 768, 9, 6),
+                                          # long down K: the combine sums 6, 16 and 17 splits
+                                          (2, 64, 4608, 3, 2), (1, 64, 13056, 3, 2),
+                                          (2, 64, 13056, 3, 2)])
 def test_moe_small_match_oracle(T, H, I, E, topk):
     x = datagen.activations(T * 7 + H, T, H)
     Wg, Wu, Wd = small_experts(100 * E + I, H, I, E)
